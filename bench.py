@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the low-bit MoE FFN layer on one MI355X.
+
+A step is one pass of the whole layer (route -> permute -> gate/up+SiLU*mul
+-> down+combine) over one batch of synthetic input resident in HBM.
+Default workload: the single-token decode layer (T=1, H=2048, E=128, top-8,
+I=768, int4 G128 experts, one always-on shared expert).  Decode throughput
+is packed-weight GB/s over the experts a step touches (codes + fp16
+scales, each touched expert counted once); prefill (--config 4) is TFLOP/s
+over 6*P*H*I useful flops.
+
+So that repeated steps measure HBM rather than the 256 MB Infinity Cache,
+decode steps rotate over R device copies of the weight bank (same routing,
+distinct addresses) with R * touched bytes >= --rotate-bytes.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE W4 FFN layer: packed-weight GB/s (decode) and TFLOP/s (prefill)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def touched_bytes(dl, counts, which=("w13", "w2")):
+    """Packed bytes (codes + fp16 scales) of the routed experts with at
+    least one pair, plus every shared expert, for the given matrices."""
+    per = {"w13": [], "w2": [], "w13_sh": [], "w2_sh": []}
+    for tag, oc, os_, (bits, group, N, K) in dl.bank.layout:
+        per[tag].append(N * K * bits // 8 + N * (K // group) * 2)
+    tot = 0
+    for m in which:
+        tot += sum(b for b, c in zip(per[m], counts) if c > 0)
+        tot += sum(per[m + "_sh"])
+    return tot
+
+
+def cpu_baseline(layer, seconds, unit_amount, unit, sample_note):
+    import numpy as np  # noqa: F401
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.oracle_layer(layer)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    return {"value": unit_amount / per, "unit": unit, "cores": cores,
+            "kind": "oracle",
+            "sample": f"{sample_note}; {n} full oracle layer passes in {el:.1f} s "
+                      f"({per * 1e3:.1f} ms each); cores = BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--rotate-bytes", type=float, default=1.5e9)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["auto", "gemv", "mfma"], default="auto")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this layer runs on one GPU; multi-GPU runs are "
+                          "not part of this benchmark (use --gpus 1)"}))
+        log("bench.py: --gpus N with N > 1 is not supported: the layer is a "
+            "single-GPU kernel library (expert-parallel sharding is design only)")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from packed_bit_grouped_amd import _lib as L
+    from packed_bit_grouped_amd.layer import DeviceLayer, run_layer
+    from synth import CONFIGS, make_layer
+
+    cfg = CONFIGS[args.config]
+    flags = {"auto": 0, "gemv": 1, "mfma": 2}[args.path]
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    log(f"[bench] generating {cfg.name} ...")
+    layer = make_layer(cfg)
+    log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
+    dl = DeviceLayer.from_synth(layer, "cuda:0")
+    act = cfg.act
+    B = dl.buffers(act)
+    st = torch.cuda.current_stream()
+
+    # routing is identical on every step: learn the touched experts once
+    dl.run(B, flags)
+    torch.cuda.synchronize()
+    counts = B.counts.cpu().numpy()
+    n_touched = int((counts > 0).sum())
+    decode = args.config != 4
+    bytes_all = touched_bytes(dl, counts)
+    bytes_w13 = touched_bytes(dl, counts, ("w13",))
+    P = cfg.T * cfg.k
+    flops = 6.0 * P * cfg.H * cfg.I + 6.0 * cfg.n_shared * cfg.T * cfg.H * cfg.I_shared
+    flops_gateup = 4.0 * P * cfg.H * cfg.I + 4.0 * cfg.n_shared * cfg.T * cfg.H * cfg.I_shared
+
+    banks = [dl.bank]
+    if decode:
+        R = max(1, math.ceil(args.rotate_bytes / bytes_all))
+        R = min(R, 128)
+        free, _ = torch.cuda.mem_get_info()
+        R = max(1, min(R, int(0.5 * free // dl.bank.buf.numel())))
+        for _ in range(R - 1):
+            banks.append(dl.bank.rebased(dl.bank.buf.clone()))
+        log(f"[bench] {n_touched} routed experts touched, {bytes_all / 1e6:.3f} MB/step; "
+            f"rotating over {R} bank copies ({R * bytes_all / 1e9:.2f} GB touched per cycle)")
+
+    def step(i):
+        run_layer(banks[i % len(banks)], dl.x, dl.logits, B, cfg.renormalize, flags)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(args.steps):
+        step(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms * 1e3:.2f} us/step")
+
+    # the dominant kernel (gate/up + SiLU*mul), timed with events on the
+    # stream it is launched on, within a second timed region
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    for i in range(args.steps):
+        bk = banks[i % len(banks)]
+        L.moe_route_topk(dl.logits, T, E, k, cfg.renormalize, B.ids, B.w)
+        L.moe_permute(B.ids, T, k, E, B.tile_m, B.counts, B.offsets, B.sorted_pair,
+                      B.pair_pos, B.tiles, B.n_tiles)
+        ev[i][0].record(st)
+        L.moe_w4_gateup_silu(B.act, dl.x, T, H, I, E, k, bk.w13, bk.w13_sh,
+                             cfg.n_shared, cfg.I_shared, B.offsets, B.sorted_pair,
+                             B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes, flags)
+        ev[i][1].record(st)
+        L.moe_w4_down_combine(B.act, B.h, T, H, I, E, k, bk.w2, bk.w2_sh, cfg.n_shared,
+                              cfg.I_shared, B.w, B.offsets, B.sorted_pair, B.pair_pos,
+                              B.tiles, B.n_tiles, B.tile_m, B.out, B.ws, B.ws_bytes, flags)
+    torch.cuda.synchronize()
+    gu_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    log(f"[bench] gate/up kernel: {gu_ms * 1e3:.2f} us/launch")
+
+    if decode:
+        value = bytes_all / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+        ach = bytes_w13 / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "proj_gemv_kernel (gate/up + SiLU*mul)",
+                "algorithmic_bytes": bytes_w13}
+    else:
+        value = flops / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        ach = flops_gateup / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
+                "kernel": "gate/up + SiLU*mul", "algorithmic_flops": flops_gateup}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        if decode:
+            cpu = cpu_baseline(layer, args.cpu_seconds, bytes_all / 1e9, "GB/s",
+                               f"{cfg.name}, same seeded layer")
+        else:
+            cpu = {"value": None, "unit": "TFLOP/s", "cores": None, "kind": "oracle",
+                   "sample": "prefill oracle not timed by default"}
+
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if act == "a16" else "int8",
+        "data": "synthetic (seeded; int4/int2 experts quantized from N(0, 0.02))",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                   "I": cfg.I, "n_shared": cfg.n_shared, "act": act,
+                   "experts_touched": n_touched,
+                   "bytes_per_step": bytes_all, "flops_per_step": flops,
+                   "bank_copies_rotated": len(banks), "path": args.path},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+/*
+ * moe_w4.h -- C ABI of a low-bit mixture-of-experts FFN layer for AMD
+ * MI355X (gfx950).
+ *
+ * The layer follows the build log "Two 96 GB Ascend cards run Qwen3.8
+ * Flash-Next" (ai-pulse-lab), section "Keep low-bit weights packed, do the
+ * work on the NPU": expert weights stay packed in device memory, tokens
+ * are routed to experts on the device, and the expert projections run as
+ * grouped operations with fused gate/up handling, blocked reduction, tile
+ * reuse and a dedicated W4A8 mode -- never by expanding the packed bank
+ * into a dequantized copy.  Section "Remove sync and launch overhead from
+ * the token loop" of the same log asks for a hot path with no
+ * device-to-host reads and reused per-step buffers; section "Make the
+ * hybrid model correct before making it fast" treats the kernel package
+ * and its host code as one versioned ABI.  Hence:
+ *
+ *   - every call is asynchronous on the caller's HIP stream and never
+ *     synchronizes with the host; sizes of device-side data (number of
+ *     tiles, tokens per expert) stay on the device and grids are sized
+ *     from host-known upper bounds;
+ *   - the library allocates nothing and keeps no state: the caller owns
+ *     every buffer (weights, descriptor tables, activations, outputs,
+ *     workspace) and keeps it alive and unmodified until the stream has
+ *     passed the call;
+ *   - calls return a moe_status and never throw; arguments are checked
+ *     on the host before anything is launched;
+ *   - one generic contract (T, H, I, E, k, group size, bit width), with
+ *     no per-model special cases.
+ *
+ * Layer definition (what the calls compute together):
+ *   ids, w   = top-k of the router logits per token (descending logit,
+ *              ties to the lower expert index); w = softmax over the
+ *              chosen k logits (renormalize=1) or the plain softmax
+ *              values (renormalize=0)
+ *   pairs    = (t, j) with flat index p = t*k + j, grouped by expert
+ *              (stable: increasing p within an expert)
+ *   gate/up  = g = x_t . W13_e[i], u = x_t . W13_e[I+i], h = SiLU(g)*u
+ *   down     = y = h . W2_e[n]
+ *   combine  = out[t] = sum_j w[t][j] * y(t, ids[t][j]) + sum_s y_s(t)
+ *   with W = code * scale (code int4 in [-8,7] or int2 in [-2,1], one
+ *   fp16 scale per row per K-group).  Shared experts are always on and
+ *   join with weight 1.0.
+ *
+ * Precision: A16 (bf16 activations): fp32 accumulation; h is rounded to
+ * bf16 between the projections.  A8: activations are quantized per row to
+ * int8 with scale = max|row| / 127 (fp32, round half to even); per-group
+ * int8 x int code partial sums are exact int32; they are scaled in fp32.
+ * out is bf16 (round to nearest even).
+ *
+ * All pointers are DEVICE pointers unless stated otherwise.
+ */
+#ifndef MOE_W4_H
+#define MOE_W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_W4_ABI_VERSION 1
+
+/* Version of the compiled library.  The Python binding refuses to load a
+ * library whose version differs from the header it was written for. */
+int moe_abi_version(void);
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_INVAL = -1,        /* bad argument (null pointer, size, shape)      */
+  MOE_E_UNSUPPORTED = -2,  /* valid but unsupported (bits, group, E, ...)   */
+  MOE_E_DEVICE = -3,       /* HIP error, or the current device is not gfx950 */
+  MOE_E_WORKSPACE = -4     /* workspace missing or smaller than required    */
+} moe_status;
+
+/* Static string for a status code (host pointer, never null). */
+const char* moe_status_str(int status);
+
+typedef enum {
+  MOE_A16 = 0,             /* bf16 activations                               */
+  MOE_A8 = 1               /* dynamic per-row int8 activations               */
+} moe_act;
+
+/* One quantized matrix W [N][K], K contiguous.  Tables of these descriptors
+ * live in DEVICE memory (one per expert); `codes` and `scales` point to
+ * device memory.
+ *   codes : N * K * bits / 8 bytes, row-major.  bits = 4: two codes per byte,
+ *           even K index in the low nibble.  bits = 2: four codes per byte,
+ *           lowest K index in the lowest two bits.  Two's complement.
+ *   scales: N * (K / group) fp16 bit patterns, row-major.
+ * Supported: bits in {2, 4}; group in {32, 64, 128, 256}; K % group == 0;
+ * a row of codes is a whole number of 16-byte chunks (K % 32 == 0 for
+ * int4, K % 64 == 0 for int2); codes 16-byte aligned, scales 4-byte
+ * aligned.  A descriptor the kernels cannot use (other bits or group,
+ * N/K different from the shape the call expects, null pointer) makes the
+ * kernels skip that expert and set bit 0 of the workspace error word. */
+typedef struct moe_qmat {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  int32_t bits;
+  int32_t group;
+  int32_t N;
+  int32_t K;
+} moe_qmat;                 /* 32 bytes */
+
+/* ---------------------------------------------------------------------
+ * moe_route_topk -- router top-k and softmax gating on the device
+ * (pages: tokens are routed to experts on the device; routing moved out of
+ * the host loop).
+ *   logits   fp32 [T][E]
+ *   topk_ids int32 [T][k]  (out) experts in descending logit order, ties
+ *                          to the lower index
+ *   topk_w   fp32 [T][k]   (out) gate weights
+ * Limits: 1 <= E <= 1024, 1 <= k <= E, T >= 0 (T = 0 launches nothing).
+ * Logits must be finite.
+ * ------------------------------------------------------------------- */
+moe_status moe_route_topk(const float* logits, int T, int E, int k,
+                          int renormalize, int32_t* topk_ids, float* topk_w,
+                          void* stream);
+
+/* ---------------------------------------------------------------------
+ * moe_permute -- stable counting sort of the T*k (token, expert) pairs by
+ * expert, plus the tile list the grouped projections walk (pages: grouped
+ * expert projections with routing and tile reuse).
+ *   topk_ids    int32 [T*k]   pair p = t*k + j goes to expert topk_ids[p]
+ *   counts      int32 [E]     (out) pairs per expert
+ *   offsets     int32 [E+1]   (out) exclusive prefix sum of counts
+ *   sorted_pair int32 [T*k]   (out) pairs grouped by expert, increasing p
+ *                             within an expert
+ *   pair_pos    int32 [T*k]   (out) inverse: pair_pos[sorted_pair[r]] = r
+ *   tiles       int32 [max_tiles][4] (out) (expert, first row, end row, 0):
+ *                             per expert, consecutive runs of at most tile_m
+ *                             sorted rows; experts in increasing order
+ *   n_tiles     int32 [1]     (out) number of tiles written
+ * max_tiles = moe_permute_max_tiles(T, k, E, tile_m).
+ * An id outside [0, E) is skipped: its pair_pos is -1, it is not counted
+ * (offsets[E] < T*k reveals it) and the tail of sorted_pair is -1.
+ * Limits: 1 <= E <= 512, 1 <= tile_m <= 4096, T*k < 2^24.
+ * ------------------------------------------------------------------- */
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E,
+                       int tile_m, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_pair, int32_t* pair_pos,
+                       int32_t* tiles, int32_t* n_tiles, void* stream);
+
+/* Host-side upper bound of n_tiles: min(T*k, floor(T*k / tile_m) + min(E, T*k)). */
+int moe_permute_max_tiles(int T, int k, int E, int tile_m);
+
+/* ---------------------------------------------------------------------
+ * moe_quant_a8_rows -- the dynamic int8 row quantizer of the A8 mode, as a
+ * standalone call (the projections run the same device code internally).
+ *   src   [R][ld] bf16 (src_is_f32 = 0) or fp32 (src_is_f32 = 1); the
+ *         first C entries of each row are quantized
+ *   q     int8 [R][C] (out), s fp32 [R] (out)
+ *   s = fp32(max|row|) / 127 (IEEE division), q = clamp(rint(v / s), -127,
+ *   127) with round half to even; a zero row gives s = 0, q = 0.
+ * ------------------------------------------------------------------- */
+moe_status moe_quant_a8_rows(const void* src, int src_is_f32, int R, int C,
+                             int ld, int8_t* q, float* s, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Workspace of the two projection calls.  One buffer of this size (device
+ * memory, 256-byte aligned) may be passed to both calls of a layer.  Its
+ * first 4 bytes are an error word the kernels OR bits into (bit 0: an
+ * expert descriptor was unusable; bit 1: a tile named an expert outside
+ * [0, E)); the caller zeroes it once and reads it when it wants to.
+ * Rows of h / y: R = T*k + n_shared*T.
+ * ------------------------------------------------------------------- */
+size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
+                           int n_shared, int I_shared);
+
+/* Flags of the projection calls. */
+#define MOE_PATH_AUTO 0       /* choose from the average pairs per expert   */
+#define MOE_PATH_GEMV 1       /* split-K wavefront GEMV (decode shapes)      */
+#define MOE_PATH_MFMA 2       /* MFMA grouped GEMM (prefill shapes)          */
+#define MOE_PATH_MASK 3
+
+/* Tile height the MFMA path is written for; pass it as moe_permute's
+ * tile_m when T*k / E is large (the GEMV path accepts any tile_m). */
+int moe_preferred_tile_m(int act, int T, int E, int k);
+
+/* ---------------------------------------------------------------------
+ * moe_w4_gateup_silu -- grouped gate/up projection of every routed pair
+ * and every shared-expert token, fused with SiLU(g) * u.
+ *   x          bf16 [T][H]
+ *   w13        device table of E moe_qmat, each [2I][H] (gate rows 0..I-1,
+ *              up rows I..2I-1)
+ *   w13_shared device table of n_shared moe_qmat, each [2*I_shared][H]
+ *              (may be null when n_shared = 0)
+ *   offsets, sorted_pair, tiles, n_tiles: from moe_permute (same tile_m)
+ *   h          (out) rows R = T*k + n_shared*T, row stride ld_h =
+ *              max(I, I_shared); row r < T*k is sorted row r, row T*k +
+ *              s*T + t is shared expert s and token t.
+ *              A16: bf16 [R][ld_h] (h rounded to bf16).
+ *              A8 : fp32 [R][ld_h].
+ * ------------------------------------------------------------------- */
+moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H,
+                              int I, int E, int k, const moe_qmat* w13,
+                              const moe_qmat* w13_shared, int n_shared,
+                              int I_shared, const int32_t* offsets,
+                              const int32_t* sorted_pair,
+                              const int32_t* tiles, const int32_t* n_tiles,
+                              int tile_m, void* h, void* workspace,
+                              size_t ws_bytes, int flags, void* stream);
+
+/* ---------------------------------------------------------------------
+ * moe_w4_down_combine -- grouped down projection of every h row and the
+ * weighted combine into the token outputs.
+ *   h          as written by moe_w4_gateup_silu (same act); A8 rows are
+ *              quantized to int8 per row inside this call
+ *   w2         device table of E moe_qmat, each [H][I]
+ *   w2_shared  device table of n_shared moe_qmat, each [H][I_shared]
+ *   topk_w     fp32 [T][k] from moe_route_topk
+ *   pair_pos   from moe_permute
+ *   out        bf16 [T][H] (out): out[t] = sum_j topk_w[t][j] * y(pair
+ *              t*k+j) + sum_s y(shared s, t), summed in fp32 in that order
+ * ------------------------------------------------------------------- */
+moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
+                               int E, int k, const moe_qmat* w2,
+                               const moe_qmat* w2_shared, int n_shared,
+                               int I_shared, const float* topk_w,
+                               const int32_t* offsets,
+                               const int32_t* sorted_pair,
+                               const int32_t* pair_pos, const int32_t* tiles,
+                               const int32_t* n_tiles, int tile_m,
+                               uint16_t* out, void* workspace,
+                               size_t ws_bytes, int flags, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Test hooks of the A8 mode: the same kernels, additionally writing the
+ * exact int32 per-group partial sums they accumulate.
+ *   gate/up: partials [R][2*ld_h][ng_ld], entry (r, n, c) = sum over the
+ *            K indices of group c of qx[t][K] * code[n][K]
+ *   down   : partials [R][H][ng_ld], from this call's own int8 h codes
+ * ng_ld >= K / group of every expert used; entries past an expert's
+ * group count are left untouched.
+ * ------------------------------------------------------------------- */
+moe_status moe_dbg_w4a8_gateup_partials(
+    const uint16_t* x, int T, int H, int I, int E, int k,
+    const moe_qmat* w13, const moe_qmat* w13_shared, int n_shared,
+    int I_shared, const int32_t* offsets, const int32_t* sorted_pair,
+    const int32_t* tiles, const int32_t* n_tiles, int tile_m, void* h,
+    void* workspace, size_t ws_bytes, int32_t* partials, int ng_ld,
+    void* stream);
+
+moe_status moe_dbg_w4a8_down_partials(
+    const void* h, int T, int H, int I, int E, int k, const moe_qmat* w2,
+    const moe_qmat* w2_shared, int n_shared, int I_shared,
+    const float* topk_w, const int32_t* offsets, const int32_t* sorted_pair,
+    const int32_t* pair_pos, const int32_t* tiles, const int32_t* n_tiles,
+    int tile_m, uint16_t* out, void* workspace, size_t ws_bytes,
+    int32_t* partials, int ng_ld, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_W4_H */

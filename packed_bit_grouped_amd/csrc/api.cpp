@@ -1,0 +1,374 @@
+// C ABI of the MoE W4 FFN layer: host-side argument checks, workspace
+// layout, path choice and kernel dispatch.  Nothing here allocates,
+// synchronizes with the device or reads device memory (build log "Two 96 GB
+// Ascend cards run Qwen3.8 Flash-Next", section "Remove sync and launch
+// overhead from the token loop").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+moe_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_E_DEVICE;
+  if (dev < kMaxDevices) {
+    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return MOE_OK;
+    if (c == 2) return MOE_E_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_E_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MOE_OK : MOE_E_DEVICE;
+}
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Shapes shared by both projections.
+moe_status check_layer(int act, int T, int H, int I, int E, int k, int n_shared,
+                       int I_shared, int tile_m, int flags) {
+  if (act != MOE_A16 && act != MOE_A8) return MOE_E_INVAL;
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || n_shared < 0) return MOE_E_INVAL;
+  if (k > E) return MOE_E_INVAL;
+  if (n_shared > 0 && I_shared <= 0) return MOE_E_INVAL;
+  if (tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
+  if (flags & ~MOE_PATH_MASK) return MOE_E_INVAL;
+  if ((flags & MOE_PATH_MASK) == 3) return MOE_E_INVAL;
+  if (H % 32 || I % 32 || (n_shared > 0 && I_shared % 32)) return MOE_E_UNSUPPORTED;
+  if (E > kPermMaxE) return MOE_E_UNSUPPORTED;
+  if ((long long)T * k >= (1LL << 24)) return MOE_E_UNSUPPORTED;
+  if ((long long)T * (k + n_shared) * H >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int ld_h_of(int I, int n_shared, int I_shared) {
+  return n_shared > 0 && I_shared > I ? I_shared : I;
+}
+
+// Work-item size: output units per workgroup such that one pass of the
+// four waves covers them (int4 codes, the common case).
+int gemv_rb(int mode, int K) {
+  const int C_r = K / 32;
+  int seg = C_r & (-C_r);
+  if (seg > 16) seg = 16;
+  const int rows = 4 * (64 / seg);
+  return mode == 0 ? rows / 2 : rows;
+}
+
+bool use_mfma(int act, int T, int E, int k, int flags) {
+  const int path = flags & MOE_PATH_MASK;
+  if (path == MOE_PATH_GEMV) return false;
+  if (path == MOE_PATH_MFMA) return true;
+  return mfma_available() && act == MOE_A16 && (long long)T * k >= 32LL * E;
+}
+
+}  // namespace
+
+namespace moe {
+WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
+                   int I_shared) {
+  (void)I; (void)E; (void)I_shared;
+  WsLayout L;
+  size_t off = 0;
+  L.err = off;
+  off += 256;
+  L.qx = off;
+  if (act == MOE_A8) off += up256((size_t)T * H);
+  L.sx = off;
+  if (act == MOE_A8) off += up256((size_t)T * 4);
+  L.y = off;
+  off += up256((size_t)T * (k + n_shared) * H * 4);
+  L.total = off;
+  return L;
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_W4_ABI_VERSION; }
+
+const char* moe_status_str(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_INVAL: return "invalid argument";
+    case MOE_E_UNSUPPORTED: return "unsupported shape or format";
+    case MOE_E_DEVICE: return "HIP error or device is not gfx950";
+    case MOE_E_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int moe_permute_max_tiles(int T, int k, int E, int tile_m) {
+  if (T <= 0 || k <= 0 || E <= 0 || tile_m <= 0) return 0;
+  const long long P = (long long)T * k;
+  const long long b = P / tile_m + (E < P ? E : P);
+  return (int)(b < P ? b : P);
+}
+
+int moe_preferred_tile_m(int act, int T, int E, int k) {
+  if (use_mfma(act, T, E, k, MOE_PATH_AUTO)) return 64;
+  return 16;
+}
+
+size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
+                           int n_shared, int I_shared) {
+  if (T < 0 || H <= 0 || k <= 0 || n_shared < 0) return 0;
+  return ws_layout(act, T, H, I, E, k, n_shared, I_shared).total;
+}
+
+moe_status moe_route_topk(const float* logits, int T, int E, int k,
+                          int renormalize, int32_t* topk_ids, float* topk_w,
+                          void* stream) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_E_INVAL;
+  if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
+  if (E > kRouteMaxE) return MOE_E_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_E_INVAL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(launch_route_topk(logits, T, E, k, renormalize, topk_ids,
+                                    topk_w, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E,
+                       int tile_m, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_pair, int32_t* pair_pos,
+                       int32_t* tiles, int32_t* n_tiles, void* stream) {
+  if (T < 0 || k <= 0 || E <= 0 || tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
+  if (E > kPermMaxE) return MOE_E_UNSUPPORTED;
+  if ((long long)T * k >= (1LL << 24)) return MOE_E_UNSUPPORTED;
+  if (!counts || !offsets || !n_tiles) return MOE_E_INVAL;
+  if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos || !tiles)) return MOE_E_INVAL;
+  if (tiles && !aligned(tiles, 16)) return MOE_E_INVAL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(launch_permute(topk_ids, T * k, E, tile_m, counts, offsets,
+                                 sorted_pair, pair_pos, tiles, n_tiles,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_quant_a8_rows(const void* src, int src_is_f32, int R, int C,
+                             int ld, int8_t* q, float* s, void* stream) {
+  if (R < 0 || C <= 0 || ld < C) return MOE_E_INVAL;
+  if (src_is_f32 != 0 && src_is_f32 != 1) return MOE_E_INVAL;
+  if (R == 0) return MOE_OK;
+  if (!src || !q || !s) return MOE_E_INVAL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(launch_quant_a8(src, src_is_f32, R, C, ld, q, s,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
+                              int E, int k, const moe_qmat* w13,
+                              const moe_qmat* w13_shared, int n_shared,
+                              int I_shared, const int32_t* offsets,
+                              const int32_t* sorted_pair, const int32_t* tiles,
+                              const int32_t* n_tiles, int tile_m, void* h,
+                              void* workspace, size_t ws_bytes, int flags,
+                              int32_t* partials, int ng_ld, void* stream) {
+  moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w13 || !offsets || !sorted_pair || !tiles || !n_tiles || !h) return MOE_E_INVAL;
+  if (n_shared > 0 && !w13_shared) return MOE_E_INVAL;
+  if (!aligned(x, 16) || !aligned(h, 16) || !aligned(tiles, 16)) return MOE_E_INVAL;
+  const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  if (partials && ng_ld <= 0) return MOE_E_INVAL;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int ld_h = ld_h_of(I, n_shared, I_shared);
+
+  ProjArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.mode = 0;
+  a.ld_in = H;
+  a.w = w13;
+  a.w_sh = w13_shared;
+  a.K = H;
+  a.K_sh = H;
+  a.U = I;
+  a.U_sh = n_shared > 0 ? I_shared : 0;
+  a.T = T;
+  a.k = k;
+  a.P = T * k;
+  a.E = E;
+  a.n_shared = n_shared;
+  a.sorted_pair = sorted_pair;
+  a.tiles = tiles;
+  a.n_tiles = n_tiles;
+  a.max_tiles = moe_permute_max_tiles(T, k, E, tile_m);
+  a.out = h;
+  a.ld_out = ld_h;
+  a.err = reinterpret_cast<int32_t*>(ws + L.err);
+  a.partials = partials;
+  a.ng_ld = ng_ld;
+  a.part_rows = 2 * ld_h;
+
+  if (use_mfma(act, T, E, k, flags)) {
+    a.in_bf16 = x;
+    return from_hip(launch_proj_mfma(a, tile_m, s));
+  }
+  if (act == MOE_A8) {
+    int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
+    float* sx = reinterpret_cast<float*>(ws + L.sx);
+    hipError_t e = launch_quant_a8(x, 0, T, H, H, qx, sx, s);
+    if (e != hipSuccess) return MOE_E_DEVICE;
+    a.in_q = qx;
+    a.in_s = sx;
+  } else {
+    a.in_bf16 = x;
+  }
+  a.maxt = gemv_maxt(T, tile_m);
+  a.sh_tile = a.maxt;
+  a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
+  a.rb = gemv_rb(0, H);
+  const int Umax = a.U > a.U_sh ? a.U : a.U_sh;
+  a.n_rb = (Umax + a.rb - 1) / a.rb;
+  return from_hip(launch_proj_gemv(a, act, s));
+}
+
+static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
+                            int k, const moe_qmat* w2, const moe_qmat* w2_shared,
+                            int n_shared, int I_shared, const float* topk_w,
+                            const int32_t* offsets, const int32_t* sorted_pair,
+                            const int32_t* pair_pos, const int32_t* tiles,
+                            const int32_t* n_tiles, int tile_m, uint16_t* out,
+                            void* workspace, size_t ws_bytes, int flags,
+                            int32_t* partials, int ng_ld, void* stream) {
+  moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!h || !w2 || !topk_w || !offsets || !sorted_pair || !pair_pos || !tiles ||
+      !n_tiles || !out)
+    return MOE_E_INVAL;
+  if (n_shared > 0 && !w2_shared) return MOE_E_INVAL;
+  if (!aligned(h, 16) || !aligned(out, 8) || !aligned(tiles, 16)) return MOE_E_INVAL;
+  const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  if (partials && ng_ld <= 0) return MOE_E_INVAL;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int ld_h = ld_h_of(I, n_shared, I_shared);
+  float* y = reinterpret_cast<float*>(ws + L.y);
+
+  ProjArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.mode = 1;
+  a.ld_in = ld_h;
+  a.w = w2;
+  a.w_sh = w2_shared;
+  a.K = I;
+  a.K_sh = n_shared > 0 ? I_shared : I;
+  a.U = H;
+  a.U_sh = H;
+  a.T = T;
+  a.k = k;
+  a.P = T * k;
+  a.E = E;
+  a.n_shared = n_shared;
+  a.sorted_pair = sorted_pair;
+  a.tiles = tiles;
+  a.n_tiles = n_tiles;
+  a.max_tiles = moe_permute_max_tiles(T, k, E, tile_m);
+  a.out = y;
+  a.ld_out = H;
+  a.err = reinterpret_cast<int32_t*>(ws + L.err);
+  a.partials = partials;
+  a.ng_ld = ng_ld;
+  a.part_rows = H;
+
+  hipError_t e;
+  if (use_mfma(act, T, E, k, flags)) {
+    a.in_bf16 = static_cast<const uint16_t*>(h);
+    e = launch_proj_mfma(a, tile_m, s);
+  } else {
+    if (act == MOE_A8) a.in_f32 = static_cast<const float*>(h);
+    else a.in_bf16 = static_cast<const uint16_t*>(h);
+    a.maxt = gemv_maxt(T, tile_m);
+    a.sh_tile = a.maxt;
+    a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
+    a.rb = gemv_rb(1, a.K < a.K_sh ? a.K : a.K_sh);
+    a.n_rb = (H + a.rb - 1) / a.rb;
+    e = launch_proj_gemv(a, act, s);
+  }
+  if (e != hipSuccess) return MOE_E_DEVICE;
+  return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
+                                 n_shared, out, s));
+}
+
+moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H, int I,
+                              int E, int k, const moe_qmat* w13,
+                              const moe_qmat* w13_shared, int n_shared,
+                              int I_shared, const int32_t* offsets,
+                              const int32_t* sorted_pair,
+                              const int32_t* tiles, const int32_t* n_tiles,
+                              int tile_m, void* h, void* workspace,
+                              size_t ws_bytes, int flags, void* stream) {
+  return gateup_impl(act, x, T, H, I, E, k, w13, w13_shared, n_shared, I_shared,
+                     offsets, sorted_pair, tiles, n_tiles, tile_m, h, workspace,
+                     ws_bytes, flags, nullptr, 0, stream);
+}
+
+moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
+                               int E, int k, const moe_qmat* w2,
+                               const moe_qmat* w2_shared, int n_shared,
+                               int I_shared, const float* topk_w,
+                               const int32_t* offsets,
+                               const int32_t* sorted_pair,
+                               const int32_t* pair_pos, const int32_t* tiles,
+                               const int32_t* n_tiles, int tile_m,
+                               uint16_t* out, void* workspace,
+                               size_t ws_bytes, int flags, void* stream) {
+  return down_impl(act, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared,
+                   topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles,
+                   tile_m, out, workspace, ws_bytes, flags, nullptr, 0, stream);
+}
+
+moe_status moe_dbg_w4a8_gateup_partials(
+    const uint16_t* x, int T, int H, int I, int E, int k,
+    const moe_qmat* w13, const moe_qmat* w13_shared, int n_shared,
+    int I_shared, const int32_t* offsets, const int32_t* sorted_pair,
+    const int32_t* tiles, const int32_t* n_tiles, int tile_m, void* h,
+    void* workspace, size_t ws_bytes, int32_t* partials, int ng_ld,
+    void* stream) {
+  if (!partials) return MOE_E_INVAL;
+  return gateup_impl(MOE_A8, x, T, H, I, E, k, w13, w13_shared, n_shared,
+                     I_shared, offsets, sorted_pair, tiles, n_tiles, tile_m, h,
+                     workspace, ws_bytes, MOE_PATH_GEMV, partials, ng_ld, stream);
+}
+
+moe_status moe_dbg_w4a8_down_partials(
+    const void* h, int T, int H, int I, int E, int k, const moe_qmat* w2,
+    const moe_qmat* w2_shared, int n_shared, int I_shared,
+    const float* topk_w, const int32_t* offsets, const int32_t* sorted_pair,
+    const int32_t* pair_pos, const int32_t* tiles, const int32_t* n_tiles,
+    int tile_m, uint16_t* out, void* workspace, size_t ws_bytes,
+    int32_t* partials, int ng_ld, void* stream) {
+  if (!partials) return MOE_E_INVAL;
+  return down_impl(MOE_A8, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared,
+                   topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles,
+                   tile_m, out, workspace, ws_bytes, MOE_PATH_GEMV, partials,
+                   ng_ld, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int kPermMaxE = 512;      // permute: experts per launch
+constexpr int kPermIdBits = 9;      // bits of an expert id below kPermMaxE
+constexpr int kRouteMaxE = 1024;    // route: 16 logits per lane
+
+// Workspace layout (byte offsets from the workspace base).
+struct WsLayout {
+  size_t err;        // int32 error word
+  size_t qx;         // A8: int8 [T][H]
+  size_t sx;         // A8: fp32 [T]
+  size_t y;          // fp32 [R][H]
+  size_t total;
+};
+WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
+                   int I_shared);
+
+// Arguments of the grouped projections (both kernels families).
+struct ProjArgs {
+  int mode;                    // 0: gate/up (+SiLU*mul), 1: down
+  // inputs
+  const uint16_t* in_bf16;     // A16: x [T][H] (gate/up) or h [R][ld_in] (down)
+  const float* in_f32;         // A8 down: h fp32 [R][ld_in]
+  const int8_t* in_q;          // A8 gate/up: qx [T][H]
+  const float* in_s;           // A8 gate/up: sx [T]
+  int ld_in;
+  // weights
+  const moe_qmat* w;           // routed experts
+  const moe_qmat* w_sh;        // shared experts
+  int K, K_sh;                 // reduction length (routed / shared)
+  int U, U_sh;                 // output units per expert: I pairs (gate/up), H rows (down)
+  // routing
+  int T, k, P, E, n_shared;
+  const int32_t* sorted_pair;
+  const int32_t* tiles;
+  const int32_t* n_tiles;
+  int max_tiles;               // host upper bound of *n_tiles
+  int maxt;                    // activation rows staged per pass (1, 2, 4, 8)
+  int sh_tile;                 // tokens per shared-expert tile
+  int n_sh_slots;              // n_shared * ceil(T / sh_tile)
+  int rb;                      // units per work item
+  int n_rb;                    // work items per tile
+  // outputs
+  void* out;                   // gate/up: h (bf16 or fp32); down: y fp32
+  int ld_out;
+  int32_t* err;
+  int32_t* partials;           // A8 test hook (null otherwise)
+  int ng_ld;
+  int part_rows;               // row stride (in weight rows) of partials
+};
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k,
+                             int renorm, int32_t* ids, float* w, hipStream_t st);
+hipError_t launch_permute(const int32_t* ids, int P, int E, int tile_m,
+                          int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos,
+                          int32_t* tiles, int32_t* n_tiles, hipStream_t st);
+hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
+                           int8_t* q, float* s, hipStream_t st);
+hipError_t launch_proj_gemv(const ProjArgs& a, int act, hipStream_t st);
+int gemv_maxt(int T, int tile_m);
+hipError_t launch_proj_mfma(const ProjArgs& a, int tile_m, hipStream_t st);
+bool mfma_available();
+hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
+                          const int32_t* pair_pos, int T, int k, int H, int P,
+                          int n_shared, uint16_t* out, hipStream_t st);
+
+}  // namespace moe

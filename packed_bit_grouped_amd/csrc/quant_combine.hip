@@ -1,0 +1,87 @@
+// Dynamic int8 row quantizer (the W4A8 mode of the build log "Two 96 GB
+// Ascend cards run Qwen3.8 Flash-Next", section "Keep low-bit weights
+// packed, do the work on the NPU") and the weighted combine of expert
+// outputs into token outputs.
+#include "moe_internal.h"
+
+namespace moe {
+
+// One workgroup (256 threads) per row: amax by block reduction, then the
+// shared a8_scale / a8_code rule.
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const void* __restrict__ src, int is_f32, int C, int ld,
+    int8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* rb = static_cast<const uint16_t*>(src) + (size_t)r * ld;
+  const float* rf = static_cast<const float*>(src) + (size_t)r * ld;
+  float amax = 0.0f;
+  for (int c = tid; c < C; c += 256) {
+    const float v = is_f32 ? rf[c] : bf16_to_f32(rb[c]);
+    amax = fmaxf(amax, fabsf(v));
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = a8_scale(amax);
+  for (int c = tid; c < C; c += 256) {
+    const float v = is_f32 ? rf[c] : bf16_to_f32(rb[c]);
+    q[(size_t)r * C + c] = (int8_t)a8_code(v, sc);
+  }
+  if (tid == 0) s[r] = sc;
+}
+
+hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
+                           int8_t* q, float* s, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  quant_rows_kernel<<<R, 256, 0, st>>>(src, is_f32, C, ld, q, s);
+  return hipGetLastError();
+}
+
+// out[t][n] = bf16( sum_j w[t][j] * y[pair_pos[t*k+j]][n] + sum_s y[P+s*T+t][n] ),
+// accumulated in fp32 in that fixed order (deterministic).  Four outputs
+// per thread with 16-byte loads.
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ y, int ld_y, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ pair_pos, int T, int k, int H, int P,
+    int n_shared, uint16_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int pp = pair_pos[t * k + j];
+    if (pp < 0) continue;
+    const float wj = topk_w[t * k + j];
+    const float4 v = *reinterpret_cast<const float4*>(y + (size_t)pp * ld_y + n);
+    acc.x = fmaf(wj, v.x, acc.x);
+    acc.y = fmaf(wj, v.y, acc.y);
+    acc.z = fmaf(wj, v.z, acc.z);
+    acc.w = fmaf(wj, v.w, acc.w);
+  }
+  for (int s = 0; s < n_shared; ++s) {
+    const float4 v =
+        *reinterpret_cast<const float4*>(y + (size_t)(P + s * T + t) * ld_y + n);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  uint2 o;
+  o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
+  o.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
+  *reinterpret_cast<uint2*>(out + (size_t)t * H + n) = o;
+}
+
+hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
+                          const int32_t* pair_pos, int T, int k, int H, int P,
+                          int n_shared, uint16_t* out, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((H / 4 + 255) / 256, T);
+  combine_kernel<<<grid, 256, 0, st>>>(y, ld_y, topk_w, pair_pos, T, k, H, P,
+                                       n_shared, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,227 @@
+// Router top-k with softmax gating, and the stable counting sort of
+// (token, expert) pairs by expert, on the device.
+//
+// Build log "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", sections
+// "Keep low-bit weights packed, do the work on the NPU" (tokens are routed
+// to experts on the device, grouped projections with routing and tile
+// reuse) and "Remove sync and launch overhead from the token loop" (no
+// device-to-host scalar reads; routing moved off the host).
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------
+// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a
+// wave arg-max with the order (value descending, index ascending) pick the
+// experts; the gate weights are exp(l_j - l_max) over their sum (the
+// softmax over the chosen logits) or over all E logits (renormalize = 0).
+template <int NV>
+__global__ __launch_bounds__(256) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm,
+    int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[NV];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? row[e] : -INFINITY;
+    if (e >= E) taken |= 1u << j;
+  }
+  float top = 0.0f, denom = 0.0f;
+  float sel_ex[NV];
+  int sel_id[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) { sel_ex[j] = 0.0f; sel_id[j] = 0; }
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = lane + 64 * j;
+      if (!((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (r == 0) top = bv;
+    const float ex = expf(bv - top);
+    denom += ex;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (r == lane + 64 * j) { sel_ex[j] = ex; sel_id[j] = bi; }
+  }
+  if (!renorm) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (lane + 64 * j < E) s += expf(v[j] - top);
+    denom = wave_sum(s);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int r = lane + 64 * j;
+    if (r < k) {
+      ids[(size_t)t * k + r] = sel_id[j];
+      w[(size_t)t * k + r] = sel_ex[j] / denom;
+    }
+  }
+}
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k,
+                             int renorm, int32_t* ids, float* w,
+                             hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((T + 3) / 4), block(256);
+  const int nv = (E + 63) / 64;
+  if (nv <= 1)
+    route_topk_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
+  else if (nv <= 2)
+    route_topk_kernel<2><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
+  else if (nv <= 4)
+    route_topk_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
+  else if (nv <= 8)
+    route_topk_kernel<8><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
+  else
+    route_topk_kernel<16><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------
+// Stable counting sort in one workgroup of 16 waves.
+//  1. Wave w owns the contiguous pair range [w*seg, (w+1)*seg) and counts
+//     its pairs per expert in LDS (integer atomics: exact).
+//  2. Per expert: total, the base of each wave's range inside the expert
+//     (prefix over waves), the exclusive scan over experts -> offsets, and
+//     the tile list (ceil(count / tile_m) tiles per expert).
+//  3. Each wave walks its range in order, 64 pairs at a time: lanes with
+//     the same expert find each other with ballots over the expert id's
+//     bits, rank = number of such lanes below, and the last of them
+//     advances the wave's cursor for that expert.  Ranges are in pair
+//     order and bases are prefix sums over waves, so within an expert the
+//     pairs land in increasing p: the sort is stable.
+constexpr int kPermWaves = 16;
+
+__device__ int block_exclusive_scan(int v, int* tmp /* kPermWaves + 1 */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < kPermWaves; ++i) {
+      const int c = tmp[i];
+      tmp[i] = run;
+      run += c;
+    }
+    tmp[kPermWaves] = run;
+  }
+  __syncthreads();
+  const int r = tmp[wave] + incl - v;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void permute_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int tile_m,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ int hist[kPermWaves * kPermMaxE];
+  __shared__ int tmp[kPermWaves + 1];
+  __shared__ int total_valid;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kPermWaves * kPermMaxE; i += 1024) hist[i] = 0;
+  __syncthreads();
+  const int seg = (P + kPermWaves - 1) / kPermWaves;
+  const int p0 = min(P, wave * seg), p1 = min(P, p0 + seg);
+  for (int p = p0 + lane; p < p1; p += 64) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave * kPermMaxE + e], 1);
+  }
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E) {
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = hist[w * kPermMaxE + tid];
+      hist[w * kPermMaxE + tid] = cnt;
+      cnt += c;
+    }
+  }
+  const int excl = block_exclusive_scan(cnt, tmp);
+  const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
+  const int texcl = block_exclusive_scan(ntile, tmp);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = excl;
+    for (int w = 0; w < kPermWaves; ++w) hist[w * kPermMaxE + tid] += excl;
+    for (int i = 0; i < ntile; ++i) {
+      const int r0 = excl + i * tile_m;
+      int4 tl;
+      tl.x = tid;
+      tl.y = r0;
+      tl.z = min(r0 + tile_m, excl + cnt);
+      tl.w = 0;
+      reinterpret_cast<int4*>(tiles)[texcl + i] = tl;
+    }
+    if (tid == E - 1) {
+      offsets[E] = excl + cnt;
+      *n_tiles = texcl + ntile;
+      total_valid = excl + cnt;
+    }
+  }
+  __syncthreads();
+  const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    const bool in = p < p1;
+    const int e = in ? ids[p] : -1;
+    const bool valid = in && (unsigned)e < (unsigned)E;
+    unsigned long long m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kPermIdBits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const unsigned long long bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    if (valid) {
+      const int pos = hist[wave * kPermMaxE + e] + __popcll(m & below);
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+      if ((m >> lane) == 1ull) hist[wave * kPermMaxE + e] = pos + 1;
+    } else if (in) {
+      pair_pos[p] = -1;
+    }
+  }
+  __syncthreads();
+  for (int i = total_valid + tid; i < P; i += 1024) sorted_pair[i] = -1;
+}
+
+hipError_t launch_permute(const int32_t* ids, int P, int E, int tile_m,
+                          int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos,
+                          int32_t* tiles, int32_t* n_tiles, hipStream_t st) {
+  permute_kernel<<<1, 1024, 0, st>>>(ids, P, E, tile_m, counts, offsets,
+                                     sorted_pair, pair_pos, tiles, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,60 @@
+"""Helpers of the GPU parity tests: run the layer through the C ABI and
+bring every intermediate back to the host (the host copies happen here,
+in the test, never inside the layer)."""
+import numpy as np
+
+ACTS = {"a16": 0, "a8": 1}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def bf16_bits_to_f64(u16):
+    u = np.asarray(u16).astype(np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def run_layer_gpu(dl, act=None, tile_m=None, flags=0, stream=None):
+    """Run one layer step on the device; returns host copies of everything."""
+    torch = torch_mod()
+    B = dl.buffers(act, tile_m)
+    dl.run(B, flags, stream)
+    torch.cuda.synchronize()
+    return collect(B), B
+
+
+def collect(B):
+    torch = torch_mod()
+    nt = int(B.n_tiles.item())
+    res = {
+        "ids": to_np(B.ids)[:B.T], "w": to_np(B.w)[:B.T].astype(np.float64),
+        "counts": to_np(B.counts), "offsets": to_np(B.offsets),
+        "sorted_pair": to_np(B.sorted_pair)[:B.P], "pair_pos": to_np(B.pair_pos)[:B.P],
+        "tiles": to_np(B.tiles)[:nt], "n_tiles": nt,
+        "out": bf16_bits_to_f64(to_np(B.out)[:B.T]),
+        "err": int(B.ws[:4].view(torch.int32).item()),
+    }
+    if B.act == 0:
+        res["h"] = bf16_bits_to_f64(to_np(B.h)[:B.R])
+    else:
+        res["h32"] = to_np(B.h)[:B.R].astype(np.float32)
+    return res
+
+
+def float_gate(got, ref, rel_l2=5e-3, max_abs_frac=2e-2):
+    """rel-L2 <= 5e-3 and max-abs <= 2e-2 * rms(ref).  Returns the errors."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    nref = np.linalg.norm(ref)
+    rl2 = np.linalg.norm(d) / nref if nref > 0 else np.linalg.norm(d)
+    rms = np.sqrt(np.mean(ref ** 2)) if ref.size else 0.0
+    mabs = np.abs(d).max() if d.size else 0.0
+    ok = rl2 <= rel_l2 and mabs <= max_abs_frac * rms if rms > 0 else mabs == 0
+    return ok, rl2, mabs, rms

@@ -1,0 +1,145 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, reports its ABI version, sizes buffers, and rejects bad
+arguments on the host before touching any device (no compute here)."""
+import os
+import re
+
+import pytest
+
+from packed_bit_grouped_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4.h")
+
+lib = pytest.importorskip("ctypes")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(
+        r"^\s*(?:moe_status|int|size_t|const char\s*\*)\s+(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.load()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.EXPORTED, n
+
+
+def test_abi_version_matches_header():
+    text = open(HEADER).read()
+    v = int(re.search(r"#define MOE_W4_ABI_VERSION (\d+)", text).group(1))
+    assert L.moe_abi_version() == v == L.ABI_VERSION
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(L.status_str(s), str) and L.status_str(s)
+
+
+def test_max_tiles_bound():
+    # min(P, floor(P / tile_m) + min(E, P))
+    assert L.moe_permute_max_tiles(1, 8, 128, 16) == 8
+    assert L.moe_permute_max_tiles(12, 8, 128, 16) == 96
+    assert L.moe_permute_max_tiles(4096, 8, 256, 64) == 512 + 256
+    assert L.moe_permute_max_tiles(0, 8, 256, 64) == 0
+
+
+def test_workspace_sizes():
+    # error word + fp32 y rows (+ int8 x and fp32 scales for A8), 256-aligned
+    assert L.moe_workspace_bytes(0, 1, 2048, 768, 128, 8, 1, 768) == 256 + 9 * 2048 * 4
+    a8 = L.moe_workspace_bytes(1, 64, 2048, 768, 128, 8, 0, 0)
+    assert a8 == 256 + 64 * 2048 + 256 + 512 * 2048 * 4
+    assert L.moe_workspace_bytes(0, 0, 2048, 768, 128, 8, 0, 0) == 256
+
+
+FAKE = 1 << 20   # a non-null pointer value; never dereferenced on the host
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, 4, 0, 1, 1, FAKE, FAKE), L.MOE_E_INVAL),       # E = 0
+    ((FAKE, 4, 8, 9, 1, FAKE, FAKE), L.MOE_E_INVAL),       # k > E
+    ((FAKE, 4, 8, 0, 1, FAKE, FAKE), L.MOE_E_INVAL),       # k = 0
+    ((FAKE, 4, 8, 2, 2, FAKE, FAKE), L.MOE_E_INVAL),       # renormalize not 0/1
+    ((FAKE, -1, 8, 2, 1, FAKE, FAKE), L.MOE_E_INVAL),      # T < 0
+    ((None, 4, 8, 2, 1, FAKE, FAKE), L.MOE_E_INVAL),       # null logits
+    ((FAKE, 4, 2000, 2, 1, FAKE, FAKE), L.MOE_E_UNSUPPORTED),  # E > 1024
+    ((None, 0, 8, 2, 1, None, None), L.MOE_OK),            # T = 0: nothing to do
+])
+def test_route_validation(args, code):
+    assert L.moe_route_topk(*args, stream=0, check=False) == code
+
+
+def test_permute_validation():
+    ok = dict(topk_ids=FAKE, T=4, k=2, E=8, tile_m=16, counts=FAKE, offsets=FAKE,
+              sorted_pair=FAKE, pair_pos=FAKE, tiles=FAKE, n_tiles=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_permute(*a.values(), stream=0, check=False)
+    assert call(E=600) == L.MOE_E_UNSUPPORTED
+    assert call(tile_m=0) == L.MOE_E_INVAL
+    assert call(counts=None) == L.MOE_E_INVAL
+    assert call(tiles=FAKE + 4) == L.MOE_E_INVAL      # tiles must be 16-byte aligned
+    assert call(T=1 << 22, k=8) == L.MOE_E_UNSUPPORTED
+
+
+def _gateup(**kw):
+    a = dict(act=0, x=FAKE, T=4, H=256, I=128, E=8, k=2, w13=FAKE, w13_shared=None,
+             n_shared=0, I_shared=0, offsets=FAKE, sorted_pair=FAKE, tiles=FAKE,
+             n_tiles=FAKE, tile_m=16, h=FAKE, workspace=FAKE, ws_bytes=1 << 30, flags=0)
+    a.update(kw)
+    return L.moe_w4_gateup_silu(*a.values(), stream=0, check=False)
+
+
+def test_gateup_validation():
+    assert _gateup(act=2) == L.MOE_E_INVAL
+    assert _gateup(k=9) == L.MOE_E_INVAL
+    assert _gateup(H=250) == L.MOE_E_UNSUPPORTED         # K % 32
+    assert _gateup(I=100) == L.MOE_E_UNSUPPORTED
+    assert _gateup(n_shared=1, I_shared=0) == L.MOE_E_INVAL
+    assert _gateup(n_shared=1, I_shared=128, w13_shared=None) == L.MOE_E_INVAL
+    assert _gateup(x=None) == L.MOE_E_INVAL
+    assert _gateup(x=FAKE + 2) == L.MOE_E_INVAL          # 16-byte alignment
+    assert _gateup(ws_bytes=16) == L.MOE_E_WORKSPACE
+    assert _gateup(workspace=None) == L.MOE_E_WORKSPACE
+    assert _gateup(workspace=FAKE + 64) == L.MOE_E_WORKSPACE  # 256-byte alignment
+    assert _gateup(flags=3) == L.MOE_E_INVAL
+    assert _gateup(flags=8) == L.MOE_E_INVAL
+    assert _gateup(E=600, k=2) == L.MOE_E_UNSUPPORTED
+    assert _gateup(T=0, x=None) == L.MOE_OK               # empty batch
+    # everything valid: only the device check remains, and there is no GPU here
+    assert _gateup() == L.MOE_E_DEVICE
+
+
+def test_down_validation():
+    a = dict(act=0, h=FAKE, T=4, H=256, I=128, E=8, k=2, w2=FAKE, w2_shared=None,
+             n_shared=0, I_shared=0, topk_w=FAKE, offsets=FAKE, sorted_pair=FAKE,
+             pair_pos=FAKE, tiles=FAKE, n_tiles=FAKE, tile_m=16, out=FAKE,
+             workspace=FAKE, ws_bytes=1 << 30, flags=0)
+
+    def call(**kw):
+        b = dict(a, **kw)
+        return L.moe_w4_down_combine(*b.values(), stream=0, check=False)
+    assert call(topk_w=None) == L.MOE_E_INVAL
+    assert call(pair_pos=None) == L.MOE_E_INVAL
+    assert call(out=FAKE + 2) == L.MOE_E_INVAL
+    assert call(ws_bytes=100) == L.MOE_E_WORKSPACE
+    assert call(T=0, h=None) == L.MOE_OK
+    assert call() == L.MOE_E_DEVICE
+
+
+def test_quant_validation():
+    assert L.moe_quant_a8_rows(FAKE, 2, 4, 8, 8, FAKE, FAKE, stream=0, check=False) == L.MOE_E_INVAL
+    assert L.moe_quant_a8_rows(FAKE, 0, 4, 8, 4, FAKE, FAKE, stream=0, check=False) == L.MOE_E_INVAL
+    assert L.moe_quant_a8_rows(None, 0, 0, 8, 8, None, None, stream=0, check=False) == L.MOE_OK
+
+
+def test_debug_hooks_need_partials():
+    assert L.moe_dbg_w4a8_gateup_partials(
+        FAKE, 4, 256, 128, 8, 2, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, 16,
+        FAKE, FAKE, 1 << 30, None, 8, stream=0, check=False) == L.MOE_E_INVAL

@@ -1,0 +1,381 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer stages (routing ids, counts, offsets, permutation, tiles, A8 codes
+and int32 per-group partials) must match bit for bit; float outputs must
+have rel-L2 <= 5e-3 and max-abs <= 2e-2 * rms(oracle).  Sizes: the small
+layers the oracle finishes in seconds (several tiles, ragged tails, int2
+and int4 experts, shared experts), the decode layers at full size, and the
+prefill layer at full size on a sample of tokens.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import CONFIGS, LayerConfig, make_layer
+from tests.gpu_util import (bf16_bits_to_f64, collect, float_gate, run_layer_gpu,
+                            to_np, torch_mod)
+from tests.minis import MINIS
+
+pytestmark = pytest.mark.gpu
+
+MID = {
+    # several tiles per expert, ragged tails, mixed int2/int4, shared expert
+    "mid_mixed": LayerConfig("mid_mixed", 200, T=100, H=512, E=16, k=4, I=256,
+                             group=64, n_int2=5, group_int2=64, n_shared=1,
+                             I_shared=192),
+    "mid_mixed_a8": LayerConfig("mid_mixed_a8", 201, T=70, H=512, E=12, k=3,
+                                I=320, group=32, n_int2=4, group_int2=32,
+                                act="a8"),
+    "mid_g128_a8_shared": LayerConfig("mid_g128_a8_shared", 202, T=33, H=1024,
+                                      E=20, k=6, I=384, group=128, n_int2=3,
+                                      group_int2=128, n_shared=2, I_shared=256,
+                                      act="a8"),
+    "mid_g256": LayerConfig("mid_g256", 203, T=9, H=768, E=10, k=2, I=512,
+                            group=256, n_int2=2, group_int2=256),
+}
+
+_cache = {}
+
+
+def _layer(cfg):
+    key = (cfg.name, cfg.key)
+    if key not in _cache:
+        _cache[key] = make_layer(cfg)
+    return _cache[key]
+
+
+def _dev(cfg):
+    from packed_bit_grouped_amd.layer import DeviceLayer
+    print(f"[parity] {cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}",
+          flush=True)
+    return DeviceLayer.from_synth(_layer(cfg))
+
+
+def _check_integer_stages(g, o, cfg):
+    assert np.array_equal(g["ids"], o["ids"])
+    assert np.allclose(g["w"], o["w"], rtol=2e-6, atol=1e-7)
+    assert np.allclose(g["w"].sum(1), 1.0, atol=2e-6) or not cfg.renormalize
+    for key in ("counts", "offsets", "sorted_pair", "pair_pos"):
+        assert np.array_equal(g[key], o[key]), key
+    assert np.array_equal(g["tiles"][:, :3], o["tiles"]), "tiles"
+    assert g["err"] == 0
+
+
+def _check_layer(cfg, act=None, tile_m=16, flags=0):
+    act = act or cfg.act
+    dl = _dev(cfg)
+    g, B = run_layer_gpu(dl, act, tile_m, flags)
+    o = oracle.oracle_layer(_layer(cfg), act=act, tile_m=tile_m)
+    _check_integer_stages(g, o, cfg)
+    if act == "a16":
+        ok, rl2, mabs, rms = float_gate(g["h"], o["h"])
+        assert ok, ("h", rl2, mabs, rms)
+    else:
+        ok, rl2, mabs, rms = float_gate(g["h32"], o["h32"])
+        assert ok, ("h", rl2, mabs, rms)
+    ok, rl2, mabs, rms = float_gate(g["out"], o["out"])
+    print(f"[parity] {cfg.name} {act}: out rel-L2 {rl2:.2e} max-abs {mabs:.2e} "
+          f"(gate {2e-2 * rms:.2e})", flush=True)
+    assert ok, ("out", rl2, mabs, rms)
+    return g, o, dl, B
+
+
+@pytest.mark.parametrize("name", list(MINIS) + list(MID))
+def test_small_layers(name):
+    cfg = MINIS.get(name) or MID[name]
+    _check_layer(cfg)
+
+
+@pytest.mark.parametrize("name", ["c0", "mixed_shared", "mid_mixed"])
+def test_small_layers_as_a8(name):
+    cfg = MINIS.get(name) or MID[name]
+    _check_layer(cfg, act="a8")
+
+
+@pytest.mark.parametrize("tile_m", [1, 3, 16, 64])
+def test_tile_sizes(tile_m):
+    _check_layer(MID["mid_mixed"], tile_m=tile_m)
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2, 3])
+def test_benchmark_layers_full(cid):
+    _check_layer(CONFIGS[cid])
+
+
+def test_route_ties_and_large_E():
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    rng = np.random.default_rng(1)
+    for T, E, k in [(37, 288, 8), (5, 1024, 33), (9, 4, 4), (64, 64, 64), (3, 1, 1)]:
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        lg[:, 1::7] = lg[:, 0:1]                 # many exact ties
+        lg[0] = 0.5
+        if E > 3:
+            lg[1, 3] = -0.0
+            lg[1, 2] = 0.0
+        dl = torch.from_numpy(lg).cuda()
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        for renorm in (1, 0):
+            L.moe_route_topk(dl, T, E, k, renorm, ids, w)
+            torch.cuda.synchronize()
+            oi, ow = oracle.route_topk(lg, k, renorm)
+            assert np.array_equal(to_np(ids), oi), (T, E, k)
+            assert np.allclose(to_np(w), ow, rtol=2e-6, atol=1e-7)
+
+
+def test_permute_edge_cases():
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    rng = np.random.default_rng(2)
+    cases = [(1, 8, 128, 16), (4096, 8, 256, 64), (333, 5, 17, 7), (50, 4, 512, 1),
+             (2, 3, 3, 4096)]
+    for T, k, E, tile_m in cases:
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        _permute_check(torch, L, ids, E, tile_m)
+    # duplicates within a token and a skewed distribution
+    ids = rng.integers(0, 3, size=(200, 6)).astype(np.int32)
+    _permute_check(torch, L, ids, 40, 5)
+
+
+def _permute_check(torch, L, ids, E, tile_m):
+    T, k = ids.shape
+    P = T * k
+    d = torch.from_numpy(ids).cuda()
+    mt = L.moe_permute_max_tiles(T, k, E, tile_m)
+    bufs = [torch.full((n,), -7, dtype=torch.int32, device="cuda")
+            for n in (E, E + 1, P, P)]
+    tiles = torch.full((max(mt, 1), 4), -7, dtype=torch.int32, device="cuda")
+    nt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.moe_permute(d, T, k, E, tile_m, *bufs, tiles, nt)
+    torch.cuda.synchronize()
+    o = oracle.permute(ids, E, tile_m)
+    for key, b in zip(("counts", "offsets", "sorted_pair", "pair_pos"), bufs):
+        assert np.array_equal(to_np(b), o[key]), (key, T, k, E, tile_m)
+    n = int(nt.item())
+    assert n == len(o["tiles"]) <= mt
+    assert np.array_equal(to_np(tiles)[:n, :3], o["tiles"])
+
+
+def test_permute_skips_out_of_range_ids():
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    ids = np.array([[0, 5], [7, 1], [-1, 2], [3, 8]], dtype=np.int32)   # E = 8
+    T, k, E = 4, 2, 8
+    d = torch.from_numpy(ids).cuda()
+    c, off = (torch.zeros(E, dtype=torch.int32, device="cuda"),
+              torch.zeros(E + 1, dtype=torch.int32, device="cuda"))
+    sp, pp = (torch.zeros(8, dtype=torch.int32, device="cuda"),
+              torch.zeros(8, dtype=torch.int32, device="cuda"))
+    tiles = torch.zeros((L.moe_permute_max_tiles(T, k, E, 4), 4), dtype=torch.int32,
+                        device="cuda")
+    nt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L.moe_permute(d, T, k, E, 4, c, off, sp, pp, tiles, nt)
+    torch.cuda.synchronize()
+    valid = ids.ravel()[(ids.ravel() >= 0) & (ids.ravel() < E)]
+    assert int(to_np(off)[E]) == valid.size == 6
+    assert to_np(pp)[4] == -1 and to_np(pp)[7] == -1
+    assert list(to_np(sp)[6:]) == [-1, -1]
+    assert np.array_equal(to_np(c), np.bincount(valid, minlength=E))
+
+
+def test_a8_quantizer_bit_exact():
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    rng = np.random.default_rng(3)
+    rows = (rng.standard_normal((50, 777)) * rng.uniform(1e-3, 300, (50, 1))).astype(np.float32)
+    rows[4] = 0
+    rows[5, :] = rows[5, 0]
+    rows[6, ::3] = 127.0 * 0.5      # exact ties at amax = 127 * 0.5 * ...
+    for src_is_f32 in (1, 0):
+        if src_is_f32:
+            src = torch.from_numpy(rows).cuda()
+            ref_rows = rows
+        else:
+            from synth.gen import bf16_bits_from_f32
+            bits = bf16_bits_from_f32(rows)
+            src = torch.from_numpy(bits.view(np.int16)).cuda()
+            ref_rows = bf16_bits_to_f64(bits).astype(np.float32)
+        q = torch.empty((50, 777), dtype=torch.int8, device="cuda")
+        s = torch.empty(50, dtype=torch.float32, device="cuda")
+        L.moe_quant_a8_rows(src, src_is_f32, 50, 777, 777, q, s)
+        torch.cuda.synchronize()
+        oq, os_ = oracle.quant_rows_a8(ref_rows)
+        assert np.array_equal(to_np(q), oq)
+        assert np.array_equal(to_np(s), os_)
+
+
+@pytest.mark.parametrize("name", ["c3", "mid_mixed_a8", "mid_g128_a8_shared", "mixed_shared_a8"])
+def test_a8_partials_bit_exact(name):
+    """Stage 1: int32 per-group partials of int8 x against int codes equal
+    the oracle's exactly.  Stage 2: the down call's int8 h codes equal the
+    oracle quantizer applied to the GPU's fp32 h, and its int32 partials
+    equal the oracle's partials computed from those codes."""
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    cfg = CONFIGS[3] if name == "c3" else (MINIS.get(name) or MID[name])
+    layer = _layer(cfg)
+    dl = _dev(cfg)
+    B = dl.buffers("a8", 16)
+    c = cfg
+    L.moe_route_topk(dl.logits, c.T, c.E, c.k, c.renormalize, B.ids, B.w)
+    L.moe_permute(B.ids, c.T, c.k, c.E, B.tile_m, B.counts, B.offsets, B.sorted_pair,
+                  B.pair_pos, B.tiles, B.n_tiles)
+    ng1 = c.H // 32
+    ng2 = B.ld_h // 32
+    p1 = torch.full((B.R, 2 * B.ld_h, ng1), -(1 << 30), dtype=torch.int32, device="cuda")
+    p2 = torch.full((B.R, c.H, ng2), -(1 << 30), dtype=torch.int32, device="cuda")
+    L.moe_dbg_w4a8_gateup_partials(dl.x, c.T, c.H, c.I, c.E, c.k, dl.bank.w13,
+                                   dl.bank.w13_sh, c.n_shared, c.I_shared, B.offsets,
+                                   B.sorted_pair, B.tiles, B.n_tiles, B.tile_m, B.h,
+                                   B.ws, B.ws_bytes, p1, ng1)
+    L.moe_dbg_w4a8_down_partials(B.h, c.T, c.H, c.I, c.E, c.k, dl.bank.w2, dl.bank.w2_sh,
+                                 c.n_shared, c.I_shared, B.w, B.offsets, B.sorted_pair,
+                                 B.pair_pos, B.tiles, B.n_tiles, B.tile_m, B.out, B.ws,
+                                 B.ws_bytes, p2, ng2)
+    torch.cuda.synchronize()
+    g = collect(B)
+    ids, _ = oracle.route_topk(layer.logits, c.k, c.renormalize)
+    perm = oracle.permute(ids, c.E, 16)
+    o1 = oracle.gateup_a8(layer, perm, want_partials=True)
+    P1 = to_np(p1)
+    for (e, s), (rows, Pg) in o1["partials"].items():
+        ex = layer.experts[e] if s is None else layer.shared[s]
+        n2, ng = ex.w13.N, ex.w13.K // ex.w13.group
+        assert np.array_equal(P1[rows, :n2, :ng], Pg), ("stage1", e, s)
+    # stage 2 from the GPU's own fp32 h
+    h32 = g["h32"]
+    qh = np.zeros((B.R, B.ld_h), np.int8)
+    sh = np.zeros(B.R, np.float32)
+    for e_, rows, s, toks in oracle.expert_rows(perm, c.E, c.T, c.n_shared):
+        I_e = (layer.experts[e_] if s is None else layer.shared[s]).w2.K
+        q_, s_ = oracle.quant_rows_a8(h32[rows, :I_e])
+        qh[rows, :I_e] = q_
+        sh[rows] = s_
+    qg = torch.empty((B.R, B.ld_h), dtype=torch.int8, device="cuda")
+    sg = torch.empty(B.R, dtype=torch.float32, device="cuda")
+    # the same rows quantized by the library's own quantizer
+    qg.zero_()
+    for e_, rows, s, toks in oracle.expert_rows(perm, c.E, c.T, c.n_shared):
+        I_e = (layer.experts[e_] if s is None else layer.shared[s]).w2.K
+        r0 = int(rows[0])
+        qt = torch.empty((len(rows), I_e), dtype=torch.int8, device="cuda")
+        L.moe_quant_a8_rows(B.h[r0:], 1, len(rows), I_e, B.ld_h, qt, sg[r0:])
+        qg[r0:r0 + len(rows), :I_e] = qt
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(qg), qh)
+    assert np.array_equal(to_np(sg), sh)
+    _, parts2 = oracle.down_a8(layer, perm, qh, sh, want_partials=True)
+    P2 = to_np(p2)
+    for (e, s), (rows, Pg) in parts2.items():
+        ex = layer.experts[e] if s is None else layer.shared[s]
+        ng = ex.w2.K // ex.w2.group
+        assert np.array_equal(P2[rows, :, :ng], Pg), ("stage2", e, s)
+    o = oracle.oracle_layer(layer, act="a8", tile_m=16)
+    ok, rl2, mabs, rms = float_gate(g["out"], o["out"])
+    assert ok, (rl2, mabs, rms)
+
+
+def test_prefill_layer_sampled_tokens():
+    """The prefill layer at full size (4096 tokens, 256 experts, 192 int4 +
+    64 int2): integer stages in full, outputs on a token sample."""
+    cfg = CONFIGS[4]
+    layer = _layer(cfg)
+    dl = _dev(cfg)
+    tile_m = 64
+    g, B = run_layer_gpu(dl, "a16", tile_m)
+    ids, w = oracle.route_topk(layer.logits, cfg.k)
+    perm = oracle.permute(ids, cfg.E, tile_m)
+    assert np.array_equal(g["ids"], ids)
+    assert np.allclose(g["w"], w, rtol=2e-6, atol=1e-7)
+    for key in ("counts", "offsets", "sorted_pair", "pair_pos"):
+        assert np.array_equal(g[key], perm[key]), key
+    assert np.array_equal(g["tiles"][:, :3], perm["tiles"])
+    assert g["err"] == 0
+    toks = list(np.random.default_rng(4).choice(cfg.T, 24, replace=False)) + [0, cfg.T - 1]
+    s = oracle.oracle_token_outputs(layer, toks)
+    ok, rl2, mabs, rms = float_gate(g["out"][toks], s["out"])
+    print(f"[parity] prefill sample: rel-L2 {rl2:.2e} max-abs {mabs:.2e}", flush=True)
+    assert ok, (rl2, mabs, rms)
+    # h rows of the sampled tokens' pairs (bf16 on both sides)
+    for n, t in enumerate(toks[:6]):
+        for j in range(cfg.k):
+            r = perm["pair_pos"][t * cfg.k + j]
+            ok, rl2, mabs, rms = float_gate(g["h"][r, :cfg.I], s["h"][(t, j)])
+            assert ok, ("h", t, j, rl2, mabs)
+
+
+def test_repeat_bitwise_identical():
+    dl = _dev(CONFIGS[2])
+    g1, _ = run_layer_gpu(dl, "a16", 16)
+    g2, _ = run_layer_gpu(dl, "a16", 16)
+    assert np.array_equal(g1["out"], g2["out"])
+    assert np.array_equal(g1["h"], g2["h"])
+    g3, _ = run_layer_gpu(dl, "a8", 16)
+    g4, _ = run_layer_gpu(dl, "a8", 16)
+    assert np.array_equal(g3["out"], g4["out"])
+
+
+def test_side_stream_with_event_handoff():
+    """Inputs written on one stream, the layer run on another after an
+    event; the producer then overwrites its buffer only after the layer's
+    event has completed (buffers stay alive and unmodified until the stream
+    passes the call)."""
+    torch = torch_mod()
+    cfg = MINIS["mixed_shared"]
+    dl = _dev(cfg)
+    o = oracle.oracle_layer(_layer(cfg))
+    prod, cons = torch.cuda.Stream(), torch.cuda.Stream()
+    x_host = dl.x.clone()
+    with torch.cuda.stream(prod):
+        dl.x.zero_()
+        dl.x.copy_(x_host)
+        ev = torch.cuda.Event()
+        ev.record(prod)
+    B = dl.buffers()
+    cons.wait_event(ev)
+    dl.run(B, 0, cons)
+    done = torch.cuda.Event()
+    done.record(cons)
+    prod.wait_event(done)
+    with torch.cuda.stream(prod):
+        dl.x.zero_()
+    torch.cuda.synchronize()
+    g = collect(B)
+    ok, rl2, mabs, rms = float_gate(g["out"], o["out"])
+    assert ok
+
+
+def test_empty_batch_is_a_no_op():
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    from packed_bit_grouped_amd.layer import LayerBuffers
+    cfg = MINIS["c0"]
+    dl = _dev(cfg)
+    B = LayerBuffers(0, cfg.H, cfg.I, cfg.E, cfg.k, device="cuda")
+    B.out.fill_(123)
+    L.moe_route_topk(dl.logits, 0, cfg.E, cfg.k, 1, B.ids, B.w)
+    L.moe_w4_gateup_silu(0, dl.x, 0, cfg.H, cfg.I, cfg.E, cfg.k, dl.bank.w13, None, 0, 0,
+                         B.offsets, B.sorted_pair, B.tiles, B.n_tiles, 16, B.h, B.ws,
+                         B.ws_bytes)
+    torch.cuda.synchronize()
+    assert int(B.out[0, 0].item()) == 123
+
+
+def test_unusable_descriptor_sets_error_word():
+    """A descriptor with an unsupported bit width is skipped by the kernels
+    (its rows are not computed) and reported in the workspace error word."""
+    torch = torch_mod()
+    import ctypes
+    from packed_bit_grouped_amd import _lib as L
+    cfg = MINIS["c0"]
+    dl = _dev(cfg)
+    raw = to_np(dl.bank.w13).copy()
+    desc = L.QMatDesc.from_buffer(raw, 0)
+    desc.bits = 3
+    dl.bank.w13.copy_(torch.from_numpy(raw))
+    g, B = run_layer_gpu(dl, "a16", 16)
+    assert g["err"] & 1
