@@ -64,18 +64,24 @@ def _check_integer_stages(g, o, cfg):
     assert g["err"] == 0
 
 
+def _valid_h(h, cfg):
+    """The written part of h: routed rows hold I values, shared rows I_shared."""
+    P = cfg.T * cfg.k
+    parts = [np.asarray(h[:P, :cfg.I], np.float64).ravel()]
+    if cfg.n_shared:
+        parts.append(np.asarray(h[P:, :cfg.I_shared], np.float64).ravel())
+    return np.concatenate(parts)
+
+
 def _check_layer(cfg, act=None, tile_m=16, flags=0):
     act = act or cfg.act
     dl = _dev(cfg)
     g, B = run_layer_gpu(dl, act, tile_m, flags)
     o = oracle.oracle_layer(_layer(cfg), act=act, tile_m=tile_m)
     _check_integer_stages(g, o, cfg)
-    if act == "a16":
-        ok, rl2, mabs, rms = float_gate(g["h"], o["h"])
-        assert ok, ("h", rl2, mabs, rms)
-    else:
-        ok, rl2, mabs, rms = float_gate(g["h32"], o["h32"])
-        assert ok, ("h", rl2, mabs, rms)
+    gh, oh = (g["h"], o["h"]) if act == "a16" else (g["h32"], o["h32"])
+    ok, rl2, mabs, rms = float_gate(_valid_h(gh, cfg), _valid_h(oh, cfg))
+    assert ok, ("h", rl2, mabs, rms)
     ok, rl2, mabs, rms = float_gate(g["out"], o["out"])
     print(f"[parity] {cfg.name} {act}: out rel-L2 {rl2:.2e} max-abs {mabs:.2e} "
           f"(gate {2e-2 * rms:.2e})", flush=True)
