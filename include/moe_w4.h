@@ -142,6 +142,19 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E,
                        int32_t* sorted_pair, int32_t* pair_pos,
                        int32_t* tiles, int32_t* n_tiles, void* stream);
 
+/* ---------------------------------------------------------------------
+ * moe_route_permute -- moe_route_topk followed by moe_permute in one launch
+ * (one workgroup), for decode batches where the two steps are each a
+ * handful of microseconds of launch and latency (pages: fused operators
+ * where a decode step is many small launches).  Same outputs, bit for bit,
+ * as the two calls.  Limits: T <= 64, T*k <= 4096, 1 <= E <= 512.
+ * ------------------------------------------------------------------- */
+moe_status moe_route_permute(const float* logits, int T, int E, int k,
+                             int renormalize, int tile_m, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos,
+                             int32_t* tiles, int32_t* n_tiles, void* stream);
+
 /* Host-side upper bound of n_tiles: min(T*k, floor(T*k / tile_m) + min(E, T*k)). */
 int moe_permute_max_tiles(int T, int k, int E, int tile_m);
 
@@ -213,6 +226,10 @@ moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H,
  *   pair_pos   from moe_permute
  *   out        bf16 [T][H] (out): out[t] = sum_j topk_w[t][j] * y(pair
  *              t*k+j) + sum_s y(shared s, t), summed in fp32 in that order
+ * On the GEMV path the combine is fused: the last workgroup to finish a
+ * range of output columns (a counter in the workspace, which returns to
+ * zero after each call) does it, so the workspace must start zeroed once
+ * and calls sharing a workspace must be ordered on one stream.
  * ------------------------------------------------------------------- */
 moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
                                int E, int k, const moe_qmat* w2,

@@ -32,6 +32,10 @@ _SIGS = {
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p]),
     "moe_permute_max_tiles": (c_int, [c_int, c_int, c_int, c_int]),
+    "moe_route_permute": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                  c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p]),
     "moe_quant_a8_rows": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
                                   c_void_p, c_void_p, c_void_p]),
     "moe_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int,
@@ -164,6 +168,18 @@ def moe_permute(topk_ids, T, k, E, tile_m, counts, offsets, sorted_pair,
     return _call("moe_permute", _ptr(topk_ids), T, k, E, tile_m, _ptr(counts),
                  _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos), _ptr(tiles),
                  _ptr(n_tiles), _stream(stream), check=check)
+
+
+def moe_route_permute(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w,
+                      counts, offsets, sorted_pair, pair_pos, tiles, n_tiles,
+                      stream=None, check=True):
+    return _call("moe_route_permute", _ptr(logits), T, E, k, renormalize, tile_m,
+                 _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                 _ptr(sorted_pair), _ptr(pair_pos), _ptr(tiles), _ptr(n_tiles),
+                 _stream(stream), check=check)
+
+
+FUSED_ROUTE_MAX_T, FUSED_ROUTE_MAX_P, PERMUTE_MAX_E = 64, 4096, 512
 
 
 def moe_quant_a8_rows(src, src_is_f32, R, C, ld, q, s, stream=None, check=True):

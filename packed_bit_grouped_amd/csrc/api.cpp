@@ -32,6 +32,29 @@ moe_status check_device() {
   return ok ? MOE_OK : MOE_E_DEVICE;
 }
 
+int g_cu_count[kMaxDevices];
+
+// Compute units of the current device (queried once per device).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices && g_cu_count[dev] > 0) return g_cu_count[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < kMaxDevices) g_cu_count[dev] = n;
+  return n;
+}
+
+// GEMV grid: one workgroup per CU, fewer when there is little work.
+int gemv_grid(const ProjArgs& a) {
+  const long long units = (long long)a.n_sh_slots * a.U_sh + (long long)a.max_tiles * a.U;
+  long long g = (units + 15) / 16;
+  const long long cap = cu_count();   // one 8-wave workgroup per CU (about 230 VGPRs)
+  if (g > cap) g = cap;
+  return (int)(g < 1 ? 1 : g);
+}
+
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -59,16 +82,6 @@ int ld_h_of(int I, int n_shared, int I_shared) {
   return n_shared > 0 && I_shared > I ? I_shared : I;
 }
 
-// Work-item size: output units per workgroup such that one pass of the
-// four waves covers them (int4 codes, the common case).
-int gemv_rb(int mode, int K) {
-  const int C_r = K / 32;
-  int seg = C_r & (-C_r);
-  if (seg > 16) seg = 16;
-  const int rows = 4 * (64 / seg);
-  return mode == 0 ? rows / 2 : rows;
-}
-
 bool use_mfma(int act, int T, int E, int k, int flags) {
   const int path = flags & MOE_PATH_MASK;
   if (path == MOE_PATH_GEMV) return false;
@@ -92,6 +105,8 @@ WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
   if (act == MOE_A8) off += up256((size_t)T * 4);
   L.y = off;
   off += up256((size_t)T * (k + n_shared) * H * 4);
+  L.cnt = off;
+  off += up256((size_t)(H / 8 + 64) * 4);
   L.total = off;
   return L;
 }
@@ -159,6 +174,26 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E,
   return from_hip(launch_permute(topk_ids, T * k, E, tile_m, counts, offsets,
                                  sorted_pair, pair_pos, tiles, n_tiles,
                                  static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route_permute(const float* logits, int T, int E, int k,
+                             int renormalize, int tile_m, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos,
+                             int32_t* tiles, int32_t* n_tiles, void* stream) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E || tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
+  if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
+  if (E > kPermMaxE || T > kFusedRouteMaxT || T * k > kFusedRouteMaxP) return MOE_E_UNSUPPORTED;
+  if (!counts || !offsets || !n_tiles) return MOE_E_INVAL;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_pair || !pair_pos || !tiles))
+    return MOE_E_INVAL;
+  if (tiles && !aligned(tiles, 16)) return MOE_E_INVAL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(launch_route_permute(logits, T, E, k, renormalize, tile_m,
+                                       topk_ids, topk_w, counts, offsets,
+                                       sorted_pair, pair_pos, tiles, n_tiles,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_quant_a8_rows(const void* src, int src_is_f32, int R, int C,
@@ -239,10 +274,7 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   a.maxt = gemv_maxt(T, tile_m);
   a.sh_tile = a.maxt;
   a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
-  a.rb = gemv_rb(0, H);
-  const int Umax = a.U > a.U_sh ? a.U : a.U_sh;
-  a.n_rb = (Umax + a.rb - 1) / a.rb;
-  return from_hip(launch_proj_gemv(a, act, s));
+  return from_hip(launch_proj_gemv(a, act, gemv_grid(a), s));
 }
 
 static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
@@ -301,16 +333,16 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
   if (use_mfma(act, T, E, k, flags)) {
     a.in_bf16 = static_cast<const uint16_t*>(h);
     e = launch_proj_mfma(a, tile_m, s);
-  } else {
-    if (act == MOE_A8) a.in_f32 = static_cast<const float*>(h);
-    else a.in_bf16 = static_cast<const uint16_t*>(h);
-    a.maxt = gemv_maxt(T, tile_m);
-    a.sh_tile = a.maxt;
-    a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
-    a.rb = gemv_rb(1, a.K < a.K_sh ? a.K : a.K_sh);
-    a.n_rb = (H + a.rb - 1) / a.rb;
-    e = launch_proj_gemv(a, act, s);
+    if (e != hipSuccess) return MOE_E_DEVICE;
+    return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
+                                   n_shared, out, s));
   }
+  if (act == MOE_A8) a.in_f32 = static_cast<const float*>(h);
+  else a.in_bf16 = static_cast<const uint16_t*>(h);
+  a.maxt = gemv_maxt(T, tile_m);
+  a.sh_tile = a.maxt;
+  a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
+  e = launch_proj_gemv(a, act, gemv_grid(a), s);
   if (e != hipSuccess) return MOE_E_DEVICE;
   return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
                                  n_shared, out, s));

@@ -58,14 +58,67 @@ __device__ __forceinline__ int sdot4(int a, int b, int c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+// ---------------------------------------------------------------------
+// Cross-lane exchange with DPP (data-parallel primitives: the operand of a
+// VALU instruction is read from another lane of the same row of 16 lanes,
+// or broadcast between rows), a few cycles each instead of the LDS round
+// trip of ds_bpermute.
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;    // lane i <- 15 - i within a row
+constexpr int kDppRowHalfMirror = 0x141;// lane i <- 7 - i within 8 lanes
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of row r -> row r+1
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 -> rows 2 and 3
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over aligned groups of `width` lanes, width in {1, 2, 4, 8, 16}; every
+// lane of a group ends with the group's sum, formed in a fixed order.
+// width 16: mirror, half mirror, xor 2, xor 1; width 8: the last three.
 __device__ __forceinline__ float group_sum(float v, int width) {
-  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if (width >= 16) v += dpp_f<kDppRowMirror>(v, v);
+  if (width >= 8) v += dpp_f<kDppRowHalfMirror>(v, v);
+  if (width >= 4) v += dpp_f<kDppXor2>(v, v);
+  if (width >= 2) v += dpp_f<kDppXor1>(v, v);
   return v;
 }
 __device__ __forceinline__ int group_sum_i(int v, int width) {
-  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if (width >= 16) v += dpp_i<kDppRowMirror>(v, v);
+  if (width >= 8) v += dpp_i<kDppRowHalfMirror>(v, v);
+  if (width >= 4) v += dpp_i<kDppXor2>(v, v);
+  if (width >= 2) v += dpp_i<kDppXor1>(v, v);
   return v;
+}
+
+// (value, index) order of the router: larger value first, ties to the
+// lower index.
+__device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = dpp_f<CTRL, ROW_MASK>(v, v);
+  const int oi = dpp_i<CTRL, ROW_MASK>(i, i);
+  if (beats(ov, oi, v, i)) { v = ov; i = oi; }
+}
+// Wave-wide arg-max; the result is returned uniform (read from lane 63).
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<kDppXor1>(v, i);
+  argmax_step<kDppXor2>(v, i);
+  argmax_step<kDppRowHalfMirror>(v, i);
+  argmax_step<kDppRowMirror>(v, i);
+  argmax_step<kDppRowBcast15, 0xA>(v, i);
+  argmax_step<kDppRowBcast31, 0xC>(v, i);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));

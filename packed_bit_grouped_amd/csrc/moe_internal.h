@@ -8,6 +8,8 @@ namespace moe {
 constexpr int kPermMaxE = 512;      // permute: experts per launch
 constexpr int kPermIdBits = 9;      // bits of an expert id below kPermMaxE
 constexpr int kRouteMaxE = 1024;    // route: 16 logits per lane
+constexpr int kFusedRouteMaxT = 64; // fused route+permute: tokens per launch
+constexpr int kFusedRouteMaxP = 4096;  // fused route+permute: pairs per launch
 
 // Workspace layout (byte offsets from the workspace base).
 struct WsLayout {
@@ -15,6 +17,7 @@ struct WsLayout {
   size_t qx;         // A8: int8 [T][H]
   size_t sx;         // A8: fp32 [T]
   size_t y;          // fp32 [R][H]
+  size_t cnt;        // int32 completion counters of the fused combine
   size_t total;
 };
 WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
@@ -43,12 +46,19 @@ struct ProjArgs {
   int maxt;                    // activation rows staged per pass (1, 2, 4, 8)
   int sh_tile;                 // tokens per shared-expert tile
   int n_sh_slots;              // n_shared * ceil(T / sh_tile)
-  int rb;                      // units per work item
-  int n_rb;                    // work items per tile
+  int rb;                      // units per work item (MFMA path)
+  int n_rb;                    // work items per tile (MFMA path)
+  int res_rows;                // rows of one result buffer in LDS (GEMV path)
   // outputs
   void* out;                   // gate/up: h (bf16 or fp32); down: y fp32
   int ld_out;
   int32_t* err;
+  // fused combine (down only): the last block of each column range sums
+  // the weighted y rows of every token into out
+  const float* topk_w;
+  const int32_t* pair_pos;
+  uint16_t* comb_out;          // null: no fused combine
+  int32_t* cnt;
   int32_t* partials;           // A8 test hook (null otherwise)
   int ng_ld;
   int part_rows;               // row stride (in weight rows) of partials
@@ -60,9 +70,14 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int tile_m,
                           int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos,
                           int32_t* tiles, int32_t* n_tiles, hipStream_t st);
+hipError_t launch_route_permute(const float* logits, int T, int E, int k,
+                                int renorm, int tile_m, int32_t* ids, float* w,
+                                int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_pair, int32_t* pair_pos,
+                                int32_t* tiles, int32_t* n_tiles, hipStream_t st);
 hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
                            int8_t* q, float* s, hipStream_t st);
-hipError_t launch_proj_gemv(const ProjArgs& a, int act, hipStream_t st);
+hipError_t launch_proj_gemv(const ProjArgs& a, int act, int grid, hipStream_t st);
 int gemv_maxt(int T, int tile_m);
 hipError_t launch_proj_mfma(const ProjArgs& a, int tile_m, hipStream_t st);
 bool mfma_available();

@@ -9,15 +9,20 @@
 // expert this work is bound by HBM, not by the matrix cores, so it runs on
 // the vector ALUs:
 //
-//  * work item = (tile of up to tile_m sorted rows of one expert, block of
-//    output units); the tile's activations are staged once in LDS in the
-//    pair order of the code unpack, and every weight row of the block is
-//    read once from HBM and applied to all of the tile's tokens (tile
-//    reuse);
-//  * a weight row is split into 16-byte chunks; `seg` lanes share a row
-//    (split-K) and combine their partial sums with a butterfly over the
-//    segment (blocked reduction); a wave covers 64/seg rows at a time;
-//  * gate row i and up row I+i of W13 are in the same work item and meet
+//  * a fixed grid of about one workgroup per CU covers every tile (tile =
+//    up to tile_m sorted rows of one expert, or a shared-expert token
+//    block): the device-side tile count decides how many workgroups split
+//    a tile's output units (gate/up row pairs or down rows), so no
+//    workgroup waits on an empty tile and none straddles two tiles;
+//  * a workgroup stages a tile's activations once in LDS, in the pair
+//    order of the code unpack, and applies every weight row it reads to
+//    all of the tile's tokens (tile reuse); each weight byte is read once;
+//  * a weight row is cut into 16-byte chunks; `seg` lanes share a row
+//    (split-K) and add their partial sums with DPP exchanges inside the
+//    segment (blocked reduction); the rows of the next iteration are
+//    loaded into a second register set while the current ones are
+//    reduced (software pipelining), so HBM latency overlaps the VALU work;
+//  * gate row i and up row I+i of W13 are in the same iteration and meet
 //    in LDS for the fused SiLU(g) * u epilogue;
 //  * A16: codes expand to bf16 (exact, biased) and v_dot2_f32_bf16 forms
 //    the products; A8: codes expand to int8 and v_dot4_i32_i8 forms exact
@@ -26,450 +31,522 @@
 
 namespace moe {
 
-constexpr int kGemvThreads = 256;
+constexpr int kGemvWaves = 8;
+constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kCplMax = 4;   // 16-byte chunks per lane held per register set
 
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 
-// Input row pointers of pass row m.
-__device__ __forceinline__ int token_of(const ProjArgs& a, bool is_sh, int r) {
-  return is_sh ? r : a.sorted_pair[r] / a.k;
+// Geometry of the rows of one expert matrix.
+struct RowGeom {
+  int bits, group, CK, C_r, seg, lseg, cpl, segs_w, RPI, UPI, ng;
+  size_t row_bytes;
+};
+
+__device__ __forceinline__ RowGeom row_geom(const moe_qmat& q, int K, int mode) {
+  RowGeom g;
+  g.bits = q.bits;
+  g.group = q.group;
+  g.CK = 128 / g.bits;                 // K positions per 16-byte chunk
+  g.C_r = K / g.CK;                    // chunks per row
+  int seg = g.C_r & (-g.C_r);
+  g.seg = seg > 16 ? 16 : seg;
+  g.lseg = __builtin_ctz(g.seg);
+  g.cpl = g.C_r >> g.lseg;             // chunks per lane per row
+  g.segs_w = 64 >> g.lseg;             // rows per wave
+  g.RPI = kGemvWaves * g.segs_w;       // rows per iteration
+  g.UPI = mode == 0 ? g.RPI / 2 : g.RPI;
+  g.ng = K / g.group;
+  g.row_bytes = (size_t)K * g.bits / 8;
+  return g;
+}
+
+// LDS layout of a staged activation row.  The activations that meet one
+// 16-byte code chunk c (in unpack order) span NJ 16-byte words (A16: 4 for
+// int4, 8 for int2; A8: 2 for int4, 4 for int2).  Word j of chunk c is
+// stored at 16-byte index j * C_r + c (C_r = chunks per row), so the lanes
+// of a segment, which hold consecutive chunks, read consecutive 16-byte
+// words: no LDS bank conflicts on the ds_read_b128.
+//
+// A8: the 8 dwords of a 32-K staging block b go to words (int4: chunk b,
+// words 0-1; int2: chunk b/2, words 2*(b%2) + 0-1).
+__device__ __forceinline__ void store_a8_planes(uint32_t* row, const uint32_t (&pr)[8], int b,
+                                                int K, int bits) {
+  const int C_r = K * bits / 128;
+  const int c = bits == 4 ? b : b >> 1;
+  const int p0 = bits == 4 ? 0 : (b & 1) * 2;
+  uint4* dst = reinterpret_cast<uint4*>(row);
+  dst[p0 * C_r + c] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+  dst[(p0 + 1) * C_r + c] = make_uint4(pr[4], pr[5], pr[6], pr[7]);
+}
+
+// Stage the activation rows [pass, pass + nt) of a tile into LDS.
+template <int ACT>
+__device__ void stage_rows(const ProjArgs& a, bool is_sh, int e, int pass, int nt,
+                           int K, int bits, uint32_t* xs, int xs_row, float* xsum,
+                           float* xsc, int xsum_row) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb32 = K / 32;
+  if (ACT == MOE_A16) {
+    for (int u = tid; u < nt * nb32; u += kGemvThreads) {
+      const int m = u / nb32, b = u - m * nb32;
+      int row;
+      if (a.mode == 0) row = is_sh ? pass + m : a.sorted_pair[pass + m] / a.k;
+      else row = is_sh ? a.P + e * a.T + pass + m : pass + m;
+      const uint4* src =
+          reinterpret_cast<const uint4*>(a.in_bf16 + (size_t)row * a.ld_in + b * 32);
+      uint32_t v[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 t4 = src[i];
+        v[4 * i] = t4.x; v[4 * i + 1] = t4.y; v[4 * i + 2] = t4.z; v[4 * i + 3] = t4.w;
+      }
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sum += bf16_to_f32(v[i] & 0xFFFFu);
+        sum += bf16_to_f32(v[i] >> 16);
+      }
+      // 16 dwords of pairs -> planes (see the layout note above)
+      uint32_t pr[16];
+      auto xv = [&](int j) -> uint32_t { return (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
+      if (bits == 4) {       // four 8-blocks, pairs (i, i+4)
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pr[blk * 4 + i] = xv(8 * blk + i) | (xv(8 * blk + i + 4) << 16);
+      } else {               // two 16-blocks, pairs (i, i+8)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            pr[blk * 8 + i] = xv(16 * blk + i) | (xv(16 * blk + i + 8) << 16);
+      }
+      const int C_r = K * bits / 128;
+      const int c = bits == 4 ? b : b >> 1;
+      const int p0 = bits == 4 ? 0 : (b & 1) * 4;
+      uint4* dst = reinterpret_cast<uint4*>(xs + m * xs_row);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[(p0 + i) * C_r + c] = make_uint4(pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]);
+      xsum[m * xsum_row + b] = sum;
+    }
+  } else if (a.mode == 0) {  // A8 gate/up: pre-quantized x
+    for (int u = tid; u < nt * nb32; u += kGemvThreads) {
+      const int m = u / nb32, b = u - m * nb32;
+      const int t = is_sh ? pass + m : a.sorted_pair[pass + m] / a.k;
+      const uint4* src = reinterpret_cast<const uint4*>(a.in_q + (size_t)t * a.ld_in + b * 32);
+      const uint4 lo = src[0], hi = src[1];
+      const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      uint32_t pr[8];
+      auto xb = [&](int j) -> uint32_t { return (d[j >> 2] >> (8 * (j & 3))) & 0xFFu; };
+      if (bits == 4) {       // 8-blocks: even quad, odd quad
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          pr[2 * blk] = xb(8 * blk) | xb(8 * blk + 2) << 8 | xb(8 * blk + 4) << 16 | xb(8 * blk + 6) << 24;
+          pr[2 * blk + 1] = xb(8 * blk + 1) | xb(8 * blk + 3) << 8 | xb(8 * blk + 5) << 16 | xb(8 * blk + 7) << 24;
+        }
+      } else {               // 16-blocks: quads (i, i+4, i+8, i+12)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pr[4 * blk + i] = xb(16 * blk + i) | xb(16 * blk + i + 4) << 8 |
+                              xb(16 * blk + i + 8) << 16 | xb(16 * blk + i + 12) << 24;
+      }
+      store_a8_planes(xs + m * xs_row, pr, b, K, bits);
+      if (b == 0) xsc[m] = a.in_s[t];
+    }
+  } else {                   // A8 down: quantize fp32 h rows here
+    for (int m = wave; m < nt; m += kGemvWaves) {
+      const int row = is_sh ? a.P + e * a.T + pass + m : pass + m;
+      const float* src = a.in_f32 + (size_t)row * a.ld_in;
+      float amax = 0.0f;
+      for (int c = lane; c < K; c += 64) amax = fmaxf(amax, fabsf(src[c]));
+      amax = wave_max(amax);
+      const float sc = a8_scale(amax);
+      for (int b = lane; b < nb32; b += 64) {
+        int cq[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) cq[j] = a8_code(src[b * 32 + j], sc) & 0xFF;
+        uint32_t pr[8];
+        if (bits == 4) {
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) {
+            pr[2 * blk] = cq[8 * blk] | cq[8 * blk + 2] << 8 | cq[8 * blk + 4] << 16 | cq[8 * blk + 6] << 24;
+            pr[2 * blk + 1] = cq[8 * blk + 1] | cq[8 * blk + 3] << 8 | cq[8 * blk + 5] << 16 | cq[8 * blk + 7] << 24;
+          }
+        } else {
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              pr[4 * blk + i] = cq[16 * blk + i] | cq[16 * blk + i + 4] << 8 |
+                                cq[16 * blk + i + 8] << 16 | (uint32_t)cq[16 * blk + i + 12] << 24;
+        }
+        store_a8_planes(xs + m * xs_row, pr, b, K, bits);
+      }
+      if (lane == 0) xsc[m] = sc;
+    }
+  }
+}
+
+// One 16-byte chunk c of a weight row against every staged token.
+template <int ACT, int MAXT, bool DUMP>
+__device__ __forceinline__ void chunk_dot(const ProjArgs& a, const uint4 wv, const uint32_t sv,
+                                          int c, const RowGeom& G, int nt, const uint32_t* xs,
+                                          int xs_row, const float* xsum, int xsum_row,
+                                          float (&acc)[MAXT], int lis, bool vrow, int wr,
+                                          int orow_base) {
+  const uint32_t W[4] = {wv.x, wv.y, wv.z, wv.w};
+  if (ACT == MOE_A16) {
+    if (G.bits == 4) {
+      uint32_t wb[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = W[j] ^ 0x88888888u;
+        wb[4 * j + 0] = (w & 0x000F000Fu) | 0x43004300u;
+        wb[4 * j + 1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+        wb[4 * j + 2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+        wb[4 * j + 3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+      }
+      const float s = fp16_to_f32(sv & 0xFFFFu);
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        if (t >= nt) break;
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_row) + c;
+        float D = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 x4 = xp[i * G.C_r];
+          D = dot2_bf16(wb[4 * i + 0], x4.x, D);
+          D = dot2_bf16(wb[4 * i + 1], x4.y, D);
+          D = dot2_bf16(wb[4 * i + 2], x4.z, D);
+          D = dot2_bf16(wb[4 * i + 3], x4.w, D);
+        }
+        acc[t] = fmaf(s, D - 136.0f * xsum[t * xsum_row + c], acc[t]);
+      }
+    } else {  // int2: 4 words x 8 pairs
+      uint32_t wb[32];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = W[j] ^ 0xAAAAAAAAu;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wb[8 * j + i] = ((w >> (2 * i)) & 0x00030003u) | 0x43004300u;
+      }
+      const float s0 = fp16_to_f32(sv & 0xFFFFu);
+      const float s1 = G.group == 32 ? fp16_to_f32(sv >> 16) : s0;
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        if (t >= nt) break;
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_row) + c;
+        float D0 = 0.0f, D1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 x4 = xp[i * G.C_r];
+          D0 = dot2_bf16(wb[4 * i + 0], x4.x, D0);
+          D0 = dot2_bf16(wb[4 * i + 1], x4.y, D0);
+          D0 = dot2_bf16(wb[4 * i + 2], x4.z, D0);
+          D0 = dot2_bf16(wb[4 * i + 3], x4.w, D0);
+        }
+#pragma unroll
+        for (int i = 4; i < 8; ++i) {
+          const uint4 x4 = xp[i * G.C_r];
+          D1 = dot2_bf16(wb[4 * i + 0], x4.x, D1);
+          D1 = dot2_bf16(wb[4 * i + 1], x4.y, D1);
+          D1 = dot2_bf16(wb[4 * i + 2], x4.z, D1);
+          D1 = dot2_bf16(wb[4 * i + 3], x4.w, D1);
+        }
+        acc[t] = fmaf(s0, D0 - 130.0f * xsum[t * xsum_row + 2 * c], acc[t]);
+        acc[t] = fmaf(s1, D1 - 130.0f * xsum[t * xsum_row + 2 * c + 1], acc[t]);
+      }
+    }
+  } else {  // A8
+    if (G.bits == 4) {
+      uint32_t wq[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wq[2 * j] = (W[j] << 4) & 0xF0F0F0F0u;
+        wq[2 * j + 1] = W[j] & 0xF0F0F0F0u;
+      }
+      const float s = fp16_to_f32(sv & 0xFFFFu);
+      const int cpg = G.group / 32;   // chunks per group (<= seg)
+      const int g = (c * 32) / G.group;
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        if (t >= nt) break;
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_row) + c;
+        const uint4 x0 = xp[0], x1 = xp[G.C_r];
+        int d = 0;
+        d = sdot4((int)wq[0], (int)x0.x, d);
+        d = sdot4((int)wq[1], (int)x0.y, d);
+        d = sdot4((int)wq[2], (int)x0.z, d);
+        d = sdot4((int)wq[3], (int)x0.w, d);
+        d = sdot4((int)wq[4], (int)x1.x, d);
+        d = sdot4((int)wq[5], (int)x1.y, d);
+        d = sdot4((int)wq[6], (int)x1.z, d);
+        d = sdot4((int)wq[7], (int)x1.w, d);
+        const int P = group_sum_i(d >> 4, cpg);
+        if ((lis & (cpg - 1)) == 0) {
+          acc[t] = fmaf(s, (float)P, acc[t]);
+          if (DUMP && vrow)
+            a.partials[((size_t)(orow_base + t) * a.part_rows + wr) * a.ng_ld + g] = P;
+        }
+      }
+    } else {  // int2
+      uint32_t wq[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wq[4 * j + 0] = (W[j] << 6) & 0xC0C0C0C0u;
+        wq[4 * j + 1] = (W[j] << 4) & 0xC0C0C0C0u;
+        wq[4 * j + 2] = (W[j] << 2) & 0xC0C0C0C0u;
+        wq[4 * j + 3] = W[j] & 0xC0C0C0C0u;
+      }
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        if (t >= nt) break;
+        const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_row) + c;
+        int d0 = 0, d1 = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 x4 = xp[i * G.C_r];
+          d0 = sdot4((int)wq[4 * i + 0], (int)x4.x, d0);
+          d0 = sdot4((int)wq[4 * i + 1], (int)x4.y, d0);
+          d0 = sdot4((int)wq[4 * i + 2], (int)x4.z, d0);
+          d0 = sdot4((int)wq[4 * i + 3], (int)x4.w, d0);
+        }
+#pragma unroll
+        for (int i = 2; i < 4; ++i) {
+          const uint4 x4 = xp[i * G.C_r];
+          d1 = sdot4((int)wq[4 * i + 0], (int)x4.x, d1);
+          d1 = sdot4((int)wq[4 * i + 1], (int)x4.y, d1);
+          d1 = sdot4((int)wq[4 * i + 2], (int)x4.z, d1);
+          d1 = sdot4((int)wq[4 * i + 3], (int)x4.w, d1);
+        }
+        if (G.group == 32) {
+          const int P0 = d0 >> 6, P1 = d1 >> 6;
+          acc[t] = fmaf(fp16_to_f32(sv & 0xFFFFu), (float)P0, acc[t]);
+          acc[t] = fmaf(fp16_to_f32(sv >> 16), (float)P1, acc[t]);
+          if (DUMP && vrow) {
+            int32_t* pp = a.partials + ((size_t)(orow_base + t) * a.part_rows + wr) * a.ng_ld;
+            pp[2 * c] = P0;
+            pp[2 * c + 1] = P1;
+          }
+        } else {
+          const int cpg = G.group / 64;
+          const int P = group_sum_i((d0 + d1) >> 6, cpg);
+          if ((lis & (cpg - 1)) == 0) {
+            acc[t] = fmaf(fp16_to_f32(sv & 0xFFFFu), (float)P, acc[t]);
+            if (DUMP && vrow)
+              a.partials[((size_t)(orow_base + t) * a.part_rows + wr) * a.ng_ld +
+                         (c * 64) / G.group] = P;
+          }
+        }
+      }
+    }
+  }
 }
 
 template <int ACT, int MAXT, bool DUMP>
 __global__ __launch_bounds__(kGemvThreads) void proj_gemv_kernel(ProjArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slot = blockIdx.x / a.n_rb;
-  const int rbi = blockIdx.x - slot * a.n_rb;
-
-  // ---- which expert and which rows
-  bool is_sh;
-  int e, r_begin, r_end;  // routed: sorted rows; shared: token indices
-  if (slot < a.n_sh_slots) {
-    const int per = (a.T + a.sh_tile - 1) / a.sh_tile;
-    const int s = slot / per, ti = slot - s * per;
-    is_sh = true;
-    e = s;
-    r_begin = ti * a.sh_tile;
-    r_end = min(a.T, r_begin + a.sh_tile);
-  } else {
-    const int j = slot - a.n_sh_slots;
-    if (j >= *a.n_tiles) return;
-    const int4 tl = reinterpret_cast<const int4*>(a.tiles)[j];
-    if ((unsigned)tl.x >= (unsigned)a.E) {
-      if (tid == 0) atomicOr(a.err, 2);
-      return;
-    }
-    is_sh = false;
-    e = tl.x;
-    r_begin = tl.y;
-    r_end = tl.z;
-  }
-  const int K = is_sh ? a.K_sh : a.K;
-  const int U = is_sh ? a.U_sh : a.U;
-  const int unit0 = rbi * a.rb;
-  if (unit0 >= U || r_end <= r_begin) return;
-  const int nunits = min(a.rb, U - unit0);
-  const moe_qmat q = is_sh ? a.w_sh[e] : a.w[e];
-  if (!qmat_usable(q, a.mode == 0 ? 2 * U : U, K)) {
-    if (tid == 0) atomicOr(a.err, 1);
-    return;
-  }
-  const int bits = q.bits, group = q.group;
-  const int CK = 128 / bits;          // K positions per 16-byte chunk
-  const int C_r = K / CK;             // chunks per row
-  int seg = C_r & (-C_r);
-  if (seg > 16) seg = 16;
-  const int lseg = __builtin_ctz(seg);
-  const int cpl = C_r >> lseg;        // chunks per lane per row
-  const int segs_w = 64 >> lseg;
-  const int lis = lane & (seg - 1);
-  const int sid = lane >> lseg;
-  const int rows_item = a.mode == 0 ? 2 * nunits : nunits;
-  const int row_stride = 4 * segs_w;
-  const int iters = (rows_item + row_stride - 1) / row_stride;
-  const size_t row_bytes = (size_t)K * bits / 8;
-  const int ng = K / group;
   const int Kl = max(a.K, a.K_sh);
-  const int rows_max = a.mode == 0 ? 2 * a.rb : a.rb;
 
   // ---- LDS carve-up
   uint32_t* xs = reinterpret_cast<uint32_t*>(smem);
-  float* xsum = nullptr;     // A16: [MAXT][Kl/32]
-  float* xsc = nullptr;      // A8: [MAXT]
-  float* res;
-  if (ACT == MOE_A16) {
-    xsum = reinterpret_cast<float*>(xs + MAXT * (Kl / 2));
-    res = xsum + MAXT * (Kl / 32);
-  } else {
-    xsc = reinterpret_cast<float*>(xs + MAXT * (Kl / 4));
-    res = xsc + MAXT;
-  }
-  const int xs_row = ACT == MOE_A16 ? Kl / 2 : Kl / 4;  // dwords per staged row
-  const int nb32 = K / 32;
+  const int xs_row = ACT == MOE_A16 ? Kl / 2 : Kl / 4;   // dwords per staged row
+  const int xsum_row = Kl / 32;
+  float* xsum = reinterpret_cast<float*>(xs + MAXT * xs_row);  // A16: [MAXT][Kl/32]
+  float* xsc = xsum;                                           // A8: [MAXT]
+  float* res = ACT == MOE_A16 ? xsum + MAXT * xsum_row : xsc + MAXT;  // [2][res_rows][MAXT]
 
-  for (int pass = r_begin; pass < r_end; pass += MAXT) {
-    const int nt = min(MAXT, r_end - pass);
-    __syncthreads();
-    // ---- stage the pass's activation rows
-    if (ACT == MOE_A16) {
-      for (int u = tid; u < nt * nb32; u += kGemvThreads) {
-        const int m = u / nb32, b = u - m * nb32;
-        int row;
-        if (a.mode == 0) row = token_of(a, is_sh, pass + m);
-        else row = is_sh ? a.P + e * a.T + pass + m : pass + m;
-        const uint4* src =
-            reinterpret_cast<const uint4*>(a.in_bf16 + (size_t)row * a.ld_in + b * 32);
-        uint32_t v[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 t4 = src[i];
-          v[4 * i] = t4.x; v[4 * i + 1] = t4.y; v[4 * i + 2] = t4.z; v[4 * i + 3] = t4.w;
-        }
-        float sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sum += bf16_to_f32(v[i] & 0xFFFFu);
-          sum += bf16_to_f32(v[i] >> 16);
-        }
-        uint32_t* dst = xs + m * xs_row + b * 16;
-        auto xv = [&](int j) -> uint32_t {
-          return (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        };
-        if (bits == 4) {       // four 8-blocks, pairs (i, i+4)
-#pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              dst[blk * 4 + i] = xv(8 * blk + i) | (xv(8 * blk + i + 4) << 16);
-        } else {               // two 16-blocks, pairs (i, i+8)
-#pragma unroll
-          for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              dst[blk * 8 + i] = xv(16 * blk + i) | (xv(16 * blk + i + 8) << 16);
-        }
-        xsum[m * (Kl / 32) + b] = sum;
-      }
-    } else if (a.mode == 0) {  // A8 gate/up: pre-quantized x
-      for (int u = tid; u < nt * nb32; u += kGemvThreads) {
-        const int m = u / nb32, b = u - m * nb32;
-        const int t = token_of(a, is_sh, pass + m);
-        const uint4* src = reinterpret_cast<const uint4*>(a.in_q + (size_t)t * a.ld_in + b * 32);
-        const uint4 lo = src[0], hi = src[1];
-        const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        uint32_t* dst = xs + m * xs_row + b * 8;
-        auto xb = [&](int j) -> uint32_t { return (d[j >> 2] >> (8 * (j & 3))) & 0xFFu; };
-        if (bits == 4) {       // 8-blocks: even quad, odd quad
-#pragma unroll
-          for (int blk = 0; blk < 4; ++blk) {
-            dst[2 * blk] = xb(8 * blk) | xb(8 * blk + 2) << 8 | xb(8 * blk + 4) << 16 | xb(8 * blk + 6) << 24;
-            dst[2 * blk + 1] = xb(8 * blk + 1) | xb(8 * blk + 3) << 8 | xb(8 * blk + 5) << 16 | xb(8 * blk + 7) << 24;
-          }
-        } else {               // 16-blocks: quads (i, i+4, i+8, i+12)
-#pragma unroll
-          for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              dst[4 * blk + i] = xb(16 * blk + i) | xb(16 * blk + i + 4) << 8 |
-                                 xb(16 * blk + i + 8) << 16 | xb(16 * blk + i + 12) << 24;
-        }
-        if (b == 0) xsc[m] = a.in_s[t];
-      }
-    } else {                   // A8 down: quantize fp32 h rows here
-      for (int m = wave; m < nt; m += 4) {
-        const int row = is_sh ? a.P + e * a.T + pass + m : pass + m;
-        const float* src = a.in_f32 + (size_t)row * a.ld_in;
-        float amax = 0.0f;
-        for (int c = lane; c < K; c += 64) amax = fmaxf(amax, fabsf(src[c]));
-        amax = wave_max(amax);
-        const float sc = a8_scale(amax);
-        for (int b = lane; b < nb32; b += 64) {
-          int cq[32];
-#pragma unroll
-          for (int j = 0; j < 32; ++j) cq[j] = a8_code(src[b * 32 + j], sc) & 0xFF;
-          uint32_t* dst = xs + m * xs_row + b * 8;
-          if (bits == 4) {
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-              dst[2 * blk] = cq[8 * blk] | cq[8 * blk + 2] << 8 | cq[8 * blk + 4] << 16 | cq[8 * blk + 6] << 24;
-              dst[2 * blk + 1] = cq[8 * blk + 1] | cq[8 * blk + 3] << 8 | cq[8 * blk + 5] << 16 | cq[8 * blk + 7] << 24;
-            }
-          } else {
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                dst[4 * blk + i] = cq[16 * blk + i] | cq[16 * blk + i + 4] << 8 |
-                                   cq[16 * blk + i + 8] << 16 | (uint32_t)cq[16 * blk + i + 12] << 24;
-          }
-        }
-        if (lane == 0) xsc[m] = sc;
-      }
+  // ---- this workgroup's work: S = shared + routed tiles (device count).
+  // With S <= grid, each tile gets floor(grid / S) workgroups splitting its
+  // units evenly; otherwise workgroups take whole tiles in a strided loop.
+  // No workgroup straddles two tiles.
+  const int S = a.n_sh_slots + *a.n_tiles;
+  const int n_wg = gridDim.x;
+  const int bps = S > 0 && S <= n_wg ? n_wg / S : 1;
+  int slot = S <= n_wg ? blockIdx.x / bps : blockIdx.x;
+  const int part = S <= n_wg ? blockIdx.x - slot * bps : 0;
+  const int slot_step = S <= n_wg ? S : n_wg;
+
+  for (; slot < S; slot += slot_step) {
+    // ---- the tile and this workgroup's unit range inside it
+    bool is_sh;
+    int e, r_begin, r_end, U, K;
+    if (slot < a.n_sh_slots) {
+      const int per_sh = (a.T + a.sh_tile - 1) / a.sh_tile;
+      const int s = slot / per_sh, ti = slot - s * per_sh;
+      is_sh = true;
+      e = s;
+      r_begin = ti * a.sh_tile;
+      r_end = min(a.T, r_begin + a.sh_tile);
+      U = a.U_sh;
+      K = a.K_sh;
+    } else {
+      const int4 tl = reinterpret_cast<const int4*>(a.tiles)[slot - a.n_sh_slots];
+      is_sh = false;
+      e = tl.x;
+      r_begin = tl.y;
+      r_end = tl.z;
+      U = a.U;
+      K = a.K;
     }
-    __syncthreads();
+    const int unit0 = (int)((long long)U * part / bps);
+    const int unit1 = (int)((long long)U * (part + 1) / bps);
+    const int nunits = unit1 - unit0;
+    if (nunits <= 0) continue;
+    if (!is_sh && (unsigned)e >= (unsigned)a.E) {
+      if (tid == 0) atomicOr(a.err, 2);
+      continue;
+    }
+    const moe_qmat q = is_sh ? a.w_sh[e] : a.w[e];
+    if (!qmat_usable(q, a.mode == 0 ? 2 * U : U, K)) {
+      if (tid == 0) atomicOr(a.err, 1);
+      continue;
+    }
+    const RowGeom G = row_geom(q, K, a.mode);
+    const int lis = lane & (G.seg - 1);
+    const int sid = lane >> G.lseg;
+    const int qrow = wave * G.segs_w + sid;     // row slot inside an iteration
+    const int n_it = (nunits + G.UPI - 1) / G.UPI;
 
-    // ---- weight rows of the work item
-    for (int it = 0; it < iters; ++it) {
-      const int qrow = it * row_stride + wave * segs_w + sid;
-      const bool vrow = qrow < rows_item;
-      int wr;
-      if (a.mode == 0) wr = qrow < nunits ? unit0 + qrow : U + unit0 + (qrow - nunits);
-      else wr = unit0 + qrow;
-      if (!vrow) wr = 0;
-      const uint4* cp = reinterpret_cast<const uint4*>(q.codes + (size_t)wr * row_bytes);
-      const uint16_t* sp = q.scales + (size_t)wr * ng;
-      float acc[MAXT];
+    // weight row of iteration `it` for this lane's row slot
+    auto wrow = [&](int it, bool& vrow) -> int {
+      const int ub = it * G.UPI;
+      int unit, wr;
+      if (a.mode == 0) {
+        const bool up = qrow >= G.UPI;
+        unit = ub + (up ? qrow - G.UPI : qrow);
+        wr = unit0 + unit + (up ? U : 0);
+      } else {
+        unit = ub + qrow;
+        wr = unit0 + unit;
+      }
+      vrow = unit < nunits;
+      return vrow ? wr : 0;
+    };
+    auto load = [&](int it, int c0, uint4 (&wv)[kCplMax], uint32_t (&sv)[kCplMax]) {
+      bool vrow;
+      const int wr = wrow(it, vrow);
+      const uint4* cp = reinterpret_cast<const uint4*>(q.codes + (size_t)wr * G.row_bytes);
+      const uint16_t* sp = q.scales + (size_t)wr * G.ng;
 #pragma unroll
-      for (int t = 0; t < MAXT; ++t) acc[t] = 0.0f;
-
-      for (int c0 = 0; c0 < cpl; c0 += 8) {
-        uint4 wv[8];
-        uint32_t sv[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const int c = lis + seg * (c0 + b);
-          if (c0 + b < cpl && vrow) {
-            const u32x4_v t4 =
-                __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(cp + c));
-            wv[b] = make_uint4(t4.x, t4.y, t4.z, t4.w);
-            if (bits == 2 && group == 32)
-              sv[b] = *reinterpret_cast<const uint32_t*>(sp + 2 * c);
-            else
-              sv[b] = sp[(c * CK) / group];
-          } else {
-            wv[b] = make_uint4(0u, 0u, 0u, 0u);
-            sv[b] = 0u;
-          }
-        }
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          if (c0 + b >= cpl) break;
-          const int c = lis + seg * (c0 + b);
-          const uint32_t W[4] = {wv[b].x, wv[b].y, wv[b].z, wv[b].w};
-          if (ACT == MOE_A16) {
-            if (bits == 4) {
-              uint32_t wb[16];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const uint32_t w = W[j] ^ 0x88888888u;
-                wb[4 * j + 0] = (w & 0x000F000Fu) | 0x43004300u;
-                wb[4 * j + 1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-                wb[4 * j + 2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-                wb[4 * j + 3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
-              }
-              const float s = fp16_to_f32(sv[b] & 0xFFFFu);
-#pragma unroll
-              for (int t = 0; t < MAXT; ++t) {
-                if (t >= nt) break;
-                const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_row + c * 16);
-                float D = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const uint4 xv4 = xp[i];
-                  D = dot2_bf16(wb[4 * i + 0], xv4.x, D);
-                  D = dot2_bf16(wb[4 * i + 1], xv4.y, D);
-                  D = dot2_bf16(wb[4 * i + 2], xv4.z, D);
-                  D = dot2_bf16(wb[4 * i + 3], xv4.w, D);
-                }
-                acc[t] = fmaf(s, D - 136.0f * xsum[t * (Kl / 32) + c], acc[t]);
-              }
-            } else {  // int2: 4 words x 8 pairs
-              uint32_t wb[32];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const uint32_t w = W[j] ^ 0xAAAAAAAAu;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                  wb[8 * j + i] = ((w >> (2 * i)) & 0x00030003u) | 0x43004300u;
-              }
-              float s0, s1;
-              if (group == 32) {
-                s0 = fp16_to_f32(sv[b] & 0xFFFFu);
-                s1 = fp16_to_f32(sv[b] >> 16);
-              } else {
-                s0 = s1 = fp16_to_f32(sv[b] & 0xFFFFu);
-              }
-#pragma unroll
-              for (int t = 0; t < MAXT; ++t) {
-                if (t >= nt) break;
-                const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_row + c * 32);
-                float D0 = 0.0f, D1 = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const uint4 xv4 = xp[i];
-                  D0 = dot2_bf16(wb[4 * i + 0], xv4.x, D0);
-                  D0 = dot2_bf16(wb[4 * i + 1], xv4.y, D0);
-                  D0 = dot2_bf16(wb[4 * i + 2], xv4.z, D0);
-                  D0 = dot2_bf16(wb[4 * i + 3], xv4.w, D0);
-                }
-#pragma unroll
-                for (int i = 4; i < 8; ++i) {
-                  const uint4 xv4 = xp[i];
-                  D1 = dot2_bf16(wb[4 * i + 0], xv4.x, D1);
-                  D1 = dot2_bf16(wb[4 * i + 1], xv4.y, D1);
-                  D1 = dot2_bf16(wb[4 * i + 2], xv4.z, D1);
-                  D1 = dot2_bf16(wb[4 * i + 3], xv4.w, D1);
-                }
-                const float X0 = xsum[t * (Kl / 32) + 2 * c];
-                const float X1 = xsum[t * (Kl / 32) + 2 * c + 1];
-                acc[t] = fmaf(s0, D0 - 130.0f * X0, acc[t]);
-                acc[t] = fmaf(s1, D1 - 130.0f * X1, acc[t]);
-              }
-            }
-          } else {  // A8
-            const int orow_base = is_sh ? a.P + e * a.T + pass : pass;
-            if (bits == 4) {
-              uint32_t wq[8];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                wq[2 * j] = (W[j] << 4) & 0xF0F0F0F0u;
-                wq[2 * j + 1] = W[j] & 0xF0F0F0F0u;
-              }
-              const float s = fp16_to_f32(sv[b] & 0xFFFFu);
-              const int cpg = group / 32;     // chunks per group (<= seg)
-              const int g = (c * 32) / group;
-#pragma unroll
-              for (int t = 0; t < MAXT; ++t) {
-                if (t >= nt) break;
-                const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_row + c * 8);
-                const uint4 x0 = xp[0], x1 = xp[1];
-                int d = 0;
-                d = sdot4((int)wq[0], (int)x0.x, d);
-                d = sdot4((int)wq[1], (int)x0.y, d);
-                d = sdot4((int)wq[2], (int)x0.z, d);
-                d = sdot4((int)wq[3], (int)x0.w, d);
-                d = sdot4((int)wq[4], (int)x1.x, d);
-                d = sdot4((int)wq[5], (int)x1.y, d);
-                d = sdot4((int)wq[6], (int)x1.z, d);
-                d = sdot4((int)wq[7], (int)x1.w, d);
-                int P = group_sum_i(d >> 4, cpg);
-                if ((lis & (cpg - 1)) == 0) {
-                  acc[t] = fmaf(s, (float)P, acc[t]);
-                  if (DUMP && vrow)
-                    a.partials[((size_t)(orow_base + t) * a.part_rows + wr) * a.ng_ld + g] = P;
-                }
-              }
-            } else {  // int2
-              uint32_t wq[16];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                wq[4 * j + 0] = (W[j] << 6) & 0xC0C0C0C0u;
-                wq[4 * j + 1] = (W[j] << 4) & 0xC0C0C0C0u;
-                wq[4 * j + 2] = (W[j] << 2) & 0xC0C0C0C0u;
-                wq[4 * j + 3] = W[j] & 0xC0C0C0C0u;
-              }
-#pragma unroll
-              for (int t = 0; t < MAXT; ++t) {
-                if (t >= nt) break;
-                const uint4* xp = reinterpret_cast<const uint4*>(xs + t * xs_row + c * 16);
-                int d0 = 0, d1 = 0;
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                  const uint4 xv4 = xp[i];
-                  d0 = sdot4((int)wq[4 * i + 0], (int)xv4.x, d0);
-                  d0 = sdot4((int)wq[4 * i + 1], (int)xv4.y, d0);
-                  d0 = sdot4((int)wq[4 * i + 2], (int)xv4.z, d0);
-                  d0 = sdot4((int)wq[4 * i + 3], (int)xv4.w, d0);
-                }
-#pragma unroll
-                for (int i = 2; i < 4; ++i) {
-                  const uint4 xv4 = xp[i];
-                  d1 = sdot4((int)wq[4 * i + 0], (int)xv4.x, d1);
-                  d1 = sdot4((int)wq[4 * i + 1], (int)xv4.y, d1);
-                  d1 = sdot4((int)wq[4 * i + 2], (int)xv4.z, d1);
-                  d1 = sdot4((int)wq[4 * i + 3], (int)xv4.w, d1);
-                }
-                if (group == 32) {
-                  const int P0 = d0 >> 6, P1 = d1 >> 6;
-                  acc[t] = fmaf(fp16_to_f32(sv[b] & 0xFFFFu), (float)P0, acc[t]);
-                  acc[t] = fmaf(fp16_to_f32(sv[b] >> 16), (float)P1, acc[t]);
-                  if (DUMP && vrow) {
-                    int32_t* pp = a.partials + ((size_t)(orow_base + t) * a.part_rows + wr) * a.ng_ld;
-                    pp[2 * c] = P0;
-                    pp[2 * c + 1] = P1;
-                  }
-                } else {
-                  const int cpg = group / 64;
-                  const int P = group_sum_i((d0 + d1) >> 6, cpg);
-                  if ((lis & (cpg - 1)) == 0) {
-                    acc[t] = fmaf(fp16_to_f32(sv[b] & 0xFFFFu), (float)P, acc[t]);
-                    if (DUMP && vrow)
-                      a.partials[((size_t)(orow_base + t) * a.part_rows + wr) * a.ng_ld +
-                                 (c * 64) / group] = P;
-                  }
-                }
-              }
-            }
-          }
+      for (int b = 0; b < kCplMax; ++b) {
+        const int c = lis + G.seg * (c0 + b);
+        if (c0 + b < G.cpl && vrow) {
+          const u32x4_v t4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(cp + c));
+          wv[b] = make_uint4(t4.x, t4.y, t4.z, t4.w);
+          sv[b] = (G.bits == 2 && G.group == 32) ? *reinterpret_cast<const uint32_t*>(sp + 2 * c)
+                                                 : (uint32_t)sp[(c * G.CK) / G.group];
+        } else {
+          wv[b] = make_uint4(0u, 0u, 0u, 0u);
+          sv[b] = 0u;
         }
       }
+    };
+
+    for (int pass = r_begin; pass < r_end; pass += MAXT) {
+      const int nt = min(MAXT, r_end - pass);
+      const int orow_base = is_sh ? a.P + e * a.T + pass : pass;
+
+      // one iteration: dot products of the iteration's rows, reduction,
+      // then the epilogue of its units
+      auto iterate = [&](int it, uint4 (&wv)[kCplMax], uint32_t (&sv)[kCplMax], int rbuf) {
+        bool vrow;
+        const int wr = wrow(it, vrow);
+        float acc[MAXT];
 #pragma unroll
-      for (int t = 0; t < MAXT; ++t) {
-        if (t >= nt) break;
-        acc[t] = group_sum(acc[t], seg);
-      }
-      if (lis == 0 && vrow) {
+        for (int t = 0; t < MAXT; ++t) acc[t] = 0.0f;
+        for (int c0 = 0; c0 < G.cpl; c0 += kCplMax) {
+          if (c0 > 0) load(it, c0, wv, sv);
+#pragma unroll
+          for (int b = 0; b < kCplMax; ++b) {
+            if (c0 + b >= G.cpl) break;
+            chunk_dot<ACT, MAXT, DUMP>(a, wv[b], sv[b], lis + G.seg * (c0 + b), G, nt, xs,
+                                       xs_row, xsum, xsum_row, acc, lis, vrow, wr, orow_base);
+          }
+        }
 #pragma unroll
         for (int t = 0; t < MAXT; ++t) {
           if (t >= nt) break;
-          res[qrow * MAXT + t] = acc[t];
+          acc[t] = group_sum(acc[t], G.seg);
         }
-      }
-    }
-    __syncthreads();
+        float* rs = res + rbuf * a.res_rows * MAXT;
+        if (lis == 0 && vrow) {
+#pragma unroll
+          for (int t = 0; t < MAXT; ++t) {
+            if (t >= nt) break;
+            rs[qrow * MAXT + t] = acc[t];
+          }
+        }
+        __syncthreads();
+        const int ub = it * G.UPI;
+        const int nu = min(G.UPI, nunits - ub);
+        if (a.mode == 0) {
+          for (int idx = tid; idx < nu * nt; idx += kGemvThreads) {
+            const int m = idx / nu, i = idx - m * nu;
+            float gv = rs[i * MAXT + m], uv = rs[(G.UPI + i) * MAXT + m];
+            if (ACT == MOE_A8) {
+              gv *= xsc[m];
+              uv *= xsc[m];
+            }
+            const float hv = silu_mul(gv, uv);
+            const size_t o = (size_t)(orow_base + m) * a.ld_out + unit0 + ub + i;
+            if (ACT == MOE_A16) static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16(hv);
+            else static_cast<float*>(a.out)[o] = hv;
+          }
+        } else {
+          for (int idx = tid; idx < nu * nt; idx += kGemvThreads) {
+            const int m = idx / nu, i = idx - m * nu;
+            float y = rs[i * MAXT + m];
+            if (ACT == MOE_A8) y *= xsc[m];
+            static_cast<float*>(a.out)[(size_t)(orow_base + m) * a.ld_out + unit0 + ub + i] = y;
+          }
+        }
+      };
 
-    // ---- epilogue
-    const int orow0 = is_sh ? a.P + e * a.T + pass : pass;
-    if (a.mode == 0) {
-      for (int idx = tid; idx < nunits * nt; idx += kGemvThreads) {
-        const int m = idx / nunits, i = idx - m * nunits;
-        float g = res[i * MAXT + m], u = res[(nunits + i) * MAXT + m];
-        if (ACT == MOE_A8) {
-          g *= xsc[m];
-          u *= xsc[m];
-        }
-        const float hv = silu_mul(g, u);
-        const size_t o = (size_t)(orow0 + m) * a.ld_out + unit0 + i;
-        if (ACT == MOE_A16) static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16(hv);
-        else static_cast<float*>(a.out)[o] = hv;
-      }
-    } else {
-      for (int idx = tid; idx < nunits * nt; idx += kGemvThreads) {
-        const int m = idx / nunits, i = idx - m * nunits;
-        float y = res[i * MAXT + m];
-        if (ACT == MOE_A8) y *= xsc[m];
-        static_cast<float*>(a.out)[(size_t)(orow0 + m) * a.ld_out + unit0 + i] = y;
+      uint4 wvA[kCplMax], wvB[kCplMax];
+      uint32_t svA[kCplMax], svB[kCplMax];
+      load(0, 0, wvA, svA);              // in flight while the activations are staged
+      __syncthreads();                   // previous users of xs / res are done
+      stage_rows<ACT>(a, is_sh, e, pass, nt, K, G.bits, xs, xs_row, xsum, xsc, xsum_row);
+      __syncthreads();
+      for (int it = 0; it < n_it; it += 2) {
+        if (it + 1 < n_it) load(it + 1, 0, wvB, svB);
+        iterate(it, wvA, svA, 0);
+        if (it + 1 >= n_it) break;
+        if (it + 2 < n_it) load(it + 2, 0, wvA, svA);
+        iterate(it + 1, wvB, svB, 1);
       }
     }
   }
-  (void)rows_max;
 }
 
 template <int ACT, int MAXT, bool DUMP>
-static hipError_t launch_t(const ProjArgs& a, hipStream_t st) {
+static hipError_t launch_t(const ProjArgs& a, int grid, hipStream_t st) {
   const int Kl = max(a.K, a.K_sh);
-  const int rows_max = a.mode == 0 ? 2 * a.rb : a.rb;
   size_t lds;
   if (ACT == MOE_A16)
-    lds = (size_t)MAXT * Kl * 2 + (size_t)MAXT * (Kl / 32) * 4 + (size_t)rows_max * MAXT * 4;
+    lds = (size_t)MAXT * Kl * 2 + (size_t)MAXT * (Kl / 32) * 4;
   else
-    lds = (size_t)MAXT * Kl + (size_t)MAXT * 4 + (size_t)rows_max * MAXT * 4;
+    lds = (size_t)MAXT * Kl + (size_t)MAXT * 4;
+  lds += (size_t)2 * a.res_rows * MAXT * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const long long blocks = (long long)(a.n_sh_slots + a.max_tiles) * a.n_rb;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  proj_gemv_kernel<ACT, MAXT, DUMP><<<(unsigned)blocks, kGemvThreads, lds, st>>>(a);
+  proj_gemv_kernel<ACT, MAXT, DUMP><<<grid, kGemvThreads, lds, st>>>(a);
   return hipGetLastError();
 }
 
 template <int ACT, bool DUMP>
-static hipError_t launch_act(const ProjArgs& a, int maxt, hipStream_t st) {
-  switch (maxt) {
-    case 1: return launch_t<ACT, 1, DUMP>(a, st);
-    case 2: return launch_t<ACT, 2, DUMP>(a, st);
-    case 4: return launch_t<ACT, 4, DUMP>(a, st);
-    default: return launch_t<ACT, 8, DUMP>(a, st);
+static hipError_t launch_act(const ProjArgs& a, int grid, hipStream_t st) {
+  switch (a.maxt) {
+    case 1: return launch_t<ACT, 1, DUMP>(a, grid, st);
+    case 2: return launch_t<ACT, 2, DUMP>(a, grid, st);
+    case 4: return launch_t<ACT, 4, DUMP>(a, grid, st);
+    default: return launch_t<ACT, 8, DUMP>(a, grid, st);
   }
 }
 
@@ -480,12 +557,30 @@ int gemv_maxt(int T, int tile_m) {
   return b <= 1 ? 1 : b <= 2 ? 2 : b <= 4 ? 4 : 8;
 }
 
-hipError_t launch_proj_gemv(const ProjArgs& a, int act, hipStream_t st) {
-  const int maxt = a.maxt;
+// Rows per iteration of the widest geometry any expert of the call can
+// have (the fewest lanes per row: K and bits decide it).
+int gemv_res_rows(int K, int K_sh) {
+  int rows = 0;
+  for (int kk : {K, K_sh}) {
+    for (int bits : {4, 2}) {
+      const int C_r = kk * bits / 128;
+      if (C_r <= 0) continue;
+      int seg = C_r & (-C_r);
+      if (seg > 16) seg = 16;
+      rows = max(rows, kGemvWaves * (64 / seg));
+    }
+  }
+  return rows;
+}
+
+hipError_t launch_proj_gemv(const ProjArgs& a_in, int act, int grid, hipStream_t st) {
+  ProjArgs a = a_in;
+  a.res_rows = gemv_res_rows(a.K, a.K_sh);
+  if (grid <= 0) return hipSuccess;
   const bool dump = a.partials != nullptr;
-  if (act == MOE_A16) return launch_act<MOE_A16, false>(a, maxt, st);
-  if (dump) return launch_act<MOE_A8, true>(a, maxt, st);
-  return launch_act<MOE_A8, false>(a, maxt, st);
+  if (act == MOE_A16) return launch_act<MOE_A16, false>(a, grid, st);
+  if (dump) return launch_act<MOE_A8, true>(a, grid, st);
+  return launch_act<MOE_A8, false>(a, grid, st);
 }
 
 }  // namespace moe

@@ -5,24 +5,25 @@
 // "Keep low-bit weights packed, do the work on the NPU" (tokens are routed
 // to experts on the device, grouped projections with routing and tile
 // reuse) and "Remove sync and launch overhead from the token loop" (no
-// device-to-host scalar reads; routing moved off the host).
+// device-to-host scalar reads; routing moved off the host; fused operators
+// where a step is many small launches).
 #include "moe_internal.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------
-// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a
-// wave arg-max with the order (value descending, index ascending) pick the
-// experts; the gate weights are exp(l_j - l_max) over their sum (the
-// softmax over the chosen logits) or over all E logits (renormalize = 0).
+// Top-k of one token's logits by one wave.  Lane l holds logits l, l+64,
+// ...; each of k rounds takes the lane-local best not yet chosen and a
+// DPP wave arg-max with the order (value descending, index ascending).
+// Gate weights: exp(l_j - l_max) over their sum (softmax over the chosen
+// logits) or over all E logits (renormalize = 0).  Lane r < k returns the
+// r-th choice in (id, weight); other lanes return id -1.
 template <int NV>
-__global__ __launch_bounds__(256) void route_topk_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int renorm,
-    int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E,
+                                            int k, int renorm, int lane,
+                                            int32_t* __restrict__ ids_out,
+                                            float* __restrict__ w_out,
+                                            int32_t* lds_ids) {
   float v[NV];
   uint32_t taken = 0;
 #pragma unroll
@@ -42,20 +43,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int e = lane + 64 * j;
-      if (!((taken >> j) & 1u) && (v[j] > bv || (v[j] == bv && e < bi))) {
+      const bool free_j = !((taken >> j) & 1u);
+      if (free_j && beats(v[j], e, bv, bi)) {
         bv = v[j];
         bi = e;
       }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (r == 0) top = bv;
     const float ex = expf(bv - top);
@@ -75,29 +69,22 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   for (int j = 0; j < NV; ++j) {
     const int r = lane + 64 * j;
     if (r < k) {
-      ids[(size_t)t * k + r] = sel_id[j];
-      w[(size_t)t * k + r] = sel_ex[j] / denom;
+      ids_out[r] = sel_id[j];
+      w_out[r] = sel_ex[j] / denom;
+      if (lds_ids) lds_ids[r] = sel_id[j];
     }
   }
 }
 
-hipError_t launch_route_topk(const float* logits, int T, int E, int k,
-                             int renorm, int32_t* ids, float* w,
-                             hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  const dim3 grid((T + 3) / 4), block(256);
-  const int nv = (E + 63) / 64;
-  if (nv <= 1)
-    route_topk_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
-  else if (nv <= 2)
-    route_topk_kernel<2><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
-  else if (nv <= 4)
-    route_topk_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
-  else if (nv <= 8)
-    route_topk_kernel<8><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
-  else
-    route_topk_kernel<16><<<grid, block, 0, st>>>(logits, T, E, k, renorm, ids, w);
-  return hipGetLastError();
+template <int NV>
+__global__ __launch_bounds__(256) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm,
+    int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token<NV>(logits + (size_t)t * E, E, k, renorm, lane, ids + (size_t)t * k,
+                  w + (size_t)t * k, nullptr);
 }
 
 // ---------------------------------------------------------------------
@@ -114,6 +101,12 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k,
 //     order and bases are prefix sums over waves, so within an expert the
 //     pairs land in increasing p: the sort is stable.
 constexpr int kPermWaves = 16;
+
+struct PermSmem {
+  int hist[kPermWaves * kPermMaxE];
+  int tmp[kPermWaves + 1];
+  int total_valid;
+};
 
 __device__ int block_exclusive_scan(int v, int* tmp /* kPermWaves + 1 */) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -140,39 +133,39 @@ __device__ int block_exclusive_scan(int v, int* tmp /* kPermWaves + 1 */) {
   return r;
 }
 
-__global__ __launch_bounds__(1024) void permute_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int tile_m,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
-  __shared__ int hist[kPermWaves * kPermMaxE];
-  __shared__ int tmp[kPermWaves + 1];
-  __shared__ int total_valid;
+// ids: global or LDS pointer to the P expert ids.
+__device__ void permute_body(const int32_t* ids, int P, int E, int tile_m,
+                             int32_t* __restrict__ counts,
+                             int32_t* __restrict__ offsets,
+                             int32_t* __restrict__ sorted_pair,
+                             int32_t* __restrict__ pair_pos,
+                             int32_t* __restrict__ tiles,
+                             int32_t* __restrict__ n_tiles, PermSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kPermWaves * kPermMaxE; i += 1024) hist[i] = 0;
+  for (int i = tid; i < kPermWaves * kPermMaxE; i += 1024) sm.hist[i] = 0;
   __syncthreads();
   const int seg = (P + kPermWaves - 1) / kPermWaves;
   const int p0 = min(P, wave * seg), p1 = min(P, p0 + seg);
   for (int p = p0 + lane; p < p1; p += 64) {
     const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave * kPermMaxE + e], 1);
+    if ((unsigned)e < (unsigned)E) atomicAdd(&sm.hist[wave * kPermMaxE + e], 1);
   }
   __syncthreads();
   int cnt = 0;
   if (tid < E) {
     for (int w = 0; w < kPermWaves; ++w) {
-      const int c = hist[w * kPermMaxE + tid];
-      hist[w * kPermMaxE + tid] = cnt;
+      const int c = sm.hist[w * kPermMaxE + tid];
+      sm.hist[w * kPermMaxE + tid] = cnt;
       cnt += c;
     }
   }
-  const int excl = block_exclusive_scan(cnt, tmp);
+  const int excl = block_exclusive_scan(cnt, sm.tmp);
   const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
-  const int texcl = block_exclusive_scan(ntile, tmp);
+  const int texcl = block_exclusive_scan(ntile, sm.tmp);
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = excl;
-    for (int w = 0; w < kPermWaves; ++w) hist[w * kPermMaxE + tid] += excl;
+    for (int w = 0; w < kPermWaves; ++w) sm.hist[w * kPermMaxE + tid] += excl;
     for (int i = 0; i < ntile; ++i) {
       const int r0 = excl + i * tile_m;
       int4 tl;
@@ -185,7 +178,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     if (tid == E - 1) {
       offsets[E] = excl + cnt;
       *n_tiles = texcl + ntile;
-      total_valid = excl + cnt;
+      sm.total_valid = excl + cnt;
     }
   }
   __syncthreads();
@@ -203,16 +196,66 @@ __global__ __launch_bounds__(1024) void permute_kernel(
       m &= bit ? bb : ~bb;
     }
     if (valid) {
-      const int pos = hist[wave * kPermMaxE + e] + __popcll(m & below);
+      const int pos = sm.hist[wave * kPermMaxE + e] + __popcll(m & below);
       sorted_pair[pos] = p;
       pair_pos[p] = pos;
-      if ((m >> lane) == 1ull) hist[wave * kPermMaxE + e] = pos + 1;
+      if ((m >> lane) == 1ull) sm.hist[wave * kPermMaxE + e] = pos + 1;
     } else if (in) {
       pair_pos[p] = -1;
     }
   }
   __syncthreads();
-  for (int i = total_valid + tid; i < P; i += 1024) sorted_pair[i] = -1;
+  for (int i = sm.total_valid + tid; i < P; i += 1024) sorted_pair[i] = -1;
+}
+
+__global__ __launch_bounds__(1024) void permute_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int tile_m,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ PermSmem sm;
+  permute_body(ids, P, E, tile_m, counts, offsets, sorted_pair, pair_pos, tiles,
+               n_tiles, sm);
+}
+
+// Route and permute in one launch for small batches: the 16 waves route
+// the tokens (ids kept in LDS as well), then the same workgroup sorts.
+template <int NV>
+__global__ __launch_bounds__(1024) void route_permute_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm,
+    int tile_m, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ PermSmem sm;
+  __shared__ int32_t lds_ids[kFusedRouteMaxP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += kPermWaves)
+    route_token<NV>(logits + (size_t)t * E, E, k, renorm, lane, ids + (size_t)t * k,
+                    w + (size_t)t * k, lds_ids + t * k);
+  __syncthreads();
+  permute_body(lds_ids, T * k, E, tile_m, counts, offsets, sorted_pair, pair_pos,
+               tiles, n_tiles, sm);
+}
+
+#define MOE_NV_DISPATCH(NVV, ...)               \
+  do {                                          \
+    const int nv_ = (E + 63) / 64;              \
+    if (nv_ <= 1) { constexpr int NVV = 1; __VA_ARGS__; }       \
+    else if (nv_ <= 2) { constexpr int NVV = 2; __VA_ARGS__; }  \
+    else if (nv_ <= 4) { constexpr int NVV = 4; __VA_ARGS__; }  \
+    else if (nv_ <= 8) { constexpr int NVV = 8; __VA_ARGS__; }  \
+    else { constexpr int NVV = 16; __VA_ARGS__; }               \
+  } while (0)
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k,
+                             int renorm, int32_t* ids, float* w,
+                             hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((T + 3) / 4), block(256);
+  MOE_NV_DISPATCH(NV, route_topk_kernel<NV><<<grid, block, 0, st>>>(
+                          logits, T, E, k, renorm, ids, w));
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, int P, int E, int tile_m,
@@ -221,6 +264,18 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int tile_m,
                           int32_t* tiles, int32_t* n_tiles, hipStream_t st) {
   permute_kernel<<<1, 1024, 0, st>>>(ids, P, E, tile_m, counts, offsets,
                                      sorted_pair, pair_pos, tiles, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k,
+                                int renorm, int tile_m, int32_t* ids, float* w,
+                                int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_pair, int32_t* pair_pos,
+                                int32_t* tiles, int32_t* n_tiles,
+                                hipStream_t st) {
+  MOE_NV_DISPATCH(NV, route_permute_kernel<NV><<<1, 1024, 0, st>>>(
+                          logits, T, E, k, renorm, tile_m, ids, w, counts,
+                          offsets, sorted_pair, pair_pos, tiles, n_tiles));
   return hipGetLastError();
 }
 

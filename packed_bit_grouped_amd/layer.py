@@ -132,13 +132,24 @@ class LayerBuffers:
         return int(self.ws[:4].view(_torch().int32).item())
 
 
+def fused_routing_ok(T, E, k) -> bool:
+    """Route and permute in one launch when the batch is small."""
+    return (0 < T <= L.FUSED_ROUTE_MAX_T and T * k <= L.FUSED_ROUTE_MAX_P
+            and E <= L.PERMUTE_MAX_E)
+
+
 def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
               flags: int = 0, stream=None) -> None:
     """One layer step: route, permute, gate/up + SiLU*mul, down + combine."""
     T, H, I, E, k = B.T, B.H, B.I, B.E, B.k
-    L.moe_route_topk(logits, T, E, k, renormalize, B.ids, B.w, stream)
-    L.moe_permute(B.ids, T, k, E, B.tile_m, B.counts, B.offsets, B.sorted_pair,
-                  B.pair_pos, B.tiles, B.n_tiles, stream)
+    if fused_routing_ok(T, E, k):
+        L.moe_route_permute(logits, T, E, k, renormalize, B.tile_m, B.ids, B.w,
+                            B.counts, B.offsets, B.sorted_pair, B.pair_pos,
+                            B.tiles, B.n_tiles, stream)
+    else:
+        L.moe_route_topk(logits, T, E, k, renormalize, B.ids, B.w, stream)
+        L.moe_permute(B.ids, T, k, E, B.tile_m, B.counts, B.offsets,
+                      B.sorted_pair, B.pair_pos, B.tiles, B.n_tiles, stream)
     L.moe_w4_gateup_silu(B.act, x, T, H, I, E, k, bank.w13, bank.w13_sh,
                          B.n_shared, B.I_shared, B.offsets, B.sorted_pair,
                          B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes,

@@ -50,11 +50,13 @@ def test_max_tiles_bound():
 
 
 def test_workspace_sizes():
-    # error word + fp32 y rows (+ int8 x and fp32 scales for A8), 256-aligned
-    assert L.moe_workspace_bytes(0, 1, 2048, 768, 128, 8, 1, 768) == 256 + 9 * 2048 * 4
+    # error word + fp32 y rows (+ int8 x and fp32 scales for A8) + combine
+    # counters (H/8 + 64 ints), each region 256-byte aligned
+    cnt = ((2048 // 8 + 64) * 4 + 255) // 256 * 256
+    assert L.moe_workspace_bytes(0, 1, 2048, 768, 128, 8, 1, 768) == 256 + 9 * 2048 * 4 + cnt
     a8 = L.moe_workspace_bytes(1, 64, 2048, 768, 128, 8, 0, 0)
-    assert a8 == 256 + 64 * 2048 + 256 + 512 * 2048 * 4
-    assert L.moe_workspace_bytes(0, 0, 2048, 768, 128, 8, 0, 0) == 256
+    assert a8 == 256 + 64 * 2048 + 256 + 512 * 2048 * 4 + cnt
+    assert L.moe_workspace_bytes(0, 0, 2048, 768, 128, 8, 0, 0) == 256 + cnt
 
 
 FAKE = 1 << 20   # a non-null pointer value; never dereferenced on the host
@@ -143,3 +145,20 @@ def test_debug_hooks_need_partials():
     assert L.moe_dbg_w4a8_gateup_partials(
         FAKE, 4, 256, 128, 8, 2, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, 16,
         FAKE, FAKE, 1 << 30, None, 8, stream=0, check=False) == L.MOE_E_INVAL
+
+
+def test_route_permute_validation():
+    ok = dict(logits=FAKE, T=4, E=8, k=2, renormalize=1, tile_m=16, topk_ids=FAKE,
+              topk_w=FAKE, counts=FAKE, offsets=FAKE, sorted_pair=FAKE, pair_pos=FAKE,
+              tiles=FAKE, n_tiles=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_route_permute(*a.values(), stream=0, check=False)
+    assert call(T=65) == L.MOE_E_UNSUPPORTED             # fused only for small batches
+    assert call(T=64, k=65, E=512) == L.MOE_E_UNSUPPORTED   # T*k > 4096
+    assert call(E=513, k=2) == L.MOE_E_UNSUPPORTED
+    assert call(k=9) == L.MOE_E_INVAL
+    assert call(tile_m=0) == L.MOE_E_INVAL
+    assert call(topk_w=None) == L.MOE_E_INVAL
+    assert call() == L.MOE_E_DEVICE

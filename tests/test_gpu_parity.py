@@ -166,6 +166,44 @@ def _permute_check(torch, L, ids, E, tile_m):
     assert np.array_equal(to_np(tiles)[:n, :3], o["tiles"])
 
 
+def test_fused_route_permute_matches_separate_calls():
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    rng = np.random.default_rng(5)
+    for T, E, k, tile_m, renorm in [(1, 128, 8, 16, 1), (12, 128, 8, 16, 1),
+                                    (64, 128, 8, 16, 1), (64, 512, 64, 3, 1),
+                                    (7, 288, 8, 1, 0), (33, 8, 8, 4096, 1)]:
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        lg[:, 3::5] = lg[:, 1:2]
+        d = torch.from_numpy(lg).cuda()
+        outs = []
+        for fused in (True, False):
+            P = T * k
+            mt = L.moe_permute_max_tiles(T, k, E, tile_m)
+            b = [torch.full((T, k), -7, dtype=torch.int32, device="cuda"),
+                 torch.full((T, k), -7.0, dtype=torch.float32, device="cuda"),
+                 torch.full((E,), -7, dtype=torch.int32, device="cuda"),
+                 torch.full((E + 1,), -7, dtype=torch.int32, device="cuda"),
+                 torch.full((P,), -7, dtype=torch.int32, device="cuda"),
+                 torch.full((P,), -7, dtype=torch.int32, device="cuda"),
+                 torch.full((mt, 4), -7, dtype=torch.int32, device="cuda"),
+                 torch.zeros(1, dtype=torch.int32, device="cuda")]
+            if fused:
+                L.moe_route_permute(d, T, E, k, renorm, tile_m, *b)
+            else:
+                L.moe_route_topk(d, T, E, k, renorm, b[0], b[1])
+                L.moe_permute(b[0], T, k, E, tile_m, *b[2:])
+            torch.cuda.synchronize()
+            n = int(b[7].item())
+            outs.append([to_np(x) for x in b[:6]] + [to_np(b[6])[:n]])
+        for a_, b_ in zip(*outs):
+            assert np.array_equal(a_, b_), (T, E, k)
+        oi, ow = oracle.route_topk(lg, k, renorm)
+        assert np.array_equal(outs[0][0], oi)
+        o = oracle.permute(oi, E, tile_m)
+        assert np.array_equal(outs[0][6][:, :3], o["tiles"])
+
+
 def test_permute_skips_out_of_range_ids():
     torch = torch_mod()
     from packed_bit_grouped_amd import _lib as L
