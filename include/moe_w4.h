@@ -184,11 +184,16 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
 /* Flags of the projection calls. */
 #define MOE_PATH_AUTO 0       /* choose from the average pairs per expert   */
 #define MOE_PATH_GEMV 1       /* split-K wavefront GEMV (decode shapes)      */
-#define MOE_PATH_MFMA 2       /* MFMA grouped GEMM (prefill shapes)          */
+#define MOE_PATH_MFMA 2       /* MFMA grouped GEMM (prefill shapes); A16 only, */
+                              /* H, I, I_shared multiples of 128, and fp16    */
+                              /* copies of x (T*H) and h (T*(k+n_shared)      */
+                              /* rows of max(I, I_shared)) under 2 GiB, else  */
+                              /* MOE_E_UNSUPPORTED                            */
 #define MOE_PATH_MASK 3
 
-/* Tile height the MFMA path is written for; pass it as moe_permute's
- * tile_m when T*k / E is large (the GEMV path accepts any tile_m). */
+/* Tile height to pass as moe_permute's tile_m: 128 (the MFMA path's row
+ * block) when T*k >= 32*E with A16, else 16.  Both paths accept any
+ * tile_m; the MFMA path walks longer tiles in 128-row chunks. */
 int moe_preferred_tile_m(int act, int T, int E, int k);
 
 /* ---------------------------------------------------------------------

@@ -82,11 +82,25 @@ int ld_h_of(int I, int n_shared, int I_shared) {
   return n_shared > 0 && I_shared > I ? I_shared : I;
 }
 
-bool use_mfma(int act, int T, int E, int k, int flags) {
+// The MFMA path covers bf16 activations, K dimensions that are whole
+// pairs of 64-wide steps for int4 and int2 alike (H, I, I_shared % 128 ==
+// 0), and fp16 activation copies the kernel addresses with 32-bit byte
+// offsets (x: T*H, h: T*(k + n_shared) rows of max(I, I_shared)).
+bool mfma_shape_ok(int act, int T, int H, int I, int k, int n_shared, int I_shared) {
+  if (act != MOE_A16 || H % 128 != 0 || I % 128 != 0) return false;
+  if (n_shared > 0 && I_shared % 128 != 0) return false;
+  const long long ld_h = n_shared > 0 && I_shared > I ? I_shared : I;
+  const long long rows = (long long)T * (k + n_shared);
+  return (long long)T * H * 2 < (1LL << 31) && rows * ld_h * 2 < (1LL << 31);
+}
+
+bool use_mfma(int act, int T, int H, int I, int E, int k, int n_shared,
+              int I_shared, int flags) {
   const int path = flags & MOE_PATH_MASK;
   if (path == MOE_PATH_GEMV) return false;
   if (path == MOE_PATH_MFMA) return true;
-  return mfma_available() && act == MOE_A16 && (long long)T * k >= 32LL * E;
+  return mfma_available() && mfma_shape_ok(act, T, H, I, k, n_shared, I_shared) &&
+         (long long)T * k >= 32LL * E;
 }
 
 }  // namespace
@@ -107,6 +121,13 @@ WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
   off += up256((size_t)T * (k + n_shared) * H * 4);
   L.cnt = off;
   off += up256((size_t)(H / 8 + 64) * 4);
+  L.a16 = off;
+  if (act == MOE_A16 && mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) {
+    const size_t ld_h = (size_t)(n_shared > 0 && I_shared > I ? I_shared : I);
+    const size_t xs = (size_t)2 * T * H * 2;
+    const size_t hs = (size_t)T * (k + n_shared) * ld_h * 2;
+    off += up256(xs > hs ? xs : hs);
+  }
   L.total = off;
   return L;
 }
@@ -135,7 +156,7 @@ int moe_permute_max_tiles(int T, int k, int E, int tile_m) {
 }
 
 int moe_preferred_tile_m(int act, int T, int E, int k) {
-  if (use_mfma(act, T, E, k, MOE_PATH_AUTO)) return 64;
+  if (act == MOE_A16 && (long long)T * k >= 32LL * E) return 128;
   return 16;
 }
 
@@ -246,6 +267,7 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   a.P = T * k;
   a.E = E;
   a.n_shared = n_shared;
+  a.offsets = offsets;
   a.sorted_pair = sorted_pair;
   a.tiles = tiles;
   a.n_tiles = n_tiles;
@@ -257,9 +279,11 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   a.ng_ld = ng_ld;
   a.part_rows = 2 * ld_h;
 
-  if (use_mfma(act, T, E, k, flags)) {
+  if (use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags)) {
+    if (!mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) return MOE_E_UNSUPPORTED;
     a.in_bf16 = x;
-    return from_hip(launch_proj_mfma(a, tile_m, s));
+    uint16_t* x16 = reinterpret_cast<uint16_t*>(ws + L.a16);
+    return from_hip(launch_proj_mfma(a, x16, x16 + (size_t)T * H, s));
   }
   if (act == MOE_A8) {
     int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
@@ -318,6 +342,7 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
   a.P = T * k;
   a.E = E;
   a.n_shared = n_shared;
+  a.offsets = offsets;
   a.sorted_pair = sorted_pair;
   a.tiles = tiles;
   a.n_tiles = n_tiles;
@@ -330,9 +355,10 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
   a.part_rows = H;
 
   hipError_t e;
-  if (use_mfma(act, T, E, k, flags)) {
+  if (use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags)) {
+    if (!mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) return MOE_E_UNSUPPORTED;
     a.in_bf16 = static_cast<const uint16_t*>(h);
-    e = launch_proj_mfma(a, tile_m, s);
+    e = launch_proj_mfma(a, reinterpret_cast<uint16_t*>(ws + L.a16), nullptr, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
                                    n_shared, out, s));

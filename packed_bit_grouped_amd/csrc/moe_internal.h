@@ -18,6 +18,7 @@ struct WsLayout {
   size_t sx;         // A8: fp32 [T]
   size_t y;          // fp32 [R][H]
   size_t cnt;        // int32 completion counters of the fused combine
+  size_t a16;        // A16 MFMA path: fp16 activation copies (x twice, or h)
   size_t total;
 };
 WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
@@ -39,6 +40,7 @@ struct ProjArgs {
   int U, U_sh;                 // output units per expert: I pairs (gate/up), H rows (down)
   // routing
   int T, k, P, E, n_shared;
+  const int32_t* offsets;
   const int32_t* sorted_pair;
   const int32_t* tiles;
   const int32_t* n_tiles;
@@ -79,7 +81,8 @@ hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
                            int8_t* q, float* s, hipStream_t st);
 hipError_t launch_proj_gemv(const ProjArgs& a, int act, int grid, hipStream_t st);
 int gemv_maxt(int T, int tile_m);
-hipError_t launch_proj_mfma(const ProjArgs& a, int tile_m, hipStream_t st);
+hipError_t launch_proj_mfma(const ProjArgs& a, uint16_t* a16_4, uint16_t* a16_2,
+                            hipStream_t st);
 bool mfma_available();
 hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
                           const int32_t* pair_pos, int T, int k, int H, int P,

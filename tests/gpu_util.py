@@ -58,3 +58,22 @@ def float_gate(got, ref, rel_l2=5e-3, max_abs_frac=2e-2):
     mabs = np.abs(d).max() if d.size else 0.0
     ok = rl2 <= rel_l2 and mabs <= max_abs_frac * rms if rms > 0 else mabs == 0
     return ok, rl2, mabs, rms
+
+
+def h_gate(got, ref, act):
+    """Check of the intermediate h.  A16: both sides round h to bf16, so an
+    element may differ by one bf16 unit in the last place (2^-7 of its
+    magnitude at most) where the two unrounded values straddle a rounding
+    boundary; otherwise max-abs <= 2e-2 * rms.  rel-L2 <= 5e-3 always.
+    A8: fp32 h, the plain float gate.  Returns (ok, rel-L2, worst ratio)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    nref = np.linalg.norm(ref)
+    rl2 = np.linalg.norm(got - ref) / nref if nref > 0 else np.linalg.norm(got - ref)
+    rms = np.sqrt(np.mean(ref ** 2)) if ref.size else 0.0
+    bound = np.full(ref.shape, 2e-2 * rms)
+    if act == "a16":
+        bound = np.maximum(bound, 2.0 ** -7 * np.abs(ref))
+    worst = float((d / np.maximum(bound, 1e-300)).max()) if d.size else 0.0
+    return (rl2 <= 5e-3 and worst <= 1.0), rl2, worst

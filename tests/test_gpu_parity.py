@@ -15,8 +15,8 @@ import pytest
 
 import oracle
 from synth import CONFIGS, LayerConfig, make_layer
-from tests.gpu_util import (bf16_bits_to_f64, collect, float_gate, run_layer_gpu,
-                            to_np, torch_mod)
+from tests.gpu_util import (bf16_bits_to_f64, collect, float_gate, h_gate,
+                            run_layer_gpu, to_np, torch_mod)
 from tests.minis import MINIS
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +35,17 @@ MID = {
                                       act="a8"),
     "mid_g256": LayerConfig("mid_g256", 203, T=9, H=768, E=10, k=2, I=512,
                             group=256, n_int2=2, group_int2=256),
+}
+
+# MFMA-path layers: H, I multiple of 128; some experts over 128 rows
+MFMA = {
+    "mfma_mixed": LayerConfig("mfma_mixed", 210, T=600, H=512, E=16, k=4, I=256,
+                              group=128, n_int2=4, group_int2=64, n_shared=1,
+                              I_shared=384),
+    "mfma_g32_int2": LayerConfig("mfma_g32_int2", 211, T=257, H=384, E=6, k=2,
+                                 I=128, group=64, n_int2=3, group_int2=32),
+    "mfma_g256": LayerConfig("mfma_g256", 212, T=130, H=1024, E=8, k=3, I=512,
+                             group=256, n_int2=2, group_int2=128),
 }
 
 _cache = {}
@@ -80,8 +91,8 @@ def _check_layer(cfg, act=None, tile_m=16, flags=0):
     o = oracle.oracle_layer(_layer(cfg), act=act, tile_m=tile_m)
     _check_integer_stages(g, o, cfg)
     gh, oh = (g["h"], o["h"]) if act == "a16" else (g["h32"], o["h32"])
-    ok, rl2, mabs, rms = float_gate(_valid_h(gh, cfg), _valid_h(oh, cfg))
-    assert ok, ("h", rl2, mabs, rms)
+    ok, rl2, worst = h_gate(_valid_h(gh, cfg), _valid_h(oh, cfg), act)
+    assert ok, ("h", rl2, worst)
     ok, rl2, mabs, rms = float_gate(g["out"], o["out"])
     print(f"[parity] {cfg.name} {act}: out rel-L2 {rl2:.2e} max-abs {mabs:.2e} "
           f"(gate {2e-2 * rms:.2e})", flush=True)
@@ -92,7 +103,7 @@ def _check_layer(cfg, act=None, tile_m=16, flags=0):
 @pytest.mark.parametrize("name", list(MINIS) + list(MID))
 def test_small_layers(name):
     cfg = MINIS.get(name) or MID[name]
-    _check_layer(cfg)
+    _check_layer(cfg, flags=1)
 
 
 @pytest.mark.parametrize("name", ["c0", "mixed_shared", "mid_mixed"])
@@ -104,6 +115,26 @@ def test_small_layers_as_a8(name):
 @pytest.mark.parametrize("tile_m", [1, 3, 16, 64])
 def test_tile_sizes(tile_m):
     _check_layer(MID["mid_mixed"], tile_m=tile_m)
+
+
+@pytest.mark.parametrize("name", list(MFMA))
+def test_mfma_path_layers(name):
+    _check_layer(MFMA[name], tile_m=128, flags=2)
+
+
+@pytest.mark.parametrize("tile_m", [16, 64, 200])
+def test_mfma_path_tile_sizes(tile_m):
+    _check_layer(MFMA["mfma_mixed"], tile_m=tile_m, flags=2)
+
+
+def test_mfma_path_rejects_a8_and_odd_shapes():
+    from packed_bit_grouped_amd import _lib as L
+    dl = _dev(MID["mid_mixed"])       # I_shared = 192: not a multiple of 128
+    B = dl.buffers("a16", 16)
+    st = L.moe_w4_gateup_silu(0, dl.x, 100, 512, 256, 16, 4, dl.bank.w13, dl.bank.w13_sh, 1,
+                              192, B.offsets, B.sorted_pair, B.tiles, B.n_tiles, 16, B.h,
+                              B.ws, B.ws_bytes, 2, check=False)
+    assert st == L.MOE_E_UNSUPPORTED
 
 
 @pytest.mark.parametrize("cid", [0, 1, 2, 3])
@@ -348,8 +379,8 @@ def test_prefill_layer_sampled_tokens():
     for n, t in enumerate(toks[:6]):
         for j in range(cfg.k):
             r = perm["pair_pos"][t * cfg.k + j]
-            ok, rl2, mabs, rms = float_gate(g["h"][r, :cfg.I], s["h"][(t, j)])
-            assert ok, ("h", t, j, rl2, mabs)
+            ok, rl2, worst = h_gate(g["h"][r, :cfg.I], s["h"][(t, j)], "a16")
+            assert ok, ("h", t, j, rl2, worst)
 
 
 def test_repeat_bitwise_identical():
