@@ -17,15 +17,18 @@
 //  * the K loop walks 64 K per step.  A (activations) comes from an fp16
 //    copy made once per call in the K order of the weight unpack, so a
 //    step's A tile is a plain copy: each thread holds its share of the
-//    next steps in a four-slot register ring and writes one step into a
-//    double-buffered LDS tile laid out [16-byte K chunk][row] (the MFMA
-//    reads of 32 consecutive rows hit consecutive 16-byte words);
+//    next steps in a four-slot register ring (8 lanes fetch one whole
+//    128-byte row slice) and writes one step into a double-buffered LDS
+//    tile laid out [row][16-byte K chunk] with an XOR swizzle of the chunk
+//    slot by the row, so LDS writes and MFMA fragment reads are both free
+//    of bank conflicts;
 //  * packed weights go from HBM straight into registers (16 bytes (int4)
 //    or 8 bytes (int2) per lane, row and step, four steps ahead) and are
-//    dequantized there, never in LDS or HBM: a code OR-ed into fp16 1024
-//    gives 1024 + (code ^ 8), a packed fp16 subtract gives the exact code,
-//    a packed fp16 multiply applies the fp16 group scale (one rounding to
-//    fp16, relative error <= 2^-11);
+//    dequantized there, never in LDS or HBM: a code field OR-ed into the
+//    mantissa of a suitable fp16 power of two reads as that power plus
+//    the field, a packed fp16 subtract gives the exact code, a packed fp16
+//    multiply applies the fp16 group scale (one rounding to fp16, relative
+//    error <= 2^-11);
 //  * the K order inside each MFMA step is permuted the same way on both
 //    operands (a contraction does not depend on the order of K);
 //  * int4 and int2 experts mix freely: a tile takes its expert's format;
@@ -60,34 +63,53 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t lo_bf16, uint32_t h
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
-// One int4 code word (8 codes, K order k0..k7) -> MFMA fragment of 8 fp16
-// in the order k0,k4,k1,k5,k2,k6,k3,k7, each = code * scale.
+// Shift-free exact unpack of one pair of codes (one per 16-bit half of
+// w, BITS wide at bit offset OFS < 10).  OR-ed into the fp16 power of two
+// 2^(10 - OFS), the field lands in the mantissa where its unit is worth
+// exactly 1, so the half reads 2^(10 - OFS) + field.  With the field's top
+// bit flipped (offset binary: code + 8 for int4, + 2 for int2) a packed
+// fp16 subtract of 2^(10 - OFS) + 8 (or + 2) leaves the signed code
+// exactly, and a packed fp16 multiply applies the group scale with one
+// rounding.  Mask, flip and OR fold into one three-input bit operation.
+template <int OFS, int BITS>
+__device__ __forceinline__ f16x2_v unpack_pair(uint32_t w, f16x2_v s2) {
+  constexpr uint32_t field = (BITS == 4 ? 0xFu : 0x3u) << OFS;
+  constexpr uint32_t flip = (BITS == 4 ? 0x8u : 0x2u) << OFS;
+  constexpr uint32_t pow2 = (uint32_t)(25 - OFS) << 10;   // fp16 bits of 2^(10 - OFS)
+  constexpr uint32_t mask = field * 0x10001u;
+  constexpr uint32_t c = (flip | pow2) * 0x10001u;
+  constexpr float bias_f = (float)(1 << (10 - OFS)) + (BITS == 4 ? 8.0f : 2.0f);
+  const f16x2_v bias = {(_Float16)bias_f, (_Float16)bias_f};
+  return (as_h2((w & mask) ^ c) - bias) * s2;
+}
+
+__device__ __forceinline__ void put_pair(f16x8_v& r, int i, f16x2_v p) {
+  r[2 * i] = p.x;
+  r[2 * i + 1] = p.y;
+}
+
+// One int4 code word (8 codes, K order k0..k7 at bits 4k) -> MFMA
+// fragment of 8 fp16 in the order k0,k4,k1,k5,k2,k6,k3,k7, each = code *
+// scale.
 __device__ __forceinline__ f16x8_v deq_int4(uint32_t w, f16x2_v s2) {
-  const f16x2_v bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  w ^= 0x88888888u;
   f16x8_v r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2_v p = (as_h2(((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u) - bias) * s2;
-    r[2 * i] = p.x;
-    r[2 * i + 1] = p.y;
-  }
+  const uint32_t w8 = w >> 8;
+  put_pair(r, 0, unpack_pair<0, 4>(w, s2));
+  put_pair(r, 1, unpack_pair<4, 4>(w, s2));
+  put_pair(r, 2, unpack_pair<0, 4>(w8, s2));
+  put_pair(r, 3, unpack_pair<4, 4>(w8, s2));
   return r;
 }
-// One int2 code word (16 codes k0..k15) -> fragment HALF (0: pairs
-// (k0,k8)..(k3,k11); 1: pairs (k4,k12)..(k7,k15)).
+// One int2 code word (16 codes k0..k15 at bits 2k) -> fragment HALF (0:
+// pairs (k0,k8)..(k3,k11); 1: pairs (k4,k12)..(k7,k15)).
 template <int HALF>
 __device__ __forceinline__ f16x8_v deq_int2(uint32_t w, f16x2_v s2) {
-  const f16x2_v bias = {(_Float16)1026.0f, (_Float16)1026.0f};
-  w ^= 0xAAAAAAAAu;
   f16x8_v r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int sh = 2 * (4 * HALF + i);
-    const f16x2_v p = (as_h2(((w >> sh) & 0x00030003u) | 0x64006400u) - bias) * s2;
-    r[2 * i] = p.x;
-    r[2 * i + 1] = p.y;
-  }
+  const uint32_t v = HALF ? w >> 8 : w;
+  put_pair(r, 0, unpack_pair<0, 2>(v, s2));
+  put_pair(r, 1, unpack_pair<2, 2>(v, s2));
+  put_pair(r, 2, unpack_pair<4, 2>(v, s2));
+  put_pair(r, 3, unpack_pair<6, 2>(v, s2));
   return r;
 }
 
@@ -163,8 +185,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            0x00020000);
 }
 
+template <int MB>
 struct AStep {
-  u32x4_v a0, a1, a2, a3;   // this thread's four 16-byte A chunks of one step
+  u32x4_v a[MB];   // this thread's 16-byte A chunks of one step
 };
 
 template <int BITS>
@@ -183,66 +206,221 @@ struct TileCtx {
   bool is_sh;
 };
 
-// The K loop and epilogue of one tile chunk for one weight format.  The
-// loop body is straight-line code (format fixed, no data-dependent
-// branches, every load unconditional) so that the compiler's counters let
-// the loads of the next kRing steps stay in flight while the matrix cores
-// work on the current one.
+// This lane's weight rows and their buffer descriptors.
+struct WeightCtx {
+  __amdgpu_buffer_rsrc_t crs, srs;
+  int coff[2], soff[2];
+  int wrow[2];
+  bool wval[2];
+  int n_st, sshift;
+};
+
+// K loop and epilogue of one chunk of up to 32 * MB rows (tok[] holds
+// their activation rows).  The loop body is straight-line code (format
+// and row blocks fixed, no data-dependent branches, every load
+// unconditional) so that the compiler's counters let the loads of the
+// next kRing steps stay in flight while the matrix cores work on the
+// current one.
+template <int MODE, int BITS, int MB>
+__device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
+                                           const WeightCtx& w, u32x4_v* As, const int* tok,
+                                           int mc, int nrows) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ln = lane & 31, kh = lane >> 5;
+  const int n_st = w.n_st;
+  constexpr int kStepBytes = kKS * BITS / 8;   // 32 (int4) or 16 (int2)
+
+  auto load_b = [&](int st, BStep<BITS>& b) {
+    st = min(st, n_st - 1);
+    const int sst = (w.sshift >= 0 ? st << w.sshift : st >> -w.sshift) * 2;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if constexpr (BITS == 4) {
+        const u32x4_v t =
+            __builtin_amdgcn_raw_buffer_load_b128(w.crs, w.coff[s], st * kStepBytes, 0);
+        b.c[s][0] = t.x; b.c[s][1] = t.y; b.c[s][2] = t.z; b.c[s][3] = t.w;
+      } else {
+        const u32x2_v t =
+            __builtin_amdgcn_raw_buffer_load_b64(w.crs, w.coff[s], st * kStepBytes, 0);
+        b.c[s][0] = t.x; b.c[s][1] = t.y;
+      }
+      b.s[s] = __builtin_amdgcn_raw_buffer_load_b16(w.srs, w.soff[s], sst, 0);
+    }
+  };
+  // A staging: 32 * MB rows x 128 bytes per step, LDS laid out [row m][8
+  // 16-byte K chunks] with chunk ci of row m stored at slot ci ^ (m & 7),
+  // so the 8 lanes of an LDS pass hit distinct banks both when a row's
+  // 8 chunks are written and when 8 rows' chunk ci are read.  Thread tid
+  // moves chunk tid & 7 of rows (tid >> 3) + 32 i (i < MB): 8 lanes read
+  // one whole 128-byte line from memory.
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(c.asrc, c.a_bytes);
+  const int ci_own = tid & 7, m_own = tid >> 3;
+  int aoff[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) aoff[i] = tok[m_own + 32 * i] * a.ld_in * 2 + ci_own * 16;
+  auto load_a = [&](int st, AStep<MB>& ar) {
+    const int o = min(st, n_st - 1) * (kKS * 2);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) ar.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ars, aoff[i], o, 0);
+  };
+  auto store_a = [&](int buf, const AStep<MB>& ar) {
+    u32x4_v* d = As + buf * kChunks * kBM + m_own * kChunks + (ci_own ^ (m_own & 7));
+#pragma unroll
+    for (int i = 0; i < MB; ++i) d[32 * kChunks * i] = ar.a[i];
+  };
+
+  f32x16_v acc[2][MB];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[s][mb][j] = 0.0f;
+
+  // steps past the last one (the loop runs whole trips of kRing steps)
+  // re-read the last step with a zero scale: they add exact zeros
+  auto compute = [&](int buf, const BStep<BITS>& b, bool live) {
+    const u32x4_v* Ab = As + buf * kChunks * kBM + ln * kChunks;
+    // the whole step's A fragments first: one LDS round trip per step
+    u32x4_v af[4][MB];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        af[st][mb] = Ab[32 * kChunks * mb + ((kh * 4 + st) ^ (ln & 7))];
+    const uint32_t m16 = live ? 0x10001u : 0u;
+    const f16x2_v s0 = as_h2(b.s[0] * m16);
+    const f16x2_v s1 = as_h2(b.s[1] * m16);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      f16x8_v b0, b1;
+      if constexpr (BITS == 4) {
+        b0 = deq_int4(b.c[0][st], s0);
+        b1 = deq_int4(b.c[1][st], s1);
+      } else {
+        if ((st & 1) == 0) {
+          b0 = deq_int2<0>(b.c[0][st >> 1], s0);
+          b1 = deq_int2<0>(b.c[1][st >> 1], s1);
+        } else {
+          b0 = deq_int2<1>(b.c[0][st >> 1], s0);
+          b1 = deq_int2<1>(b.c[1][st >> 1], s1);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const f16x8_v av = __builtin_bit_cast(f16x8_v, af[st][mb]);
+        acc[0][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b0, acc[0][mb], 0, 0, 0);
+        acc[1][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b1, acc[1][mb], 0, 0, 0);
+      }
+    }
+    // Issue order for the step: the A fragments of the first two
+    // sub-steps, the unpack of sub-step 0, then each MFMA followed by a
+    // share of the next sub-step's unpack (one wave per SIMD, so the
+    // VALU work has to run in the shadow of its own MFMAs) and the LDS
+    // reads of the sub-step after next.
+    constexpr int kMfmaPerSub = 2 * MB;
+    constexpr int kValuPerSub = 26;
+    constexpr int kValuPerMfma = (kValuPerSub + kMfmaPerSub - 1) / kMfmaPerSub;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValuPerSub, 0);
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+#pragma unroll
+      for (int i = 0; i < kMfmaPerSub; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+        if (sub < 2 && i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+
+  // ---- K loop over a ring of kRing register slots: step s computes
+  // from LDS buffer s & 1 and weight slot s % kRing, writes the
+  // activations of step s + 1 (loaded three steps earlier) into the
+  // other LDS buffer, then refills slot s % kRing with step s + kRing.
+  AStep<MB> ar0, ar1, ar2, ar3;
+  BStep<BITS> b0, b1, b2, b3;
+  load_a(0, ar0); load_b(0, b0);
+  load_a(1, ar1); load_b(1, b1);
+  load_a(2, ar2); load_b(2, b2);
+  load_a(3, ar3); load_b(3, b3);
+  store_a(0, ar0);
+  __syncthreads();
+#define MOE_STEP(J, AC, BC, AN)                     \
+  compute(J & 1, BC, base + J < n_st);              \
+  store_a((J + 1) & 1, AN);                         \
+  load_a(base + J + kRing, AC);                     \
+  load_b(base + J + kRing, BC);                     \
+  __syncthreads();
+  for (int base = 0; base < n_st; base += kRing) {
+    MOE_STEP(0, ar0, b0, ar1)
+    MOE_STEP(1, ar1, b1, ar2)
+    MOE_STEP(2, ar2, b2, ar3)
+    MOE_STEP(3, ar3, b3, ar0)
+  }
+#undef MOE_STEP
+
+  // ---- epilogue
+  const int orow0 = c.is_sh ? a.P + c.e * a.T + mc : mc;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int m = 32 * mb + (j >> 2) * 8 + kh * 4 + (j & 3);
+      if (m >= nrows) continue;
+      if (MODE == 0) {
+        if (!w.wval[0]) continue;
+        const float hv = silu_mul(acc[0][mb][j], acc[1][mb][j]);
+        static_cast<uint16_t*>(a.out)[(size_t)(orow0 + m) * a.ld_out + w.wrow[0]] =
+            (uint16_t)f32_to_bf16(hv);
+      } else {
+        float* y = static_cast<float*>(a.out) + (size_t)(orow0 + m) * a.ld_out;
+        if (w.wval[0]) y[w.wrow[0]] = acc[0][mb][j];
+        if (w.wval[1]) y[w.wrow[1]] = acc[1][mb][j];
+      }
+    }
+  }
+}
+
+// Every chunk of one tile for one weight format: chunks of up to 32, 64
+// or 128 rows take matching row-block counts, so a tile's ragged tail
+// costs what its rows need.
 template <int MODE, int BITS>
 __device__ __forceinline__ void mfma_tile(const ProjArgs& a, const TileCtx& c, u32x4_v* As,
                                           int* tok) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, kh = lane >> 5;
   const int K = c.K, U = c.U;
-  const int n_st = K / kKS;
   const int ng = K / c.group;
-  constexpr int kStepBytes = kKS * BITS / 8; // 32 (int4) or 16 (int2)
-  constexpr int kLaneBytes = kStepBytes / 2; // per lane half
+  constexpr int kLaneBytes = kKS * BITS / 16;   // per lane half and step
   const int row_bytes = K * BITS / 8;
 
+  WeightCtx w;
+  w.n_st = K / kKS;
   // this lane's two weight rows: gate/up of one unit, or two down rows
-  int wrow[2];
-  bool wval[2];
   if (MODE == 0) {
     const int unit = c.u0 + 32 * wave + ln;
-    wval[0] = wval[1] = unit < U;
-    wrow[0] = unit;
-    wrow[1] = U + unit;
+    w.wval[0] = w.wval[1] = unit < U;
+    w.wrow[0] = unit;
+    w.wrow[1] = U + unit;
   } else {
     const int r0 = c.u0 + 64 * wave + ln;
-    wval[0] = r0 < U;
-    wval[1] = r0 + 32 < U;
-    wrow[0] = r0;
-    wrow[1] = r0 + 32;
+    w.wval[0] = r0 < U;
+    w.wval[1] = r0 + 32 < U;
+    w.wrow[0] = r0;
+    w.wrow[1] = r0 + 32;
   }
   const int n_wrows = MODE == 0 ? 2 * U : U;
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(c.codes, (uint32_t)(n_wrows * row_bytes));
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(c.scales, (uint32_t)(n_wrows * ng * 2));
-  int coff[2], soff[2];
+  w.crs = make_rsrc(c.codes, (uint32_t)(n_wrows * row_bytes));
+  w.srs = make_rsrc(c.scales, (uint32_t)(n_wrows * ng * 2));
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int r = wval[s] ? wrow[s] : 0;
-    coff[s] = r * row_bytes + kh * kLaneBytes;
-    soff[s] = (r * ng + (c.group == 32 ? kh : 0)) * 2;
+    const int r = w.wval[s] ? w.wrow[s] : 0;
+    w.coff[s] = r * row_bytes + kh * kLaneBytes;
+    w.soff[s] = (r * ng + (c.group == 32 ? kh : 0)) * 2;
   }
   // scale index of step st: (64 st + 32 kh) / group
-  const int sshift = c.group == 32 ? 1 : (c.group == 64 ? 0 : (c.group == 128 ? -1 : -2));
-  auto load_b = [&](int st, BStep<BITS>& b) {
-    st = min(st, n_st - 1);
-    const int sst = (sshift >= 0 ? st << sshift : st >> -sshift) * 2;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if constexpr (BITS == 4) {
-        const u32x4_v t = __builtin_amdgcn_raw_buffer_load_b128(crs, coff[s], st * kStepBytes, 0);
-        b.c[s][0] = t.x; b.c[s][1] = t.y; b.c[s][2] = t.z; b.c[s][3] = t.w;
-      } else {
-        const u32x2_v t = __builtin_amdgcn_raw_buffer_load_b64(crs, coff[s], st * kStepBytes, 0);
-        b.c[s][0] = t.x; b.c[s][1] = t.y;
-      }
-      b.s[s] = __builtin_amdgcn_raw_buffer_load_b16(srs, soff[s], sst, 0);
-    }
-  };
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(c.asrc, c.a_bytes);
+  w.sshift = c.group == 32 ? 1 : (c.group == 64 ? 0 : (c.group == 128 ? -1 : -2));
 
   for (int mc = c.r_begin; mc < c.r_end; mc += kBM) {
     const int nrows = min(kBM, c.r_end - mc);
@@ -255,116 +433,9 @@ __device__ __forceinline__ void mfma_tile(const ProjArgs& a, const TileCtx& c, u
       tok[tid] = r;
     }
     __syncthreads();
-    // A staging: 16 KB per step = 1024 16-byte chunks [K chunk ci][row m];
-    // thread tid moves chunks q = tid + 256 i (i < 4): row tid % 128,
-    // K chunks 2 i + tid / 128
-    const int aoff = tok[tid % kBM] * a.ld_in * 2 + (tid / kBM) * 16;
-    auto load_a = [&](int st, AStep& ar) {
-      const int o = min(st, n_st - 1) * (kKS * 2);
-      ar.a0 = __builtin_amdgcn_raw_buffer_load_b128(ars, aoff, o, 0);
-      ar.a1 = __builtin_amdgcn_raw_buffer_load_b128(ars, aoff + 32, o, 0);
-      ar.a2 = __builtin_amdgcn_raw_buffer_load_b128(ars, aoff + 64, o, 0);
-      ar.a3 = __builtin_amdgcn_raw_buffer_load_b128(ars, aoff + 96, o, 0);
-    };
-    auto store_a = [&](int buf, const AStep& ar) {
-      u32x4_v* d = As + buf * kChunks * kBM + tid;
-      d[0] = ar.a0;
-      d[kMThreads] = ar.a1;
-      d[2 * kMThreads] = ar.a2;
-      d[3 * kMThreads] = ar.a3;
-    };
-
-    f32x16_v acc[2][kMB];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[s][mb][j] = 0.0f;
-
-    // steps past the last one (the loop runs whole trips of kRing steps)
-    // re-read the last step with a zero scale: they add exact zeros
-    auto compute = [&](int buf, const BStep<BITS>& b, bool live) {
-      const u32x4_v* Ab = As + buf * kChunks * kBM + ln;
-      // the whole step's A fragments first: one LDS round trip per step
-      u32x4_v af[4][kMB];
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) af[st][mb] = Ab[(kh * 4 + st) * kBM + 32 * mb];
-      const uint32_t m16 = live ? 0x10001u : 0u;
-      const f16x2_v s0 = as_h2(b.s[0] * m16);
-      const f16x2_v s1 = as_h2(b.s[1] * m16);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        f16x8_v b0, b1;
-        if constexpr (BITS == 4) {
-          b0 = deq_int4(b.c[0][st], s0);
-          b1 = deq_int4(b.c[1][st], s1);
-        } else {
-          if ((st & 1) == 0) {
-            b0 = deq_int2<0>(b.c[0][st >> 1], s0);
-            b1 = deq_int2<0>(b.c[1][st >> 1], s1);
-          } else {
-            b0 = deq_int2<1>(b.c[0][st >> 1], s0);
-            b1 = deq_int2<1>(b.c[1][st >> 1], s1);
-          }
-        }
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-          const f16x8_v av = __builtin_bit_cast(f16x8_v, af[st][mb]);
-          acc[0][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b0, acc[0][mb], 0, 0, 0);
-          acc[1][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b1, acc[1][mb], 0, 0, 0);
-        }
-      }
-    };
-
-    // ---- K loop over a ring of kRing register slots: step s computes
-    // from LDS buffer s & 1 and weight slot s % kRing, writes the
-    // activations of step s + 1 (loaded three steps earlier) into the
-    // other LDS buffer, then refills slot s % kRing with step s + kRing.
-    AStep ar0, ar1, ar2, ar3;
-    BStep<BITS> b0, b1, b2, b3;
-    load_a(0, ar0); load_b(0, b0);
-    load_a(1, ar1); load_b(1, b1);
-    load_a(2, ar2); load_b(2, b2);
-    load_a(3, ar3); load_b(3, b3);
-    store_a(0, ar0);
-    __syncthreads();
-#define MOE_STEP(J, AC, BC, AN)                     \
-    compute(J & 1, BC, base + J < n_st);            \
-    store_a((J + 1) & 1, AN);                       \
-    load_a(base + J + kRing, AC);                   \
-    load_b(base + J + kRing, BC);                   \
-    __syncthreads();
-    for (int base = 0; base < n_st; base += kRing) {
-      MOE_STEP(0, ar0, b0, ar1)
-      MOE_STEP(1, ar1, b1, ar2)
-      MOE_STEP(2, ar2, b2, ar3)
-      MOE_STEP(3, ar3, b3, ar0)
-    }
-#undef MOE_STEP
-
-    // ---- epilogue
-    const int orow0 = c.is_sh ? a.P + c.e * a.T + mc : mc;
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = 32 * mb + (j >> 2) * 8 + kh * 4 + (j & 3);
-        if (m >= nrows) continue;
-        if (MODE == 0) {
-          if (!wval[0]) continue;
-          const float hv = silu_mul(acc[0][mb][j], acc[1][mb][j]);
-          static_cast<uint16_t*>(a.out)[(size_t)(orow0 + m) * a.ld_out + wrow[0]] =
-              (uint16_t)f32_to_bf16(hv);
-        } else {
-          float* y = static_cast<float*>(a.out) + (size_t)(orow0 + m) * a.ld_out;
-          if (wval[0]) y[wrow[0]] = acc[0][mb][j];
-          if (wval[1]) y[wrow[1]] = acc[1][mb][j];
-        }
-      }
-    }
+    if (nrows > 64) mfma_chunk<MODE, BITS, 4>(a, c, w, As, tok, mc, nrows);
+    else if (nrows > 32) mfma_chunk<MODE, BITS, 2>(a, c, w, As, tok, mc, nrows);
+    else mfma_chunk<MODE, BITS, 1>(a, c, w, As, tok, mc, nrows);
   }
 }
 
@@ -373,7 +444,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 void proj_mfma_kernel(ProjArgs a, const uint16_t* x16_4,
                                                               const uint16_t* x16_2) {
   extern __shared__ __align__(16) unsigned char smem[];
-  u32x4_v* As = reinterpret_cast<u32x4_v*>(smem);                  // [2][kChunks][kBM]
+  u32x4_v* As = reinterpret_cast<u32x4_v*>(smem);                  // [2][kBM][kChunks]
   int* tok = reinterpret_cast<int*>(smem + 2 * kChunks * kBM * 16);  // [kBM]
   const int tid = threadIdx.x;
 
