@@ -109,7 +109,6 @@ def main():
     dl = DeviceLayer.from_synth(layer, "cuda:0")
     act = cfg.act
     B = dl.buffers(act)
-    st = torch.cuda.current_stream()
 
     # routing is identical on every step: learn the touched experts once
     dl.run(B, flags)
@@ -137,38 +136,60 @@ def main():
     def step(i):
         run_layer(banks[i % len(banks)], dl.x, dl.logits, B, cfg.renormalize, flags)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for i in range(args.steps):
-        step(i)
-    e1.record(st)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms * 1e3:.2f} us/step")
-
-    # the dominant kernel (gate/up + SiLU*mul), timed with events on the
-    # stream it is launched on, within a second timed region
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
-    for i in range(args.steps):
-        bk = banks[i % len(banks)]
-        L.moe_route_topk(dl.logits, T, E, k, cfg.renormalize, B.ids, B.w)
-        L.moe_permute(B.ids, T, k, E, B.tile_m, B.counts, B.offsets, B.sorted_pair,
-                      B.pair_pos, B.tiles, B.n_tiles)
-        ev[i][0].record(st)
+
+    def gateup(bk):
         L.moe_w4_gateup_silu(B.act, dl.x, T, H, I, E, k, bk.w13, bk.w13_sh,
                              cfg.n_shared, cfg.I_shared, B.offsets, B.sorted_pair,
                              B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes, flags)
-        ev[i][1].record(st)
-        L.moe_w4_down_combine(B.act, B.h, T, H, I, E, k, bk.w2, bk.w2_sh, cfg.n_shared,
-                              cfg.I_shared, B.w, B.offsets, B.sorted_pair, B.pair_pos,
-                              B.tiles, B.n_tiles, B.tile_m, B.out, B.ws, B.ws_bytes, flags)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        for i in range(n):
+            fn(i)
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for i in range(args.warmup):
+        step(i)
+    # eager issue from Python (secondary number: includes host launch cost)
+    ms_eager = timed(step, args.steps)
+    log(f"[bench] eager: {ms_eager * 1e3:.2f} us/step")
+
+    # the served form: one HIP graph per weight-bank copy holding the whole
+    # step (route+permute, gate/up, down+combine), replayed back to back
+    graphs = []
+    for bi in range(len(banks)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_layer(banks[bi], dl.x, dl.logits, B, cfg.renormalize, flags)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    ms = timed(lambda i: graphs[i % len(graphs)].replay(), args.steps)
+    log(f"[bench] graph replay: {args.steps} steps: {ms * 1e3:.2f} us/step")
+    # check the replayed step against an eager one (same inputs, same bank)
+    out_g = B.out.clone()
+    step(args.steps - 1)
     torch.cuda.synchronize()
-    gu_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    if not torch.equal(out_g, B.out):
+        log("[bench] graph replay output differs from the eager step")
+        sys.exit(3)
+
+    # the dominant kernel (gate/up + SiLU*mul) alone: a graph of back-to-back
+    # launches over distinct bank copies, timed with events on the stream
+    # the graph runs on
+    n_k = min(len(banks), 32) if decode else 4
+    gk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gk):
+        for i in range(n_k):
+            gateup(banks[i % len(banks)])
+    gk.replay()
+    reps = max(1, args.steps // n_k)
+    gu_ms = timed(lambda i: gk.replay(), reps) / n_k
     log(f"[bench] gate/up kernel: {gu_ms * 1e3:.2f} us/launch")
 
     if decode:
@@ -207,7 +228,9 @@ def main():
                    "I": cfg.I, "n_shared": cfg.n_shared, "act": act,
                    "experts_touched": n_touched,
                    "bytes_per_step": bytes_all, "flops_per_step": flops,
-                   "bank_copies_rotated": len(banks), "path": args.path},
+                   "bank_copies_rotated": len(banks), "path": args.path,
+                   "timing": "HIP graph replay of the whole step, back to back",
+                   "ms_per_step_eager": ms_eager},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -221,6 +221,30 @@ moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H,
                               size_t ws_bytes, int flags, void* stream);
 
 /* ---------------------------------------------------------------------
+ * moe_w4_route_gateup_silu -- moe_route_permute followed by
+ * moe_w4_gateup_silu, with the outputs of both (same argument meanings).
+ * Build log "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", section
+ * "Remove sync and launch overhead from the token loop": a decode step is
+ * dominated by launches and round trips, so for bf16 activations with
+ * T*k <= 64, E <= 512, H <= 2048 and tiles of at most 16 rows (the split-K
+ * path) this is ONE launch in which every workgroup routes and sorts the
+ * batch itself before its share of the gate/up work; other shapes issue
+ * the routing call and the gate/up call.  Errors: those of the two calls.
+ * ------------------------------------------------------------------- */
+moe_status moe_w4_route_gateup_silu(int act, const float* logits,
+                                    const uint16_t* x, int T, int H, int I,
+                                    int E, int k, int renormalize,
+                                    const moe_qmat* w13,
+                                    const moe_qmat* w13_shared, int n_shared,
+                                    int I_shared, int tile_m,
+                                    int32_t* topk_ids, float* topk_w,
+                                    int32_t* counts, int32_t* offsets,
+                                    int32_t* sorted_pair, int32_t* pair_pos,
+                                    int32_t* tiles, int32_t* n_tiles, void* h,
+                                    void* workspace, size_t ws_bytes,
+                                    int flags, void* stream);
+
+/* ---------------------------------------------------------------------
  * moe_w4_down_combine -- grouped down projection of every h row and the
  * weighted combine into the token outputs.
  *   h          as written by moe_w4_gateup_silu (same act); A8 rows are
@@ -231,10 +255,11 @@ moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H,
  *   pair_pos   from moe_permute
  *   out        bf16 [T][H] (out): out[t] = sum_j topk_w[t][j] * y(pair
  *              t*k+j) + sum_s y(shared s, t), summed in fp32 in that order
- * On the GEMV path the combine is fused: the last workgroup to finish a
- * range of output columns (a counter in the workspace, which returns to
- * zero after each call) does it, so the workspace must start zeroed once
- * and calls sharing a workspace must be ordered on one stream.
+ * Decode batches with bf16 activations (tiles of at most 16 rows, I <= 1024,
+ * every h row of the layer fitting in 64 KB of LDS) combine inside the
+ * down kernel: a workgroup owns a range of output columns of every token.
+ * Otherwise y goes through the workspace (fp32 [R][H]) to a combine kernel.
+ * Calls sharing a workspace must be ordered on one stream.
  * ------------------------------------------------------------------- */
 moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
                                int E, int k, const moe_qmat* w2,

@@ -46,6 +46,12 @@ _SIGS = {
                                    c_int, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_int, c_void_p, c_void_p,
                                    c_size_t, c_int, c_void_p]),
+    "moe_w4_route_gateup_silu": (c_int, [c_int, c_void_p, c_void_p, c_int, c_int,
+                                         c_int, c_int, c_int, c_int, c_void_p,
+                                         c_void_p, c_int, c_int, c_int, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_size_t, c_int, c_void_p]),
     "moe_w4_down_combine": (c_int, [c_int, c_void_p, c_int, c_int, c_int,
                                     c_int, c_int, c_void_p, c_void_p, c_int,
                                     c_int, c_void_p, c_void_p, c_void_p,
@@ -194,6 +200,19 @@ def moe_w4_gateup_silu(act, x, T, H, I, E, k, w13, w13_shared, n_shared,
                  _ptr(w13_shared), n_shared, I_shared, _ptr(offsets),
                  _ptr(sorted_pair), _ptr(tiles), _ptr(n_tiles), tile_m, _ptr(h),
                  _ptr(workspace), ws_bytes, flags, _stream(stream), check=check)
+
+
+def moe_w4_route_gateup_silu(act, logits, x, T, H, I, E, k, renormalize, w13,
+                             w13_shared, n_shared, I_shared, tile_m, topk_ids,
+                             topk_w, counts, offsets, sorted_pair, pair_pos, tiles,
+                             n_tiles, h, workspace, ws_bytes, flags=0, stream=None,
+                             check=True):
+    return _call("moe_w4_route_gateup_silu", act, _ptr(logits), _ptr(x), T, H, I, E,
+                 k, renormalize, _ptr(w13), _ptr(w13_shared), n_shared, I_shared,
+                 tile_m, _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                 _ptr(sorted_pair), _ptr(pair_pos), _ptr(tiles), _ptr(n_tiles),
+                 _ptr(h), _ptr(workspace), ws_bytes, flags, _stream(stream),
+                 check=check)
 
 
 def moe_w4_down_combine(act, h, T, H, I, E, k, w2, w2_shared, n_shared,

@@ -119,8 +119,6 @@ WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
   if (act == MOE_A8) off += up256((size_t)T * 4);
   L.y = off;
   off += up256((size_t)T * (k + n_shared) * H * 4);
-  L.cnt = off;
-  off += up256((size_t)(H / 8 + 64) * 4);
   L.a16 = off;
   if (act == MOE_A16 && mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) {
     const size_t ld_h = (size_t)(n_shared > 0 && I_shared > I ? I_shared : I);
@@ -298,6 +296,10 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   a.maxt = gemv_maxt(T, tile_m);
   a.sh_tile = a.maxt;
   a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
+  if (act == MOE_A16 && !partials && dec_gateup_ok(T, H, tile_m)) {
+    a.maxt = dec_maxt(T, tile_m);
+    return from_hip(launch_dec_gateup(a, s));
+  }
   return from_hip(launch_proj_gemv(a, act, gemv_grid(a), s));
 }
 
@@ -368,6 +370,13 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
   a.maxt = gemv_maxt(T, tile_m);
   a.sh_tile = a.maxt;
   a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
+  if (act == MOE_A16 && !partials &&
+      dec_down_ok(T, k, E, n_shared, H, I, I_shared, ld_h, tile_m, a.max_tiles)) {
+    a.maxt = dec_maxt(T, tile_m);
+    a.topk_w = topk_w;
+    a.pair_pos = pair_pos;
+    return from_hip(launch_dec_down_combine(a, out, s));
+  }
   e = launch_proj_gemv(a, act, gemv_grid(a), s);
   if (e != hipSuccess) return MOE_E_DEVICE;
   return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
@@ -385,6 +394,76 @@ moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H, int I,
   return gateup_impl(act, x, T, H, I, E, k, w13, w13_shared, n_shared, I_shared,
                      offsets, sorted_pair, tiles, n_tiles, tile_m, h, workspace,
                      ws_bytes, flags, nullptr, 0, stream);
+}
+
+moe_status moe_w4_route_gateup_silu(int act, const float* logits, const uint16_t* x, int T,
+                                    int H, int I, int E, int k, int renormalize,
+                                    const moe_qmat* w13, const moe_qmat* w13_shared,
+                                    int n_shared, int I_shared, int tile_m, int32_t* topk_ids,
+                                    float* topk_w, int32_t* counts, int32_t* offsets,
+                                    int32_t* sorted_pair, int32_t* pair_pos, int32_t* tiles,
+                                    int32_t* n_tiles, void* h, void* workspace,
+                                    size_t ws_bytes, int flags, void* stream) {
+  moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
+  if (st != MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
+  const bool fused = act == MOE_A16 && T > 0 &&
+                     !use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
+                     dec_route_gateup_ok(T, H, E, k, tile_m);
+  if (!fused) {
+    // the two calls, each with its own checks
+    if (T <= kFusedRouteMaxT && (long long)T * k <= kFusedRouteMaxP && E <= kPermMaxE) {
+      st = moe_route_permute(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w, counts,
+                             offsets, sorted_pair, pair_pos, tiles, n_tiles, stream);
+    } else {
+      st = moe_route_topk(logits, T, E, k, renormalize, topk_ids, topk_w, stream);
+      if (st == MOE_OK)
+        st = moe_permute(topk_ids, T, k, E, tile_m, counts, offsets, sorted_pair, pair_pos,
+                         tiles, n_tiles, stream);
+    }
+    if (st != MOE_OK) return st;
+    return moe_w4_gateup_silu(act, x, T, H, I, E, k, w13, w13_shared, n_shared, I_shared,
+                              offsets, sorted_pair, tiles, n_tiles, tile_m, h, workspace,
+                              ws_bytes, flags, stream);
+  }
+  if (!logits || !x || !w13 || !topk_ids || !topk_w || !counts || !offsets || !sorted_pair ||
+      !pair_pos || !tiles || !n_tiles || !h)
+    return MOE_E_INVAL;
+  if (n_shared > 0 && !w13_shared) return MOE_E_INVAL;
+  if (!aligned(x, 16) || !aligned(h, 16) || !aligned(tiles, 16)) return MOE_E_INVAL;
+  const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  ProjArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.mode = 0;
+  a.in_bf16 = x;
+  a.ld_in = H;
+  a.w = w13;
+  a.w_sh = w13_shared;
+  a.K = H;
+  a.K_sh = H;
+  a.U = I;
+  a.U_sh = n_shared > 0 ? I_shared : 0;
+  a.T = T;
+  a.k = k;
+  a.P = T * k;
+  a.E = E;
+  a.n_shared = n_shared;
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.tiles = tiles;
+  a.n_tiles = n_tiles;
+  a.max_tiles = moe_permute_max_tiles(T, k, E, tile_m);
+  a.maxt = dec_maxt(T, tile_m);
+  a.out = h;
+  a.ld_out = ld_h_of(I, n_shared, I_shared);
+  a.err = reinterpret_cast<int32_t*>(ws + L.err);
+  return from_hip(launch_dec_route_gateup(a, logits, renormalize, tile_m, topk_ids, topk_w,
+                                          counts, offsets, sorted_pair, pair_pos, tiles,
+                                          n_tiles, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,

@@ -17,7 +17,6 @@ struct WsLayout {
   size_t qx;         // A8: int8 [T][H]
   size_t sx;         // A8: fp32 [T]
   size_t y;          // fp32 [R][H]
-  size_t cnt;        // int32 completion counters of the fused combine
   size_t a16;        // A16 MFMA path: fp16 activation copies (x twice, or h)
   size_t total;
 };
@@ -55,12 +54,10 @@ struct ProjArgs {
   void* out;                   // gate/up: h (bf16 or fp32); down: y fp32
   int ld_out;
   int32_t* err;
-  // fused combine (down only): the last block of each column range sums
-  // the weighted y rows of every token into out
+  // down with the combine fused (decode kernels): gate weights and the
+  // sorted row of every pair
   const float* topk_w;
   const int32_t* pair_pos;
-  uint16_t* comb_out;          // null: no fused combine
-  int32_t* cnt;
   int32_t* partials;           // A8 test hook (null otherwise)
   int ng_ld;
   int part_rows;               // row stride (in weight rows) of partials
@@ -84,6 +81,22 @@ int gemv_maxt(int T, int tile_m);
 hipError_t launch_proj_mfma(const ProjArgs& a, uint16_t* a16_4, uint16_t* a16_2,
                             hipStream_t st);
 bool mfma_available();
+// Decode-shape A16 projections (proj_decode.hip): tiles of at most 16
+// rows, H <= 2048 (gate/up) and I <= 1024 (down), down with the combine
+// fused when every h row of the layer fits in LDS.  a.maxt must be
+// dec_maxt(T, tile_m).
+int dec_maxt(int T, int tile_m);
+bool dec_gateup_ok(int T, int H, int tile_m);
+bool dec_down_ok(int T, int k, int E, int n_shared, int H, int I, int I_shared, int ld,
+                 int tile_m, int max_tiles);
+hipError_t launch_dec_gateup(const ProjArgs& a, hipStream_t st);
+hipError_t launch_dec_down_combine(const ProjArgs& a, uint16_t* out, hipStream_t st);
+// Route + permute + gate/up in one launch (T * k <= 64, E <= 512).
+bool dec_route_gateup_ok(int T, int H, int E, int k, int tile_m);
+hipError_t launch_dec_route_gateup(const ProjArgs& a, const float* logits, int renorm,
+                                   int tile_m, int32_t* ids, float* w, int32_t* counts,
+                                   int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                   int32_t* tiles, int32_t* n_tiles, hipStream_t st);
 hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
                           const int32_t* pair_pos, int T, int k, int H, int P,
                           int n_shared, uint16_t* out, hipStream_t st);

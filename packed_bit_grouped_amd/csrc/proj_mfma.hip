@@ -46,7 +46,6 @@ typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
 
 constexpr int kMThreads = 256;    // 4 waves, one per SIMD
 constexpr int kBM = 128;            // activation rows per tile chunk
-constexpr int kMB = kBM / 32;       // 32-row blocks (every wave covers all rows)
 constexpr int kRing = 4;            // steps in flight (register ring slots)
 constexpr int kKS = 64;             // K per pipeline step
 constexpr int kChunks = kKS / 8;    // 16-byte fp16 chunks per row and step

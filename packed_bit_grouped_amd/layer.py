@@ -139,10 +139,18 @@ def fused_routing_ok(T, E, k) -> bool:
 
 
 def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
-              flags: int = 0, stream=None) -> None:
-    """One layer step: route, permute, gate/up + SiLU*mul, down + combine."""
+              flags: int = 0, stream=None, fused: bool = True) -> None:
+    """One layer step: route, permute, gate/up + SiLU*mul, down + combine.
+    With ``fused`` the first three go through moe_w4_route_gateup_silu (one
+    launch for decode batches, else the separate calls)."""
     T, H, I, E, k = B.T, B.H, B.I, B.E, B.k
-    if fused_routing_ok(T, E, k):
+    if fused:
+        L.moe_w4_route_gateup_silu(B.act, logits, x, T, H, I, E, k, renormalize,
+                                   bank.w13, bank.w13_sh, B.n_shared, B.I_shared,
+                                   B.tile_m, B.ids, B.w, B.counts, B.offsets,
+                                   B.sorted_pair, B.pair_pos, B.tiles, B.n_tiles,
+                                   B.h, B.ws, B.ws_bytes, flags, stream)
+    elif fused_routing_ok(T, E, k):
         L.moe_route_permute(logits, T, E, k, renormalize, B.tile_m, B.ids, B.w,
                             B.counts, B.offsets, B.sorted_pair, B.pair_pos,
                             B.tiles, B.n_tiles, stream)
@@ -150,10 +158,11 @@ def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
         L.moe_route_topk(logits, T, E, k, renormalize, B.ids, B.w, stream)
         L.moe_permute(B.ids, T, k, E, B.tile_m, B.counts, B.offsets,
                       B.sorted_pair, B.pair_pos, B.tiles, B.n_tiles, stream)
-    L.moe_w4_gateup_silu(B.act, x, T, H, I, E, k, bank.w13, bank.w13_sh,
-                         B.n_shared, B.I_shared, B.offsets, B.sorted_pair,
-                         B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes,
-                         flags, stream)
+    if not fused:
+        L.moe_w4_gateup_silu(B.act, x, T, H, I, E, k, bank.w13, bank.w13_sh,
+                             B.n_shared, B.I_shared, B.offsets, B.sorted_pair,
+                             B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes,
+                             flags, stream)
     L.moe_w4_down_combine(B.act, B.h, T, H, I, E, k, bank.w2, bank.w2_sh,
                           B.n_shared, B.I_shared, B.w, B.offsets,
                           B.sorted_pair, B.pair_pos, B.tiles, B.n_tiles,
@@ -189,6 +198,6 @@ class DeviceLayer:
         return LayerBuffers(c.T, c.H, c.I, c.E, c.k, c.n_shared, c.I_shared, a,
                             tile_m, self.x.device)
 
-    def run(self, B: LayerBuffers, flags: int = 0, stream=None) -> None:
+    def run(self, B: LayerBuffers, flags: int = 0, stream=None, fused: bool = True) -> None:
         run_layer(self.bank, self.x, self.logits, B, self.cfg.renormalize,
-                  flags, stream)
+                  flags, stream, fused)

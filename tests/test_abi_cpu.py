@@ -54,24 +54,21 @@ def up256(n):
 
 
 def test_workspace_sizes():
-    # error word + fp32 y rows (+ int8 x and fp32 scales for A8) + combine
-    # counters (H/8 + 64 ints) (+ fp16 activation copies for the A16 matrix
-    # core path when H, I, I_shared are multiples of 128), each region
-    # 256-byte aligned
-    cnt = up256((2048 // 8 + 64) * 4)
+    # error word + fp32 y rows (+ int8 x and fp32 scales for A8) (+ fp16
+    # activation copies for the A16 matrix core path when H, I, I_shared are
+    # multiples of 128), each region 256-byte aligned
     a16 = up256(max(2 * 1 * 2048 * 2, 9 * 768 * 2))
     assert L.moe_workspace_bytes(0, 1, 2048, 768, 128, 8, 1, 768) == \
-        256 + 9 * 2048 * 4 + cnt + a16
+        256 + 9 * 2048 * 4 + a16
     a8 = L.moe_workspace_bytes(1, 64, 2048, 768, 128, 8, 0, 0)
-    assert a8 == 256 + 64 * 2048 + 256 + 512 * 2048 * 4 + cnt
-    assert L.moe_workspace_bytes(0, 0, 2048, 768, 128, 8, 0, 0) == 256 + cnt
+    assert a8 == 256 + 64 * 2048 + 256 + 512 * 2048 * 4
+    assert L.moe_workspace_bytes(0, 0, 2048, 768, 128, 8, 0, 0) == 256
     # no matrix-core copies when a dimension is not a multiple of 128
-    assert L.moe_workspace_bytes(0, 4, 256, 96, 8, 2, 0, 0) == \
-        256 + up256(8 * 256 * 4) + up256((256 // 8 + 64) * 4)
+    assert L.moe_workspace_bytes(0, 4, 256, 96, 8, 2, 0, 0) == 256 + up256(8 * 256 * 4)
     # shared expert wider than the routed ones sets the h stride
     a16 = up256(max(2 * 3 * 512 * 2, 3 * (2 + 1) * 384 * 2))
     assert L.moe_workspace_bytes(0, 3, 512, 256, 8, 2, 1, 384) == \
-        256 + up256(3 * 3 * 512 * 4) + up256((512 // 8 + 64) * 4) + a16
+        256 + up256(3 * 3 * 512 * 4) + a16
 
 
 FAKE = 1 << 20   # a non-null pointer value; never dereferenced on the host

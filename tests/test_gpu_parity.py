@@ -235,6 +235,22 @@ def test_fused_route_permute_matches_separate_calls():
         assert np.array_equal(outs[0][6][:, :3], o["tiles"])
 
 
+@pytest.mark.parametrize("name", ["c0", "c1", "e288", "k1", "mixed_shared", "norenorm"])
+def test_fused_route_gateup_matches_separate_calls(name):
+    """moe_w4_route_gateup_silu (one launch for decode batches) writes the
+    same routing tables and the same h, bit for bit, as moe_route_permute /
+    moe_route_topk + moe_permute followed by moe_w4_gateup_silu."""
+    cfg = {"c0": CONFIGS[0], "c1": CONFIGS[1], **MINIS}[name]
+    dl = _dev(cfg)
+    g1, _ = run_layer_gpu(dl, "a16", 16, fused=True)
+    g2, _ = run_layer_gpu(dl, "a16", 16, fused=False)
+    for key in ("ids", "w", "counts", "offsets", "sorted_pair", "pair_pos", "tiles",
+                "n_tiles", "out"):
+        assert np.array_equal(g1[key], g2[key]), key
+    assert np.array_equal(_valid_h(g1["h"], cfg), _valid_h(g2["h"], cfg))
+    assert g1["err"] == 0
+
+
 def test_permute_skips_out_of_range_ids():
     torch = torch_mod()
     from packed_bit_grouped_amd import _lib as L
@@ -392,6 +408,36 @@ def test_repeat_bitwise_identical():
     g3, _ = run_layer_gpu(dl, "a8", 16)
     g4, _ = run_layer_gpu(dl, "a8", 16)
     assert np.array_equal(g3["out"], g4["out"])
+
+
+@pytest.mark.parametrize("name", ["c1", "mixed_shared", "mfma_mixed"])
+def test_graph_replay_matches_eager(name):
+    """The whole step captured in a HIP graph (decode, split-K GEMV and
+    matrix-core forms): every replay, with eager work and synchronizations
+    in between, reproduces the eager step bit for bit."""
+    torch = torch_mod()
+    cfg = {"c1": CONFIGS[1], **MINIS, **MFMA}[name]
+    dl = _dev(cfg)
+    B = dl.buffers()
+    dl.run(B, 0)
+    torch.cuda.synchronize()
+    ref = collect(B)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dl.run(B, 0)
+    for rep in range(3):
+        B.out.zero_()
+        B.h.zero_()
+        B.sorted_pair.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = collect(B)
+        for key in ("ids", "counts", "offsets", "sorted_pair", "pair_pos", "tiles", "out"):
+            assert np.array_equal(got[key], ref[key]), (rep, key)
+        assert np.array_equal(_valid_h(got["h"], cfg), _valid_h(ref["h"], cfg)), (rep, "h")
+        dl.run(B, 0)
+        torch.cuda.synchronize()
 
 
 def test_side_stream_with_event_handoff():
