@@ -49,6 +49,23 @@ def touched_bytes(dl, counts, which=("w13", "w2")):
     return tot
 
 
+def measured_traffic(key):
+    """HBM bytes per launch from the byte-counter profiles (profiles/
+    traffic.json), or None when they are absent or were taken on other
+    kernel sources."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            t = json.load(f)[key]
+        h = hashlib.sha256()
+        for src in t["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        return t["bytes_per_launch"] if h.hexdigest() == t["source_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(layer, seconds, unit_amount, unit, sample_note):
     import numpy as np  # noqa: F401
     import oracle
@@ -82,6 +99,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=["auto", "gemv", "mfma"], default="auto")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="after the run, one device copy of MB MiB (a plain copy kernel of "
+                         "known size, the scale for hardware byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -139,9 +159,16 @@ def main():
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
 
     def gateup(bk):
-        L.moe_w4_gateup_silu(B.act, dl.x, T, H, I, E, k, bk.w13, bk.w13_sh,
-                             cfg.n_shared, cfg.I_shared, B.offsets, B.sorted_pair,
-                             B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes, flags)
+        if decode:   # the call run_layer makes: one launch for decode batches
+            L.moe_w4_route_gateup_silu(B.act, dl.logits, dl.x, T, H, I, E, k,
+                                       cfg.renormalize, bk.w13, bk.w13_sh, cfg.n_shared,
+                                       cfg.I_shared, B.tile_m, B.ids, B.w, B.counts,
+                                       B.offsets, B.sorted_pair, B.pair_pos, B.tiles,
+                                       B.n_tiles, B.h, B.ws, B.ws_bytes, flags)
+        else:
+            L.moe_w4_gateup_silu(B.act, dl.x, T, H, I, E, k, bk.w13, bk.w13_sh,
+                                 cfg.n_shared, cfg.I_shared, B.offsets, B.sorted_pair,
+                                 B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes, flags)
 
     def timed(fn, n):
         torch.cuda.synchronize()
@@ -159,21 +186,26 @@ def main():
     ms_eager = timed(step, args.steps)
     log(f"[bench] eager: {ms_eager * 1e3:.2f} us/step")
 
-    # the served form: one HIP graph per weight-bank copy holding the whole
-    # step (route+permute, gate/up, down+combine), replayed back to back
+    # the served form: HIP graphs of G consecutive steps over G distinct
+    # weight-bank copies (as a model's decode graph holds its layers, each
+    # with its own weights), replayed back to back
+    G = next(g for g in (16, 8, 4, 2, 1) if g <= len(banks) and args.steps % g == 0)
+    n_graphs = len(banks) // G
     graphs = []
-    for bi in range(len(banks)):
+    for gi in range(n_graphs):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            run_layer(banks[bi], dl.x, dl.logits, B, cfg.renormalize, flags)
+            for i in range(G):
+                run_layer(banks[gi * G + i], dl.x, dl.logits, B, cfg.renormalize, flags)
         graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
-    ms = timed(lambda i: graphs[i % len(graphs)].replay(), args.steps)
-    log(f"[bench] graph replay: {args.steps} steps: {ms * 1e3:.2f} us/step")
-    # check the replayed step against an eager one (same inputs, same bank)
+    reps = args.steps // G
+    for i in range(max(1, args.warmup // G)):
+        graphs[i % n_graphs].replay()
+    ms = timed(lambda i: graphs[i % n_graphs].replay(), reps) / G
+    log(f"[bench] graph replay: {reps * G} steps ({G} per graph): {ms * 1e3:.2f} us/step")
+    # check the replayed steps against an eager one (same inputs, same bank)
     out_g = B.out.clone()
-    step(args.steps - 1)
+    step((reps - 1) % n_graphs * G + G - 1)
     torch.cuda.synchronize()
     if not torch.equal(out_g, B.out):
         log("[bench] graph replay output differs from the eager step")
@@ -183,6 +215,8 @@ def main():
     # launches over distinct bank copies, timed with events on the stream
     # the graph runs on
     n_k = min(len(banks), 32) if decode else 4
+    kname = ("dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)" if decode
+             else "proj_mfma_kernel<0> + convert_x_kernel (gate/up + SiLU*mul)")
     gk = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gk):
         for i in range(n_k):
@@ -197,16 +231,18 @@ def main():
         unit = "GB/s"
         ach = bytes_w13 / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                "kernel": "proj_gemv_kernel (gate/up + SiLU*mul)",
+                "frac": ach / HBM_PEAK_GBS,
+                "traffic": measured_traffic(f"dec_route_gateup_kernel@{cfg.name}"),
+                "kernel": kname,
                 "algorithmic_bytes": bytes_w13}
     else:
         value = flops / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
         ach = flops_gateup / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None,
-                "kernel": "gate/up + SiLU*mul", "algorithmic_flops": flops_gateup}
+                "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                "traffic": measured_traffic(f"gateup_call@{cfg.name}"),
+                "kernel": kname, "algorithmic_flops": flops_gateup}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -229,12 +265,20 @@ def main():
                    "experts_touched": n_touched,
                    "bytes_per_step": bytes_all, "flops_per_step": flops,
                    "bank_copies_rotated": len(banks), "path": args.path,
-                   "timing": "HIP graph replay of the whole step, back to back",
+                   "timing": f"HIP graphs of {G} steps over {G} weight copies, replayed back to back",
                    "ms_per_step_eager": ms_eager},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.copy_probe > 0:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {n} bytes read and written")
 
 
 if __name__ == "__main__":
