@@ -192,7 +192,6 @@ struct AStep {
 template <int BITS>
 struct BStep {
   uint32_t c[2][BITS];   // code words of the two weight rows (16 or 8 bytes each)
-  uint32_t s[2];         // fp16 group scale of each row (low half)
 };
 
 // Where one workgroup works: a tile chunk of sorted rows of one matrix.
@@ -205,13 +204,15 @@ struct TileCtx {
   bool is_sh;
 };
 
-// This lane's weight rows and their buffer descriptors.
+// This lane's weight rows, their code buffer descriptor and their group
+// scales, staged in LDS once per tile.
 struct WeightCtx {
-  __amdgpu_buffer_rsrc_t crs, srs;
-  int coff[2], soff[2];
+  __amdgpu_buffer_rsrc_t crs;
+  int coff[2];
+  const uint16_t* sc[2];   // LDS: this lane's two rows of group scales
   int wrow[2];
   bool wval[2];
-  int n_st, sshift;
+  int n_st, gsh;           // steps, log2(group)
 };
 
 // K loop and epilogue of one chunk of up to 32 * MB rows (tok[] holds
@@ -231,7 +232,6 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
 
   auto load_b = [&](int st, BStep<BITS>& b) {
     st = min(st, n_st - 1);
-    const int sst = (w.sshift >= 0 ? st << w.sshift : st >> -w.sshift) * 2;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if constexpr (BITS == 4) {
@@ -243,7 +243,6 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
             __builtin_amdgcn_raw_buffer_load_b64(w.crs, w.coff[s], st * kStepBytes, 0);
         b.c[s][0] = t.x; b.c[s][1] = t.y;
       }
-      b.s[s] = __builtin_amdgcn_raw_buffer_load_b16(w.srs, w.soff[s], sst, 0);
     }
   };
   // A staging: 32 * MB rows x 128 bytes per step, LDS laid out [row m][8
@@ -278,7 +277,11 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
 
   // steps past the last one (the loop runs whole trips of kRing steps)
   // re-read the last step with a zero scale: they add exact zeros
-  auto compute = [&](int buf, const BStep<BITS>& b, bool live) {
+  auto compute = [&](int buf, const BStep<BITS>& b, int stg) {
+    const bool live = stg < n_st;
+    // group scales of this step (64 stg + 32 kh lies in group (..) >> gsh)
+    const int gi = (min(stg, n_st - 1) * kKS + kh * 32) >> w.gsh;
+    const uint32_t sc0 = w.sc[0][gi], sc1 = w.sc[1][gi];
     const u32x4_v* Ab = As + buf * kChunks * kBM + ln * kChunks;
     // the whole step's A fragments first: one LDS round trip per step
     u32x4_v af[4][MB];
@@ -288,8 +291,8 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
       for (int mb = 0; mb < MB; ++mb)
         af[st][mb] = Ab[32 * kChunks * mb + ((kh * 4 + st) ^ (ln & 7))];
     const uint32_t m16 = live ? 0x10001u : 0u;
-    const f16x2_v s0 = as_h2(b.s[0] * m16);
-    const f16x2_v s1 = as_h2(b.s[1] * m16);
+    const f16x2_v s0 = as_h2(sc0 * m16);
+    const f16x2_v s1 = as_h2(sc1 * m16);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       f16x8_v b0, b1;
@@ -346,7 +349,7 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
   store_a(0, ar0);
   __syncthreads();
 #define MOE_STEP(J, AC, BC, AN)                     \
-  compute(J & 1, BC, base + J < n_st);              \
+  compute(J & 1, BC, base + J);                     \
   store_a((J + 1) & 1, AN);                         \
   load_a(base + J + kRing, AC);                     \
   load_b(base + J + kRing, BC);                     \
@@ -386,7 +389,7 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
 // costs what its rows need.
 template <int MODE, int BITS>
 __device__ __forceinline__ void mfma_tile(const ProjArgs& a, const TileCtx& c, u32x4_v* As,
-                                          int* tok) {
+                                          int* tok, uint16_t* ssc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, kh = lane >> 5;
   const int K = c.K, U = c.U;
@@ -411,15 +414,38 @@ __device__ __forceinline__ void mfma_tile(const ProjArgs& a, const TileCtx& c, u
   }
   const int n_wrows = MODE == 0 ? 2 * U : U;
   w.crs = make_rsrc(c.codes, (uint32_t)(n_wrows * row_bytes));
-  w.srs = make_rsrc(c.scales, (uint32_t)(n_wrows * ng * 2));
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int r = w.wval[s] ? w.wrow[s] : 0;
     w.coff[s] = r * row_bytes + kh * kLaneBytes;
-    w.soff[s] = (r * ng + (c.group == 32 ? kh : 0)) * 2;
   }
-  // scale index of step st: (64 st + 32 kh) / group
-  w.sshift = c.group == 32 ? 1 : (c.group == 64 ? 0 : (c.group == 128 ? -1 : -2));
+  w.gsh = 31 - __builtin_clz(c.group);
+
+  // ---- the group scales of the workgroup's 256 weight rows into LDS,
+  // [local row][group]: gate rows u0.. then up rows U+u0.. (gate/up), or
+  // down rows u0..; two contiguous runs of the scale matrix, copied in
+  // 16-byte words (row runs start at multiples of 128 rows, so they are
+  // 16-byte aligned).  The first barrier of the chunk loop publishes them.
+  {
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(c.scales, (uint32_t)(n_wrows * ng * 2));
+    const int run_rows = MODE == 0 ? kBM : min(2 * kBM, U - c.u0);
+    const int run_words = run_rows * ng * 2 / 16;
+    const int n_runs = MODE == 0 ? 2 : 1;
+    for (int q = tid; q < n_runs * run_words; q += kMThreads) {
+      const int run = q >= run_words, qq = q - run * run_words;
+      const int row0 = run ? U + c.u0 : c.u0;
+      const u32x4_v v =
+          __builtin_amdgcn_raw_buffer_load_b128(srs, row0 * ng * 2 + qq * 16, 0, 0);
+      reinterpret_cast<u32x4_v*>(ssc + (size_t)run * kBM * ng)[qq] = v;
+    }
+  }
+  if (MODE == 0) {
+    w.sc[0] = ssc + (32 * wave + ln) * ng;
+    w.sc[1] = ssc + (kBM + 32 * wave + ln) * ng;
+  } else {
+    w.sc[0] = ssc + (64 * wave + ln) * ng;
+    w.sc[1] = ssc + (64 * wave + ln + 32) * ng;
+  }
 
   for (int mc = c.r_begin; mc < c.r_end; mc += kBM) {
     const int nrows = min(kBM, c.r_end - mc);
@@ -445,13 +471,23 @@ void proj_mfma_kernel(ProjArgs a, const uint16_t* x16_4,
   extern __shared__ __align__(16) unsigned char smem[];
   u32x4_v* As = reinterpret_cast<u32x4_v*>(smem);                  // [2][kBM][kChunks]
   int* tok = reinterpret_cast<int*>(smem + 2 * kChunks * kBM * 16);  // [kBM]
+  uint16_t* ssc = reinterpret_cast<uint16_t*>(tok + kBM);             // [256][K / group]
   const int tid = threadIdx.x;
 
-  // ---- block -> (tile slot, unit block); blocks of one slot share an XCD
+  // ---- block -> (tile slot, unit block).  Block b runs on XCD b mod 8; each
+  // XCD takes a contiguous range of the device-side slots, in order, so
+  // the blocks of one tile (they share its activation rows) and the tiles
+  // of one expert (they share its weights) run on one XCD at about the
+  // same time and meet in its L2.
   const int b = blockIdx.x;
   const int xcd = b % kXcd, li = b / kXcd;
   const int nb = li % a.n_rb;
-  const int slot = (li / a.n_rb) * kXcd + xcd;
+  const int n_slots = a.n_sh_slots + min(*a.n_tiles, a.max_tiles);
+  const int per_xcd = (n_slots + kXcd - 1) / kXcd;
+  const int local = li / a.n_rb;
+  if (local >= per_xcd) return;
+  const int slot = xcd * per_xcd + local;
+  if (slot >= n_slots) return;
   TileCtx c;
   if (slot < a.n_sh_slots) {
     const int per = (a.T + a.sh_tile - 1) / a.sh_tile;
@@ -490,10 +526,10 @@ void proj_mfma_kernel(ProjArgs a, const uint16_t* x16_4,
   c.a_bytes = (uint32_t)((size_t)(MODE == 0 ? a.T : a.P + a.n_shared * a.T) * a.ld_in * 2);
   if (q.bits == 4) {
     c.asrc = MODE == 0 ? x16_4 : a.in_bf16;
-    mfma_tile<MODE, 4>(a, c, As, tok);
+    mfma_tile<MODE, 4>(a, c, As, tok, ssc);
   } else {
     c.asrc = MODE == 0 ? x16_2 : a.in_bf16;
-    mfma_tile<MODE, 2>(a, c, As, tok);
+    mfma_tile<MODE, 2>(a, c, As, tok, ssc);
   }
 }
 
@@ -521,7 +557,12 @@ hipError_t launch_proj_mfma(const ProjArgs& a_in, uint16_t* a16_4, uint16_t* a16
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)2 * kChunks * kBM * 16 + kBM * sizeof(int);
+  // A tile, row table, and the scales of 256 weight rows at the smallest
+  // group (32)
+  const int Kmax = a.K_sh > a.K ? a.K_sh : a.K;
+  const size_t lds = (size_t)2 * kChunks * kBM * 16 + kBM * sizeof(int) +
+                     (size_t)2 * kBM * (Kmax / 32) * 2;
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
   if (a.mode == 0)
     proj_mfma_kernel<0><<<(unsigned)blocks, kMThreads, lds, st>>>(a, a16_4, a16_2);
   else
