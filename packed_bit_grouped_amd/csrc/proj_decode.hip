@@ -488,17 +488,19 @@ __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs 
 
   // ---- the tiles: 4 rows (columns n0..n0+3) of each, every token
   auto run = [&](const int i) {
-    if (!ok[i]) return;
-    // one pass: the launcher guarantees a tile has at most MAXT rows
-    const int nt = min(MAXT, tr1[i] - tr0[i]);
-    const int hrow0 = (shr[i] ? a.P + te[i] * a.T : 0) + tr0[i];
+    // one pass: the launcher guarantees a tile has at most MAXT rows; a
+    // wave without a tile in this round computes nothing and stores
+    // nothing (no early exit, so both rounds stay one straight block)
+    const int nt = ok[i] ? min(MAXT, tr1[i] - tr0[i]) : 0;
+    const int hrow0 = ok[i] ? (shr[i] ? a.P + te[i] * a.T : 0) + tr0[i] : 0;
+    const int C_r = ok[i] ? G[i].C_r : 0;
     float acc[MAXT];
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) acc[t] = 0.0f;
 #pragma unroll
     for (int b = 0; b < CPL; ++b) {
       const int c = lis + kDecDnLanes * b;
-      if (c < G[i].C_r)
+      if (c < C_r)
         chunk_dot<MOE_A16, MAXT, false>(a, wv[i][b], sv[i][b], c, G[i], nt,
                                         xs + (size_t)hrow0 * xs_row, xs_row,
                                         xsum + (size_t)hrow0 * xsum_row, xsum_row, acc, lis,
@@ -524,10 +526,22 @@ __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs 
   for (int idx = tid; idx < a.T * kDecDnCols; idx += kDecThreads) {
     const int t = idx / kDecDnCols, cc = idx - t * kDecDnCols;
     float acc = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-      const int pp = ppos[t * a.k + j];
-      if (pp < 0) continue;
-      acc = fmaf(gw[t * a.k + j], yb[(size_t)pp * kDecDnCols + cc], acc);
+    // eight pairs at a time: all LDS reads first, then the fma chain in j
+    // order
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+      int pp[8];
+      float wj[8], yv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = j0 + u < a.k;
+        pp[u] = in ? ppos[t * a.k + j0 + u] : -1;
+        wj[u] = in ? gw[t * a.k + j0 + u] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) yv[u] = pp[u] >= 0 ? yb[(size_t)pp[u] * kDecDnCols + cc] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (pp[u] >= 0) acc = fmaf(wj[u], yv[u], acc);
     }
     for (int s = 0; s < a.n_shared; ++s) acc += yb[(size_t)(a.P + s * a.T + t) * kDecDnCols + cc];
     out[(size_t)t * H + n0 + cc] = (uint16_t)f32_to_bf16(acc);
