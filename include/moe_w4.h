@@ -189,6 +189,10 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
                               /* copies of x (T*H) and h (T*(k+n_shared)      */
                               /* rows of max(I, I_shared)) under 2 GiB, else  */
                               /* MOE_E_UNSUPPORTED                            */
+#define MOE_PATH_MFMA16 3     /* 16x16 MFMA tiles of at most 16 rows (decode */
+                              /* batches; both modes): tile_m <= 16 and the   */
+                              /* tile's activations within 160 KB of LDS,     */
+                              /* else MOE_E_UNSUPPORTED                       */
 #define MOE_PATH_MASK 3
 
 /* Tile height to pass as moe_permute's tile_m: 128 (the MFMA path's row

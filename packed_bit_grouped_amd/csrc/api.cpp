@@ -70,7 +70,6 @@ moe_status check_layer(int act, int T, int H, int I, int E, int k, int n_shared,
   if (n_shared > 0 && I_shared <= 0) return MOE_E_INVAL;
   if (tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
   if (flags & ~MOE_PATH_MASK) return MOE_E_INVAL;
-  if ((flags & MOE_PATH_MASK) == 3) return MOE_E_INVAL;
   if (H % 32 || I % 32 || (n_shared > 0 && I_shared % 32)) return MOE_E_UNSUPPORTED;
   if (E > kPermMaxE) return MOE_E_UNSUPPORTED;
   if ((long long)T * k >= (1LL << 24)) return MOE_E_UNSUPPORTED;
@@ -94,10 +93,14 @@ bool mfma_shape_ok(int act, int T, int H, int I, int k, int n_shared, int I_shar
   return (long long)T * H * 2 < (1LL << 31) && rows * ld_h * 2 < (1LL << 31);
 }
 
+// Decode batches up to this many pairs take the vector-ALU decode kernels
+// (about one row per expert tile); larger ones the 16-row MFMA tiles.
+constexpr long long kDecPairs = 64;
+
 bool use_mfma(int act, int T, int H, int I, int E, int k, int n_shared,
               int I_shared, int flags) {
   const int path = flags & MOE_PATH_MASK;
-  if (path == MOE_PATH_GEMV) return false;
+  if (path == MOE_PATH_GEMV || path == MOE_PATH_MFMA16) return false;
   if (path == MOE_PATH_MFMA) return true;
   return mfma_available() && mfma_shape_ok(act, T, H, I, k, n_shared, I_shared) &&
          (long long)T * k >= 32LL * E;
@@ -117,6 +120,14 @@ WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
   if (act == MOE_A8) off += up256((size_t)T * H);
   L.sx = off;
   if (act == MOE_A8) off += up256((size_t)T * 4);
+  L.qh = off;
+  L.sh = off;
+  if (act == MOE_A8) {
+    const size_t R = (size_t)T * (k + n_shared);
+    off += up256(R * (size_t)ld_h_of(I, n_shared, I_shared));
+    L.sh = off;
+    off += up256(R * 4);
+  }
   L.y = off;
   off += up256((size_t)T * (k + n_shared) * H * 4);
   L.a16 = off;
@@ -223,7 +234,7 @@ moe_status moe_quant_a8_rows(const void* src, int src_is_f32, int R, int C,
   if (!src || !q || !s) return MOE_E_INVAL;
   const moe_status d = check_device();
   if (d != MOE_OK) return d;
-  return from_hip(launch_quant_a8(src, src_is_f32, R, C, ld, q, s,
+  return from_hip(launch_quant_a8(src, src_is_f32, R, C, ld, q, C, s,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -244,6 +255,11 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
   if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return MOE_E_WORKSPACE;
   if (partials && ng_ld <= 0) return MOE_E_INVAL;
+  const int path = flags & MOE_PATH_MASK;
+  const bool m16 = !partials && m16_ok(act, 0, T, H, H, tile_m);
+  if (path == MOE_PATH_MFMA16 && !m16) return MOE_E_UNSUPPORTED;
+  if (path == MOE_PATH_MFMA && !mfma_shape_ok(act, T, H, I, k, n_shared, I_shared))
+    return MOE_E_UNSUPPORTED;
   st = check_device();
   if (st != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -286,17 +302,23 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   if (act == MOE_A8) {
     int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
     float* sx = reinterpret_cast<float*>(ws + L.sx);
-    hipError_t e = launch_quant_a8(x, 0, T, H, H, qx, sx, s);
+    hipError_t e = launch_quant_a8(x, 0, T, H, H, qx, H, sx, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     a.in_q = qx;
     a.in_s = sx;
   } else {
     a.in_bf16 = x;
   }
+  const bool dec = act == MOE_A16 && !partials && dec_gateup_ok(T, H, tile_m);
+  if (path == MOE_PATH_MFMA16 ||
+      (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs))) {
+    if (act == MOE_A8) a.ld_in = H;
+    return from_hip(launch_proj_m16(a, act, s));
+  }
   a.maxt = gemv_maxt(T, tile_m);
   a.sh_tile = a.maxt;
   a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
-  if (act == MOE_A16 && !partials && dec_gateup_ok(T, H, tile_m)) {
+  if (dec) {
     a.maxt = dec_maxt(T, tile_m);
     return from_hip(launch_dec_gateup(a, s));
   }
@@ -322,6 +344,11 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
   const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
   if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return MOE_E_WORKSPACE;
   if (partials && ng_ld <= 0) return MOE_E_INVAL;
+  const int path = flags & MOE_PATH_MASK;
+  const bool m16 = !partials && m16_ok(act, 1, T, I, n_shared > 0 ? I_shared : I, tile_m);
+  if (path == MOE_PATH_MFMA16 && !m16) return MOE_E_UNSUPPORTED;
+  if (path == MOE_PATH_MFMA && !mfma_shape_ok(act, T, H, I, k, n_shared, I_shared))
+    return MOE_E_UNSUPPORTED;
   st = check_device();
   if (st != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -367,11 +394,31 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
   }
   if (act == MOE_A8) a.in_f32 = static_cast<const float*>(h);
   else a.in_bf16 = static_cast<const uint16_t*>(h);
+  const bool dec = act == MOE_A16 && !partials &&
+                   dec_down_ok(T, k, E, n_shared, H, I, I_shared, ld_h, tile_m, a.max_tiles);
+  if (path == MOE_PATH_MFMA16 ||
+      (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs))) {
+    if (act == MOE_A8) {   // int8 h rows for the int8 MFMA
+      int8_t* qh = reinterpret_cast<int8_t*>(ws + L.qh);
+      float* sh = reinterpret_cast<float*>(ws + L.sh);
+      const int P = T * k;
+      e = launch_quant_a8(h, 1, P, I, ld_h, qh, ld_h, sh, s);
+      if (e == hipSuccess && n_shared > 0)
+        e = launch_quant_a8(static_cast<const float*>(h) + (size_t)P * ld_h, 1, n_shared * T,
+                            I_shared, ld_h, qh + (size_t)P * ld_h, ld_h, sh + P, s);
+      if (e != hipSuccess) return MOE_E_DEVICE;
+      a.in_q = qh;
+      a.in_s = sh;
+    }
+    e = launch_proj_m16(a, act, s);
+    if (e != hipSuccess) return MOE_E_DEVICE;
+    return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
+                                   n_shared, out, s));
+  }
   a.maxt = gemv_maxt(T, tile_m);
   a.sh_tile = a.maxt;
   a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
-  if (act == MOE_A16 && !partials &&
-      dec_down_ok(T, k, E, n_shared, H, I, I_shared, ld_h, tile_m, a.max_tiles)) {
+  if (dec) {
     a.maxt = dec_maxt(T, tile_m);
     a.topk_w = topk_w;
     a.pair_pos = pair_pos;
@@ -407,7 +454,7 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits, const uint16_t
   moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
   if (st != MOE_OK) return st;
   if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
-  const bool fused = act == MOE_A16 && T > 0 &&
+  const bool fused = act == MOE_A16 && T > 0 && (flags & MOE_PATH_MASK) != MOE_PATH_MFMA16 &&
                      !use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
                      dec_route_gateup_ok(T, H, E, k, tile_m);
   if (!fused) {

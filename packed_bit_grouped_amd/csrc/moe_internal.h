@@ -16,6 +16,8 @@ struct WsLayout {
   size_t err;        // int32 error word
   size_t qx;         // A8: int8 [T][H]
   size_t sx;         // A8: fp32 [T]
+  size_t qh;         // A8: int8 h rows [R][ld_h] (matrix-core decode path)
+  size_t sh;         // A8: fp32 [R]
   size_t y;          // fp32 [R][H]
   size_t a16;        // A16 MFMA path: fp16 activation copies (x twice, or h)
   size_t total;
@@ -74,8 +76,9 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k,
                                 int32_t* counts, int32_t* offsets,
                                 int32_t* sorted_pair, int32_t* pair_pos,
                                 int32_t* tiles, int32_t* n_tiles, hipStream_t st);
+// Rows [R][C] (row stride ld) to int8 rows of stride ldq and fp32 scales.
 hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
-                           int8_t* q, float* s, hipStream_t st);
+                           int8_t* q, int ldq, float* s, hipStream_t st);
 hipError_t launch_proj_gemv(const ProjArgs& a, int act, int grid, hipStream_t st);
 int gemv_maxt(int T, int tile_m);
 hipError_t launch_proj_mfma(const ProjArgs& a, uint16_t* a16_4, uint16_t* a16_2,
@@ -97,6 +100,11 @@ hipError_t launch_dec_route_gateup(const ProjArgs& a, const float* logits, int r
                                    int tile_m, int32_t* ids, float* w, int32_t* counts,
                                    int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                                    int32_t* tiles, int32_t* n_tiles, hipStream_t st);
+// Tiles of at most 16 rows on 16x16 MFMAs (proj_m16.hip).  A8 inputs are
+// int8 rows (a.in_q, stride a.ld_in) with fp32 row scales (a.in_s): x for
+// gate/up, the quantized h rows for down.
+bool m16_ok(int act, int mode, int T, int K, int K_sh, int tile_m);
+hipError_t launch_proj_m16(const ProjArgs& a, int act, hipStream_t st);
 hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
                           const int32_t* pair_pos, int T, int k, int H, int P,
                           int n_shared, uint16_t* out, hipStream_t st);

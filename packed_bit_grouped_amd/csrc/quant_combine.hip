@@ -10,7 +10,7 @@ namespace moe {
 // shared a8_scale / a8_code rule.
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const void* __restrict__ src, int is_f32, int C, int ld,
-    int8_t* __restrict__ q, float* __restrict__ s) {
+    int8_t* __restrict__ q, int ldq, float* __restrict__ s) {
   __shared__ float red[4];
   const int r = blockIdx.x, tid = threadIdx.x;
   const uint16_t* rb = static_cast<const uint16_t*>(src) + (size_t)r * ld;
@@ -27,15 +27,15 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const float sc = a8_scale(amax);
   for (int c = tid; c < C; c += 256) {
     const float v = is_f32 ? rf[c] : bf16_to_f32(rb[c]);
-    q[(size_t)r * C + c] = (int8_t)a8_code(v, sc);
+    q[(size_t)r * ldq + c] = (int8_t)a8_code(v, sc);
   }
   if (tid == 0) s[r] = sc;
 }
 
 hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
-                           int8_t* q, float* s, hipStream_t st) {
+                           int8_t* q, int ldq, float* s, hipStream_t st) {
   if (R == 0) return hipSuccess;
-  quant_rows_kernel<<<R, 256, 0, st>>>(src, is_f32, C, ld, q, s);
+  quant_rows_kernel<<<R, 256, 0, st>>>(src, is_f32, C, ld, q, ldq, s);
   return hipGetLastError();
 }
 

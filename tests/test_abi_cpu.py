@@ -60,8 +60,11 @@ def test_workspace_sizes():
     a16 = up256(max(2 * 1 * 2048 * 2, 9 * 768 * 2))
     assert L.moe_workspace_bytes(0, 1, 2048, 768, 128, 8, 1, 768) == \
         256 + 9 * 2048 * 4 + a16
+    # A8: int8 x + scales, then int8 h rows (stride max(I, I_shared)) + scales
     a8 = L.moe_workspace_bytes(1, 64, 2048, 768, 128, 8, 0, 0)
-    assert a8 == 256 + 64 * 2048 + 256 + 512 * 2048 * 4
+    assert a8 == 256 + 64 * 2048 + 256 + 512 * 768 + 512 * 4 + 512 * 2048 * 4
+    a8 = L.moe_workspace_bytes(1, 3, 512, 256, 8, 2, 1, 384)
+    assert a8 == 256 + up256(3 * 512) + 256 + up256(9 * 384) + 256 + up256(9 * 512 * 4)
     assert L.moe_workspace_bytes(0, 0, 2048, 768, 128, 8, 0, 0) == 256
     # no matrix-core copies when a dimension is not a multiple of 128
     assert L.moe_workspace_bytes(0, 4, 256, 96, 8, 2, 0, 0) == 256 + up256(8 * 256 * 4)
@@ -122,8 +125,15 @@ def test_gateup_validation():
     assert _gateup(ws_bytes=16) == L.MOE_E_WORKSPACE
     assert _gateup(workspace=None) == L.MOE_E_WORKSPACE
     assert _gateup(workspace=FAKE + 64) == L.MOE_E_WORKSPACE  # 256-byte alignment
-    assert _gateup(flags=3) == L.MOE_E_INVAL
+    assert _gateup(flags=4) == L.MOE_E_INVAL
     assert _gateup(flags=8) == L.MOE_E_INVAL
+    # forced 16-row MFMA tiles: tiles of at most 16 rows, activations in LDS
+    assert _gateup(flags=L.MOE_PATH_MFMA16, tile_m=32) == L.MOE_E_UNSUPPORTED
+    assert _gateup(flags=L.MOE_PATH_MFMA16, T=16, H=8192) == L.MOE_E_UNSUPPORTED
+    assert _gateup(flags=L.MOE_PATH_MFMA16) == L.MOE_E_DEVICE
+    # forced MFMA grouped GEMM on a shape it does not cover
+    assert _gateup(flags=L.MOE_PATH_MFMA, I=96) == L.MOE_E_UNSUPPORTED
+    assert _gateup(flags=L.MOE_PATH_MFMA, act=1) == L.MOE_E_UNSUPPORTED
     assert _gateup(E=600, k=2) == L.MOE_E_UNSUPPORTED
     assert _gateup(T=0, x=None) == L.MOE_OK               # empty batch
     # everything valid: only the device check remains, and there is no GPU here
@@ -144,6 +154,8 @@ def test_down_validation():
     assert call(out=FAKE + 2) == L.MOE_E_INVAL
     assert call(ws_bytes=100) == L.MOE_E_WORKSPACE
     assert call(T=0, h=None) == L.MOE_OK
+    assert call(flags=L.MOE_PATH_MFMA16, tile_m=17) == L.MOE_E_UNSUPPORTED
+    assert call(flags=L.MOE_PATH_MFMA16) == L.MOE_E_DEVICE
     assert call() == L.MOE_E_DEVICE
 
 

@@ -142,6 +142,31 @@ def test_benchmark_layers_full(cid):
     _check_layer(CONFIGS[cid])
 
 
+# 16-row MFMA tiles (flags 3): every small layer (int4 and int2 experts,
+# groups 32..256, shared experts, E = 1, k = E), both activation modes,
+# ragged tile sizes, and the decode layers at full size.
+@pytest.mark.parametrize("name", list(MINIS) + list(MID))
+def test_m16_path_layers(name):
+    cfg = MINIS.get(name) or MID[name]
+    _check_layer(cfg, flags=3)
+
+
+@pytest.mark.parametrize("name", ["c0", "mixed_shared", "mid_mixed", "mid_g256", "e288"])
+def test_m16_path_as_a8(name):
+    cfg = MINIS.get(name) or MID[name]
+    _check_layer(cfg, act="a8", flags=3)
+
+
+@pytest.mark.parametrize("tile_m", [1, 5, 16])
+def test_m16_tile_sizes(tile_m):
+    _check_layer(MID["mid_mixed"], tile_m=tile_m, flags=3)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_m16_benchmark_layers(cid):
+    _check_layer(CONFIGS[cid], flags=3)
+
+
 def test_route_ties_and_large_E():
     torch = torch_mod()
     from packed_bit_grouped_amd import _lib as L
