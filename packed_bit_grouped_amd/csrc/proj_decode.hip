@@ -356,10 +356,9 @@ __global__ __launch_bounds__(kDecThreads) void dec_route_gateup_kernel(ProjArgs 
   // ---- round trip 1: descriptors and logits; routing and sorting
   copy_descs(descs, a);
   const bool writer = blockIdx.x == 0;
-  for (int t = wave; t < a.T; t += kDecWaves)
-    route_token<NV>(logits + (size_t)t * E, E, a.k, renorm, lane,
-                    writer ? ro.ids + t * a.k : nullptr, writer ? ro.w + t * a.k : nullptr,
-                    rid + t * a.k, rw + t * a.k);
+  static_assert(kFusedMaxP <= 8 * kDecWaves, "every token routed in two passes");
+  route_tokens<NV, 2>(logits, a.T, E, a.k, renorm, lane, wave, kDecWaves,
+                      writer ? ro.ids : nullptr, writer ? ro.w : nullptr, rid, rw);
   __syncthreads();
   if (wave == 0) wave_permute<NV>(rid, P, E, tile_m, srt, til, ntl, writer ? &ro : nullptr);
   __syncthreads();

@@ -133,77 +133,92 @@ __device__ __forceinline__ int m16_src_row(const ProjArgs& a, bool is_sh, int e,
   return is_sh ? a.P + e * a.T + r_begin + t : r_begin + t;
 }
 
-// Stage rows [r_begin, r_begin + nt) into LDS (layout in the file comment)
-// and, for bf16, the sum of every 32-K block of each row.  No barrier.
-template <int MODE, int ACT, int BITS>
-__device__ __forceinline__ void m16_stage_x(const ProjArgs& a, bool is_sh, int e, int r_begin,
-                                            int nt, int S, unsigned char* xs, int xstride,
-                                            float* bsum, float* xsc, int Sl) {
-  const int tid = threadIdx.x, nth = kM16Threads;
-  const int items = nt * S;   // (row, 32-K block)
-  for (int base = 0; base < items; base += nth * kM16StageIt) {
-    if (ACT == MOE_A16) {
-      u32x4_v v[kM16StageIt][4];
+// Activation staging (layout in the file comment).  Work item = (tile row
+// t, 32-K block b), it = t * S + b; a thread takes items tid + i * threads.
+// The rows of the first batch are resolved before the weight descriptor
+// is read (m16_first_rows), their loads are issued before the weight ring
+// (m16_x_load), and the LDS stores follow the ring issue (m16_x_store).
+template <int ACT>
+struct M16XRegs {
+  u32x4_v v[kM16StageIt][ACT == MOE_A16 ? 4 : 2];
+};
+
+template <int MODE>
+__device__ __forceinline__ void m16_row_loads(const ProjArgs& a, int r_begin, int nt, int S,
+                                              int (&srow)[kM16StageIt],
+                                              int (&trow)[kM16StageIt]) {
+  // every index clamped into the tile (r_begin + t < P also for shared
+  // slots, whose rows are tokens), so the loads are issued together
 #pragma unroll
-      for (int i = 0; i < kM16StageIt; ++i) {
-        const int it = base + i * nth + tid;
-        if (it < items) {
-          const int t = it / S, b = it - t * S;
-          const int row = m16_src_row<MODE>(a, is_sh, e, r_begin, t);
-          const u32x4_v* src =
-              reinterpret_cast<const u32x4_v*>(a.in_bf16 + (size_t)row * a.ld_in + 32 * b);
+  for (int i = 0; i < kM16StageIt; ++i) {
+    trow[i] = min((i * kM16Threads + (int)threadIdx.x) / S, nt - 1);
+    if (MODE == 0) srow[i] = ld_global(a.sorted_pair + r_begin + trow[i]);
+  }
+}
+template <int MODE>
+__device__ __forceinline__ void m16_row_finish(const ProjArgs& a, bool is_sh, int e, int r_begin,
+                                               int (&srow)[kM16StageIt],
+                                               const int (&trow)[kM16StageIt]) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[i][c] = ld_global(src + c);
-        }
-      }
+  for (int i = 0; i < kM16StageIt; ++i) {
+    if (MODE == 0) srow[i] = is_sh ? r_begin + trow[i] : srow[i] / a.k;
+    else srow[i] = m16_src_row<MODE>(a, is_sh, e, r_begin, trow[i]);
+  }
+}
+
+template <int ACT>
+__device__ __forceinline__ void m16_x_load(const ProjArgs& a, int base, int items, int S,
+                                           const int (&srow)[kM16StageIt], M16XRegs<ACT>& x) {
 #pragma unroll
-      for (int i = 0; i < kM16StageIt; ++i) {
-        const int it = base + i * nth + tid;
-        if (it < items) {
-          const int t = it / S, b = it - t * S;
-          u32x4_v* dst = reinterpret_cast<u32x4_v*>(xs + t * xstride + 64 * b);
-          float sum = 0.0f;
+  for (int i = 0; i < kM16StageIt; ++i) {
+    const int it = base + i * kM16Threads + threadIdx.x;
+    if (it < items) {
+      const int b = it - (it / S) * S;
+      if (ACT == MOE_A16) {
+        const u32x4_v* src =
+            reinterpret_cast<const u32x4_v*>(a.in_bf16 + (size_t)srow[i] * a.ld_in + 32 * b);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            dst[c] = m16_order_a16(v[i][c]);
-            sum += bf16_to_f32(v[i][c].x & 0xFFFFu) + bf16_to_f32(v[i][c].x >> 16);
-            sum += bf16_to_f32(v[i][c].y & 0xFFFFu) + bf16_to_f32(v[i][c].y >> 16);
-            sum += bf16_to_f32(v[i][c].z & 0xFFFFu) + bf16_to_f32(v[i][c].z >> 16);
-            sum += bf16_to_f32(v[i][c].w & 0xFFFFu) + bf16_to_f32(v[i][c].w >> 16);
-          }
-          bsum[t * Sl + b] = sum;
-        }
-      }
-    } else {
-      u32x4_v v[kM16StageIt][2];
-#pragma unroll
-      for (int i = 0; i < kM16StageIt; ++i) {
-        const int it = base + i * nth + tid;
-        if (it < items) {
-          const int t = it / S, b = it - t * S;
-          const int row = m16_src_row<MODE>(a, is_sh, e, r_begin, t);
-          const u32x4_v* src =
-              reinterpret_cast<const u32x4_v*>(a.in_q + (size_t)row * a.ld_in + 32 * b);
-          v[i][0] = ld_global(src);
-          v[i][1] = ld_global(src + 1);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kM16StageIt; ++i) {
-        const int it = base + i * nth + tid;
-        if (it < items) {
-          const int t = it / S, b = it - t * S;
-          uint64_t* dst = reinterpret_cast<uint64_t*>(xs + t * xstride + 32 * b);
-          dst[0] = m16_order_a8<BITS>(v[i][0].x, v[i][0].y);
-          dst[1] = m16_order_a8<BITS>(v[i][0].z, v[i][0].w);
-          dst[2] = m16_order_a8<BITS>(v[i][1].x, v[i][1].y);
-          dst[3] = m16_order_a8<BITS>(v[i][1].z, v[i][1].w);
-        }
+        for (int c = 0; c < 4; ++c) x.v[i][c] = ld_global(src + c);
+      } else {
+        const u32x4_v* src =
+            reinterpret_cast<const u32x4_v*>(a.in_q + (size_t)srow[i] * a.ld_in + 32 * b);
+        x.v[i][0] = ld_global(src);
+        x.v[i][1] = ld_global(src + 1);
       }
     }
   }
-  if (ACT == MOE_A8 && tid < kM16MaxRows)
-    xsc[tid] = tid < nt ? ld_global(a.in_s + m16_src_row<MODE>(a, is_sh, e, r_begin, tid)) : 0.0f;
+}
+
+template <int ACT, int BITS>
+__device__ __forceinline__ void m16_x_store(int base, int items, int S, const M16XRegs<ACT>& x,
+                                            unsigned char* xs, int xstride, float* bsum, int Sl) {
+#pragma unroll
+  for (int i = 0; i < kM16StageIt; ++i) {
+    const int it = base + i * kM16Threads + threadIdx.x;
+    if (it < items) {
+      const int t = it / S, b = it - t * S;
+      if (ACT == MOE_A16) {
+        u32x4_v* dst = reinterpret_cast<u32x4_v*>(xs + t * xstride + 64 * b);
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4_v d = x.v[i][c];
+          dst[c] = m16_order_a16(d);
+          sum += bf16_to_f32(d.x & 0xFFFFu) + bf16_to_f32(d.x >> 16);
+          sum += bf16_to_f32(d.y & 0xFFFFu) + bf16_to_f32(d.y >> 16);
+          sum += bf16_to_f32(d.z & 0xFFFFu) + bf16_to_f32(d.z >> 16);
+          sum += bf16_to_f32(d.w & 0xFFFFu) + bf16_to_f32(d.w >> 16);
+        }
+        bsum[t * Sl + b] = sum;
+      } else {
+        uint64_t* dst = reinterpret_cast<uint64_t*>(xs + t * xstride + 32 * b);
+        dst[0] = m16_order_a8<BITS>(x.v[i][0].x, x.v[i][0].y);
+        dst[1] = m16_order_a8<BITS>(x.v[i][0].z, x.v[i][0].w);
+        dst[2] = m16_order_a8<BITS>(x.v[i][1].x, x.v[i][1].y);
+        dst[3] = m16_order_a8<BITS>(x.v[i][1].z, x.v[i][1].w);
+      }
+    }
+  }
 }
 
 // Rows of the down matrix or gate/up rows a workgroup covers.
@@ -221,12 +236,14 @@ __device__ __forceinline__ float m16_scale(const uint16_t* ssc, int lrow, int ng
 template <int MODE, int ACT, int BITS, bool WIDE>
 __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, bool is_sh, int e,
                                          int r_begin, int nt, int U, int K, int u0, int mt,
-                                         unsigned char* smem) {
+                                         const int (&srow)[kM16StageIt], unsigned char* smem) {
   using Sh = M16Shape<MODE>;
   constexpr int NT = Sh::NT;
   // ring depth in loads per N-tile: WIDE loads cover 4 steps (64 bytes of a
-  // row), the others one step
-  constexpr int R = WIDE ? (MODE == 0 ? 8 : 4) : Sh::R;
+  // row), the others one step.  Shallow on purpose: with every resident
+  // wave streaming, deeper rings measured slower (more scattered requests
+  // outstanding per CU, not more bandwidth).
+  constexpr int R = WIDE ? (MODE == 0 ? 4 : 2) : Sh::R;
   constexpr int SPL = WIDE ? 4 : 1;                      // steps per load
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, qd = lane >> 4;
@@ -247,7 +264,29 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
   uint16_t* ssc = reinterpret_cast<uint16_t*>(
       aux + (ACT == MOE_A16 ? 32 * Sl : kM16MaxRows));   // [blocks * block rows][ng]
 
-  // ---- this wave's weight rows and the ring of code loads
+  // ---- first batch of the activations, then the scales, then the ring
+  const int items = nt * S;
+  M16XRegs<ACT> xr;
+  m16_x_load<ACT>(a, 0, items, S, srow, xr);
+
+  // the rows' scales: one contiguous block per row block (gate, up / down)
+  constexpr int kBR = M16Rows<MODE>::kBlock;
+  const int nr = min(kBR, U - u0);                        // rows of each block
+  const int ndw = nr * ng / 2;                            // dwords per block (nr is even)
+  constexpr int kSclIt = 8;
+  const uint32_t* s0 = reinterpret_cast<const uint32_t*>(q.scales + (size_t)u0 * ng);
+  const uint32_t* s1 = reinterpret_cast<const uint32_t*>(q.scales + (size_t)(U + u0) * ng);
+  uint32_t* d32 = reinterpret_cast<uint32_t*>(ssc);
+  const int blk_dw = kBR * ng / 2;
+  const int tot = ndw * M16Rows<MODE>::kBlocks;
+  uint32_t sv[kSclIt];
+#pragma unroll
+  for (int i = 0; i < kSclIt; ++i) {
+    const int idx = i * kM16Threads + tid;
+    if (idx < tot) sv[i] = ld_global(idx < ndw ? s0 + idx : s1 + (idx - ndw));
+  }
+
+  // this wave's weight rows and the ring of code loads
   const int nrows = MODE == 0 ? 2 * U : U;
   const __amdgpu_buffer_rsrc_t crs = m16_rsrc(q.codes, (uint32_t)((size_t)nrows * row_bytes));
   int coff[NT], lrow[NT];
@@ -276,25 +315,8 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
 #pragma unroll
   for (int r = 0; r < R; ++r) load(min(r, L - 1), r);
 
-  // ---- the rows' scales (one contiguous block of scales per row block)
-  constexpr int kBR = M16Rows<MODE>::kBlock;
-  const int nr = min(kBR, U - u0);                        // rows of each block
-  const int ndw = nr * ng / 2;                            // dwords per block (nr is even)
-  constexpr int kSclIt = 8;
-  const uint32_t* s0 = reinterpret_cast<const uint32_t*>(q.scales + (size_t)u0 * ng);
-  const uint32_t* s1 = reinterpret_cast<const uint32_t*>(q.scales + (size_t)(U + u0) * ng);
-  uint32_t* d32 = reinterpret_cast<uint32_t*>(ssc);
-  const int blk_dw = kBR * ng / 2;
-  const int tot = ndw * M16Rows<MODE>::kBlocks;
-  uint32_t sv[kSclIt];
-#pragma unroll
-  for (int i = 0; i < kSclIt; ++i) {
-    const int idx = i * kM16Threads + tid;
-    if (idx < tot) sv[i] = ld_global(idx < ndw ? s0 + idx : s1 + (idx - ndw));
-  }
-
-  // ---- activations of the tile (in flight together with the ring)
-  m16_stage_x<MODE, ACT, BITS>(a, is_sh, e, r_begin, nt, S, xs, xstride, bsum, xsc, Sl);
+  // ---- LDS stores (the ring stays in flight), further batches if any
+  m16_x_store<ACT, BITS>(0, items, S, xr, xs, xstride, bsum, Sl);
 #pragma unroll
   for (int i = 0; i < kSclIt; ++i) {
     const int idx = i * kM16Threads + tid;
@@ -302,6 +324,18 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
   }
   for (int idx = kSclIt * kM16Threads + tid; idx < tot; idx += kM16Threads)
     d32[idx < ndw ? idx : blk_dw + (idx - ndw)] = ld_global(idx < ndw ? s0 + idx : s1 + (idx - ndw));
+  for (int base = kM16Threads * kM16StageIt; base < items; base += kM16Threads * kM16StageIt) {
+    int rows[kM16StageIt];
+#pragma unroll
+    for (int i = 0; i < kM16StageIt; ++i) {
+      const int it = base + i * kM16Threads + tid;
+      rows[i] = it < items ? m16_src_row<MODE>(a, is_sh, e, r_begin, it / S) : 0;
+    }
+    m16_x_load<ACT>(a, base, items, S, rows, xr);
+    m16_x_store<ACT, BITS>(base, items, S, xr, xs, xstride, bsum, Sl);
+  }
+  if (ACT == MOE_A8 && tid < kM16MaxRows)
+    xsc[tid] = tid < nt ? ld_global(a.in_s + m16_src_row<MODE>(a, is_sh, e, r_begin, tid)) : 0.0f;
   __syncthreads();
   if (ACT == MOE_A16) {   // per-group sums of the staged rows
     const int bpg = 1 << lbpg;
@@ -440,10 +474,14 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
 template <int MODE, int ACT>
 __global__ __launch_bounds__(kM16Threads) void proj_m16_kernel(ProjArgs a, int mt, int nblk) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int n_slots = a.n_sh_slots + *a.n_tiles;
   const int slot = blockIdx.x / nblk;
   const int blk = blockIdx.x - slot * nblk;
-  if (slot >= n_slots) return;
+  // the tile entry is read together with the tile count (slot - shared
+  // slots < max_tiles for every block of the grid)
+  int4 tl = reinterpret_cast<const int4*>(a.tiles)[max(slot - a.n_sh_slots, 0)];
+  int n_tiles = *a.n_tiles;
+  __asm__ volatile("" : "+s"(tl.x), "+s"(tl.y), "+s"(tl.z), "+s"(n_tiles));
+  if (slot >= a.n_sh_slots + n_tiles) return;
   bool is_sh;
   int e, r_begin, r_end, U, K;
   if (slot < a.n_sh_slots) {
@@ -456,7 +494,6 @@ __global__ __launch_bounds__(kM16Threads) void proj_m16_kernel(ProjArgs a, int m
     U = a.U_sh;
     K = a.K_sh;
   } else {
-    const int4 tl = reinterpret_cast<const int4*>(a.tiles)[slot - a.n_sh_slots];
     is_sh = false;
     e = tl.x;
     r_begin = tl.y;
@@ -471,17 +508,28 @@ __global__ __launch_bounds__(kM16Threads) void proj_m16_kernel(ProjArgs a, int m
     if (threadIdx.x == 0) atomicOr(a.err, 2);
     return;
   }
-  const moe_qmat q = is_sh ? a.w_sh[e] : a.w[e];
+  // the 32-byte descriptor (two 16-byte loads) and the pair numbers of the
+  // first staged rows are in flight together
+  const u32x4_v* dp = reinterpret_cast<const u32x4_v*>(is_sh ? a.w_sh + e : a.w + e);
+  u32x4_v d0 = ld_global(dp), d1 = ld_global(dp + 1);
+  int srow[kM16StageIt], trow[kM16StageIt];   // activation rows of the first staging batch
+  m16_row_loads<MODE>(a, r_begin, nt, K >> 5, srow, trow);
+  __asm__ volatile("" : "+v"(d0), "+v"(d1));
+  m16_row_finish<MODE>(a, is_sh, e, r_begin, srow, trow);
+  struct {
+    u32x4_v lo, hi;
+  } raw = {d0, d1};
+  const moe_qmat q = __builtin_bit_cast(moe_qmat, raw);
   if (!qmat_usable(q, MODE == 0 ? 2 * U : U, K)) {
     if (threadIdx.x == 0) atomicOr(a.err, 1);
     return;
   }
   if (q.bits == 4 && q.group >= 128)
-    m16_tile<MODE, ACT, 4, true>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, smem);
+    m16_tile<MODE, ACT, 4, true>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
   else if (q.bits == 4)
-    m16_tile<MODE, ACT, 4, false>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, smem);
+    m16_tile<MODE, ACT, 4, false>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
   else
-    m16_tile<MODE, ACT, 2, false>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, smem);
+    m16_tile<MODE, ACT, 2, false>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
 }
 
 int m16_rows(int T) { return T < kM16MaxRows ? T : kM16MaxRows; }

@@ -1,5 +1,5 @@
-// Top-k routing of one token by one wave, shared by the routing kernels
-// and the fused decode kernel.
+// Top-k routing of a token by a group of lanes (a whole wave, or one row of
+// 16 lanes), shared by the routing kernels and the fused decode kernel.
 #pragma once
 
 #include "moe_internal.h"
@@ -7,71 +7,174 @@
 namespace moe {
 
 // ---------------------------------------------------------------------
-// Top-k of one token's logits by one wave.  Lane l holds logits l, l+64,
-// ...; each of k rounds takes the lane-local best not yet chosen and a
-// DPP wave arg-max with the order (value descending, index ascending).
-// Gate weights: exp(l_j - l_max) over their sum (softmax over the chosen
-// logits) or over all E logits (renormalize = 0).  The r-th choice (r < k)
-// goes to ids_out[r] / w_out[r] (global, skipped when null) and to
+// Top-k of one token's logits by LANES lanes (64: a wave; 16: a row of the
+// wave, four tokens per wave).  Lane r of the group holds logits r,
+// r + LANES, ...; each of k rounds takes the lane-local best not yet chosen
+// and an arg-max across the group with the order (value descending, index
+// ascending).  The order is carried by one 64-bit key per candidate: the
+// value mapped monotonically to 32 bits (-0 taken as +0) above the inverted
+// index, so one unsigned compare decides, and taken or absent candidates
+// have key 0.  Gate weights: exp(l_j - l_max) over their sum in selection
+// order (softmax over the chosen logits), or over all E logits
+// (renormalize = 0; per-lane sums added across the group).  The r-th choice
+// (r < k) goes to ids_out[r] / w_out[r] (global, skipped when null) and to
 // lds_ids[r] / lds_w[r] (skipped when null).
-template <int NV>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E,
-                                            int k, int renorm, int lane,
-                                            int32_t* __restrict__ ids_out,
-                                            float* __restrict__ w_out,
-                                            int32_t* lds_ids, float* lds_w = nullptr) {
-  float v[NV];
+__device__ __forceinline__ uint32_t route_ord(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float route_unord(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void key_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t ohi = (uint32_t)dpp_i<CTRL, ROW_MASK>((int)hi, (int)hi);
+  const uint32_t olo = (uint32_t)dpp_i<CTRL, ROW_MASK>((int)lo, (int)lo);
+  const uint64_t a = ((uint64_t)hi << 32) | lo, b = ((uint64_t)ohi << 32) | olo;
+  if (b > a) {
+    hi = ohi;
+    lo = olo;
+  }
+}
+
+template <int LANES, int NVV>
+__device__ __forceinline__ void route_group_load(const float* __restrict__ row, int E, int r,
+                                                 float (&v)[NVV]) {
+#pragma unroll
+  for (int j = 0; j < NVV; ++j) {
+    const int e = r + LANES * j;
+    v[j] = e < E ? row[e] : -INFINITY;
+  }
+}
+
+template <int LANES, int NVV>
+__device__ __forceinline__ void route_group_vals(const float (&v)[NVV], int E, int k,
+                                                 int renorm, int r, bool write,
+                                                 int32_t* __restrict__ ids_out,
+                                                 float* __restrict__ w_out, int32_t* lds_ids,
+                                                 float* lds_w) {
+  uint32_t key_hi[NVV];
   uint32_t taken = 0;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < E ? row[e] : -INFINITY;
-    if (e >= E) taken |= 1u << j;
+  for (int j = 0; j < NVV; ++j) {
+    key_hi[j] = route_ord(v[j]);
+    if (r + LANES * j >= E) taken |= 1u << j;
   }
   float top = 0.0f, denom = 0.0f;
-  float sel_ex[NV];
-  int sel_id[NV];
+  float sel_ex[NVV];
+  int sel_id[NVV];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) { sel_ex[j] = 0.0f; sel_id[j] = 0; }
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  for (int j = 0; j < NVV; ++j) { sel_ex[j] = 0.0f; sel_id[j] = 0; }
+  for (int rr = 0; rr < k; ++rr) {
+    uint32_t hi = 0, lo = 0;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int e = lane + 64 * j;
+    for (int j = 0; j < NVV; ++j) {
       const bool free_j = !((taken >> j) & 1u);
-      if (free_j && beats(v[j], e, bv, bi)) {
-        bv = v[j];
-        bi = e;
+      const uint32_t chi = free_j ? key_hi[j] : 0u;
+      const uint32_t clo = free_j ? ~(uint32_t)(r + LANES * j) : 0u;
+      const uint64_t a = ((uint64_t)hi << 32) | lo, b = ((uint64_t)chi << 32) | clo;
+      if (b > a) {
+        hi = chi;
+        lo = clo;
       }
     }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (r == 0) top = bv;
+    key_max_step<kDppXor1>(hi, lo);
+    key_max_step<kDppXor2>(hi, lo);
+    key_max_step<kDppRowHalfMirror>(hi, lo);
+    key_max_step<kDppRowMirror>(hi, lo);
+    if (LANES == 64) {
+      key_max_step<kDppRowBcast15, 0xA>(hi, lo);
+      key_max_step<kDppRowBcast31, 0xC>(hi, lo);
+      hi = __builtin_amdgcn_readlane(hi, 63);
+      lo = __builtin_amdgcn_readlane(lo, 63);
+    }
+    const int bi = (int)~lo;
+    const float bv = route_unord(hi);
+    if (bi % LANES == r) taken |= 1u << (bi / LANES);
+    if (rr == 0) top = bv;
     const float ex = expf(bv - top);
     denom += ex;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      if (r == lane + 64 * j) { sel_ex[j] = ex; sel_id[j] = bi; }
+    for (int j = 0; j < NVV; ++j)
+      if (rr == r + LANES * j) { sel_ex[j] = ex; sel_id[j] = bi; }
   }
   if (!renorm) {
-    float s = 0.0f;
+    float sm = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      if (lane + 64 * j < E) s += expf(v[j] - top);
-    denom = wave_sum(s);
+    for (int j = 0; j < NVV; ++j)
+      if (r + LANES * j < E) sm += expf(v[j] - top);
+    denom = LANES == 64 ? wave_sum(sm) : group_sum(sm, 16);
   }
+  if (!write) return;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int r = lane + 64 * j;
-    if (r < k) {
+  for (int j = 0; j < NVV; ++j) {
+    const int rr = r + LANES * j;
+    if (rr < k) {
       const float wr = sel_ex[j] / denom;
       if (ids_out) {
-        ids_out[r] = sel_id[j];
-        w_out[r] = wr;
+        ids_out[rr] = sel_id[j];
+        w_out[rr] = wr;
       }
-      if (lds_ids) lds_ids[r] = sel_id[j];
-      if (lds_w) lds_w[r] = wr;
+      if (lds_ids) lds_ids[rr] = sel_id[j];
+      if (lds_w) lds_w[rr] = wr;
+    }
+  }
+}
+
+// Batches of at least this many tokens route one token per row of 16 lanes
+// (when E <= 256): four tokens per wave at once, for throughput; smaller
+// batches one token per wave, for latency.  Every routing kernel applies
+// the same rule, so their results agree bit for bit.
+constexpr int kRouteRowMinT = 16;
+
+// Route tokens [0, T) with the waves w0, w0 + ws, ... of the caller (w0 =
+// this wave's index among the ws routing waves).  Each wave handles up to
+// 4 * MAXPER tokens; all its loads are issued before its first top-k.
+template <int NV, int MAXPER>
+__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, int T, int E,
+                                             int k, int renorm, int lane, int w0, int ws,
+                                             int32_t* ids, float* w, int32_t* lds_ids,
+                                             float* lds_w) {
+  if (NV <= 4 && T >= kRouteRowMinT) {
+    constexpr int NVL = NV <= 4 ? 4 * NV : 1;
+    const int r = lane & 15, sub = lane >> 4;
+    float v[MAXPER][NVL];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      const int t = min((w0 + ws * i) * 4 + sub, T - 1);
+      if ((w0 + ws * i) * 4 < T) route_group_load<16, NVL>(logits + (size_t)t * E, E, r, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      const int t0 = (w0 + ws * i) * 4;
+      if (t0 < T) {
+        const int t = t0 + sub;
+        const bool ok = t < T;
+        const int tt = ok ? t : T - 1;
+        route_group_vals<16, NVL>(v[i], E, k, renorm, r, ok,
+                                  ids ? ids + (size_t)tt * k : nullptr,
+                                  w ? w + (size_t)tt * k : nullptr,
+                                  lds_ids ? lds_ids + tt * k : nullptr,
+                                  lds_w ? lds_w + tt * k : nullptr);
+      }
+    }
+  } else {
+    float v[MAXPER * 4][NV];
+#pragma unroll
+    for (int i = 0; i < MAXPER * 4; ++i) {
+      const int t = w0 + ws * i;
+      if (t < T) route_group_load<64, NV>(logits + (size_t)t * E, E, lane, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < MAXPER * 4; ++i) {
+      const int t = w0 + ws * i;
+      if (t < T)
+        route_group_vals<64, NV>(v[i], E, k, renorm, lane, true,
+                                 ids ? ids + (size_t)t * k : nullptr,
+                                 w ? w + (size_t)t * k : nullptr,
+                                 lds_ids ? lds_ids + t * k : nullptr,
+                                 lds_w ? lds_w + t * k : nullptr);
     }
   }
 }

@@ -15,11 +15,11 @@ template <int NV>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm,
     int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  route_token<NV>(logits + (size_t)t * E, E, k, renorm, lane, ids + (size_t)t * k,
-                  w + (size_t)t * k, nullptr);
+  // 16 tokens per workgroup: four per wave (one per row of 16 lanes, or
+  // one after another for E > 256)
+  route_tokens<NV, 1>(logits, T, E, k, renorm, threadIdx.x & 63,
+                      blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4, ids, w, nullptr,
+                      nullptr);
 }
 
 // ---------------------------------------------------------------------
@@ -164,10 +164,9 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(
     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
   __shared__ PermSmem sm;
   __shared__ int32_t lds_ids[kFusedRouteMaxP];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int t = wave; t < T; t += kPermWaves)
-    route_token<NV>(logits + (size_t)t * E, E, k, renorm, lane, ids + (size_t)t * k,
-                    w + (size_t)t * k, lds_ids + t * k);
+  static_assert(kFusedRouteMaxT == 4 * kPermWaves, "one token per row of 16 lanes");
+  route_tokens<NV, 1>(logits, T, E, k, renorm, threadIdx.x & 63, threadIdx.x >> 6, kPermWaves,
+                      ids, w, lds_ids, nullptr);
   __syncthreads();
   permute_body(lds_ids, T * k, E, tile_m, counts, offsets, sorted_pair, pair_pos,
                tiles, n_tiles, sm);
@@ -187,7 +186,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k,
                              int renorm, int32_t* ids, float* w,
                              hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((T + 3) / 4), block(256);
+  const dim3 grid((T + 15) / 16), block(256);
   MOE_NV_DISPATCH(NV, route_topk_kernel<NV><<<grid, block, 0, st>>>(
                           logits, T, E, k, renorm, ids, w));
   return hipGetLastError();
