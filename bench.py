@@ -158,8 +158,14 @@ def main():
 
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
 
+    # bf16 decode batches of at most 64 pairs route, sort and run gate/up in
+    # one launch (the library's rule for moe_w4_route_gateup_silu); other
+    # shapes time the gate/up call alone (A8: with its int8 x quantizer)
+    fused = (decode and act == "a16" and cfg.T * cfg.k <= 64 and cfg.E <= 512
+             and B.tile_m <= 16 and cfg.H <= 2048)
+
     def gateup(bk):
-        if decode:   # the call run_layer makes: one launch for decode batches
+        if fused:
             L.moe_w4_route_gateup_silu(B.act, dl.logits, dl.x, T, H, I, E, k,
                                        cfg.renormalize, bk.w13, bk.w13_sh, cfg.n_shared,
                                        cfg.I_shared, B.tile_m, B.ids, B.w, B.counts,
@@ -215,8 +221,13 @@ def main():
     # launches over distinct bank copies, timed with events on the stream
     # the graph runs on
     n_k = min(len(banks), 32) if decode else 4
-    kname = ("dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)" if decode
-             else "proj_mfma_kernel<0> + convert_x_kernel (gate/up + SiLU*mul)")
+    if fused:
+        kname = "dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)"
+    elif decode:
+        kname = ("proj_m16_kernel<0> (gate/up + SiLU*mul)" if act == "a16" else
+                 "quant_rows_kernel + proj_m16_kernel<0> (int8 x, gate/up + SiLU*mul)")
+    else:
+        kname = "proj_mfma_kernel<0> + convert_x_kernel (gate/up + SiLU*mul)"
     gk = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gk):
         for i in range(n_k):
@@ -232,7 +243,8 @@ def main():
         ach = bytes_w13 / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS,
-                "traffic": measured_traffic(f"dec_route_gateup_kernel@{cfg.name}"),
+                "traffic": measured_traffic(("dec_route_gateup_kernel@" if fused else
+                                             "gateup_call@") + cfg.name),
                 "kernel": kname,
                 "algorithmic_bytes": bytes_w13}
     else:

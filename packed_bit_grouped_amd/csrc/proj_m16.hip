@@ -13,12 +13,14 @@
 // out of bytes.  Here the tile's rows are the M side of a 16x16 MFMA:
 //
 //  * lane l feeds token row l%16 of A and weight row l%16 of B, each with
-//    the 8-wide K slice l/16 of a 32-K step.  Per lane, N-tile and step one
-//    32-bit code word (int4) or 16-bit half word (int2) and the row's fp16
-//    scale of that step's group are loaded with buffer loads (the step
-//    offset is a scalar) into a ring of R steps.  Every load is issued
-//    unconditionally (steps past the end re-read the last one), so the
-//    compiler's wait counts stay graded.
+//    the 8-wide K slice l/16 of a 32-K step.  Codes come with buffer loads
+//    (the step offset is a scalar) into a ring of loads: for int4 with scale
+//    groups of 128 or more, 16 bytes of the lane's row per 4 steps (MFMA m
+//    of the 4 takes dword m, so the four lane slices of one MFMA span 128 K
+//    of one group) with the workgroup's row scales copied to LDS once;
+//    otherwise one 32-bit (int4) or 16-bit (int2) word and the row's scale
+//    per step.  Every load is issued unconditionally (steps past the end
+//    re-read the last one), so the compiler's wait counts stay graded.
 //  * Codes expand in registers to exact integers: bf16 136 + v (int4) or
 //    130 + v (int2), the bias removed per scale group with the staged sum
 //    of the tile's activations over that group; or int8 16 v / 64 v, whose
