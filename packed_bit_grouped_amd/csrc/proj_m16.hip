@@ -518,9 +518,17 @@ __global__ __launch_bounds__(kM16Threads) void proj_m16_kernel(ProjArgs a, int m
   m16_row_loads<MODE>(a, r_begin, nt, K >> 5, srow, trow);
   __asm__ volatile("" : "+v"(d0), "+v"(d1));
   m16_row_finish<MODE>(a, is_sh, e, r_begin, srow, trow);
+  // the descriptor is the same for the whole workgroup: scalar registers,
+  // so the buffer resources built from it need no per-lane loop
+  u32x4_v lo, hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)d0[i]);
+    hi[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)d1[i]);
+  }
   struct {
     u32x4_v lo, hi;
-  } raw = {d0, d1};
+  } raw = {lo, hi};
   const moe_qmat q = __builtin_bit_cast(moe_qmat, raw);
   if (!qmat_usable(q, MODE == 0 ? 2 * U : U, K)) {
     if (threadIdx.x == 0) atomicOr(a.err, 1);
