@@ -299,22 +299,21 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
     uint16_t* x16 = reinterpret_cast<uint16_t*>(ws + L.a16);
     return from_hip(launch_proj_mfma(a, x16, x16 + (size_t)T * H, s));
   }
-  if (act == MOE_A8) {
+  const bool dec = act == MOE_A16 && !partials && dec_gateup_ok(T, H, tile_m);
+  const bool on_m16 = path == MOE_PATH_MFMA16 ||
+                      (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs));
+  a.in_bf16 = x;
+  if (act == MOE_A8 && !(on_m16 && m16_quant_ok(0, T, H, H))) {
+    // int8 x rows for the kernels that read them (the 16-row matrix tiles
+    // quantize their staged rows themselves when a tile's rows fit)
     int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
     float* sx = reinterpret_cast<float*>(ws + L.sx);
     hipError_t e = launch_quant_a8(x, 0, T, H, H, qx, H, sx, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     a.in_q = qx;
     a.in_s = sx;
-  } else {
-    a.in_bf16 = x;
   }
-  const bool dec = act == MOE_A16 && !partials && dec_gateup_ok(T, H, tile_m);
-  if (path == MOE_PATH_MFMA16 ||
-      (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs))) {
-    if (act == MOE_A8) a.ld_in = H;
-    return from_hip(launch_proj_m16(a, act, s));
-  }
+  if (on_m16) return from_hip(launch_proj_m16(a, act, s));
   a.maxt = gemv_maxt(T, tile_m);
   a.sh_tile = a.maxt;
   a.n_sh_slots = n_shared * ((T + a.sh_tile - 1) / a.sh_tile);
@@ -398,7 +397,8 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
                    dec_down_ok(T, k, E, n_shared, H, I, I_shared, ld_h, tile_m, a.max_tiles);
   if (path == MOE_PATH_MFMA16 ||
       (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs))) {
-    if (act == MOE_A8) {   // int8 h rows for the int8 MFMA
+    if (act == MOE_A8 && !m16_quant_ok(1, T, I, n_shared > 0 ? I_shared : I)) {
+      // int8 h rows for the int8 MFMA (made in the kernel when a tile's rows fit)
       int8_t* qh = reinterpret_cast<int8_t*>(ws + L.qh);
       float* sh = reinterpret_cast<float*>(ws + L.sh);
       const int P = T * k;

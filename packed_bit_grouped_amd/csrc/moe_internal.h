@@ -104,6 +104,9 @@ hipError_t launch_dec_route_gateup(const ProjArgs& a, const float* logits, int r
 // int8 rows (a.in_q, stride a.ld_in) with fp32 row scales (a.in_s): x for
 // gate/up, the quantized h rows for down.
 bool m16_ok(int act, int mode, int T, int K, int K_sh, int tile_m);
+// A8: the kernel makes the int8 rows of a tile itself (from bf16 x or fp32
+// h, a.in_q null) when they fit one staging batch.
+bool m16_quant_ok(int mode, int T, int K, int K_sh);
 hipError_t launch_proj_m16(const ProjArgs& a, int act, hipStream_t st);
 hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
                           const int32_t* pair_pos, int T, int k, int H, int P,

@@ -223,6 +223,83 @@ __device__ __forceinline__ void m16_x_store(int base, int items, int S, const M1
   }
 }
 
+// W4A8 with the int8 rows made here (the row quantizer's rule, a8_scale /
+// a8_code, over each staged row): items of the first batch only (the host
+// checks that every item fits it).  Gate/up reads bf16 x, down fp32 h.
+template <int MODE>
+struct M16QRegs {
+  static constexpr int kIt = MODE == 0 ? kM16StageIt : kM16StageIt / 2;   // items per thread
+  static constexpr int kVec = MODE == 0 ? 4 : 8;                          // 16-byte words per item
+  u32x4_v v[kIt][kVec];
+};
+
+template <int MODE>
+__device__ __forceinline__ void m16_q_load(const ProjArgs& a, int items, int S,
+                                           const int (&srow)[kM16StageIt], M16QRegs<MODE>& x) {
+#pragma unroll
+  for (int i = 0; i < M16QRegs<MODE>::kIt; ++i) {
+    const int it = i * kM16Threads + threadIdx.x;
+    if (it < items) {
+      const int b = it - (it / S) * S;
+      const u32x4_v* src =
+          MODE == 0 ? reinterpret_cast<const u32x4_v*>(a.in_bf16 + (size_t)srow[i] * a.ld_in + 32 * b)
+                    : reinterpret_cast<const u32x4_v*>(a.in_f32 + (size_t)srow[i] * a.ld_in + 32 * b);
+#pragma unroll
+      for (int c = 0; c < M16QRegs<MODE>::kVec; ++c) x.v[i][c] = ld_global(src + c);
+    }
+  }
+}
+
+// value j (0..31) of an item
+template <int MODE>
+__device__ __forceinline__ float m16_q_val(const u32x4_v (&v)[M16QRegs<MODE>::kVec], int j) {
+  if (MODE == 0) {
+    const uint32_t w = v[j >> 3][(j >> 1) & 3];
+    return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+  return __uint_as_float(v[j >> 2][j & 3]);
+}
+
+// row maxima of |v| into rmax (unsigned bits of non-negative floats)
+template <int MODE>
+__device__ __forceinline__ void m16_q_amax(int items, int S, const M16QRegs<MODE>& x,
+                                           uint32_t* rmax) {
+#pragma unroll
+  for (int i = 0; i < M16QRegs<MODE>::kIt; ++i) {
+    const int it = i * kM16Threads + threadIdx.x;
+    if (it < items) {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) m = fmaxf(m, fabsf(m16_q_val<MODE>(x.v[i], j)));
+      atomicMax(rmax + it / S, __float_as_uint(m));
+    }
+  }
+}
+
+template <int MODE, int BITS>
+__device__ __forceinline__ void m16_q_store(int items, int S, const M16QRegs<MODE>& x,
+                                            const uint32_t* rmax, unsigned char* xs, int xstride) {
+#pragma unroll
+  for (int i = 0; i < M16QRegs<MODE>::kIt; ++i) {
+    const int it = i * kM16Threads + threadIdx.x;
+    if (it < items) {
+      const int t = it / S, b = it - t * S;
+      const float sc = a8_scale(__uint_as_float(rmax[t]));
+      uint64_t* dst = reinterpret_cast<uint64_t*>(xs + t * xstride + 32 * b);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {     // 8-K slices
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lo |= ((uint32_t)a8_code(m16_q_val<MODE>(x.v[i], 8 * sl + j), sc) & 0xFFu) << (8 * j);
+          hi |= ((uint32_t)a8_code(m16_q_val<MODE>(x.v[i], 8 * sl + 4 + j), sc) & 0xFFu) << (8 * j);
+        }
+        dst[sl] = m16_order_a8<BITS>(lo, hi);
+      }
+    }
+  }
+}
+
 // Rows of the down matrix or gate/up rows a workgroup covers.
 template <int MODE>
 struct M16Rows {
@@ -235,7 +312,7 @@ __device__ __forceinline__ float m16_scale(const uint16_t* ssc, int lrow, int ng
   return fp16_to_f32(ssc[lrow * ng + g]);
 }
 
-template <int MODE, int ACT, int BITS, bool WIDE>
+template <int MODE, int ACT, int BITS, bool WIDE, bool QX>
 __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, bool is_sh, int e,
                                          int r_begin, int nt, int U, int K, int u0, int mt,
                                          const int (&srow)[kM16StageIt], unsigned char* smem) {
@@ -263,13 +340,20 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
   float* bsum = aux;                   // A16: [16][Sl]
   float* xsum = aux + 16 * Sl;         // A16: [Sl][16]
   float* xsc = aux;                    // A8: [16]
+  uint32_t* rmax = reinterpret_cast<uint32_t*>(aux + kM16MaxRows);   // A8, QX: [16]
   uint16_t* ssc = reinterpret_cast<uint16_t*>(
-      aux + (ACT == MOE_A16 ? 32 * Sl : kM16MaxRows));   // [blocks * block rows][ng]
+      aux + (ACT == MOE_A16 ? 32 * Sl : 2 * kM16MaxRows));   // [blocks * block rows][ng]
 
   // ---- first batch of the activations, then the scales, then the ring
   const int items = nt * S;
   M16XRegs<ACT> xr;
-  m16_x_load<ACT>(a, 0, items, S, srow, xr);
+  M16QRegs<MODE> xq;
+  if constexpr (QX) {
+    if (tid < kM16MaxRows) rmax[tid] = 0u;
+    m16_q_load<MODE>(a, items, S, srow, xq);
+  } else {
+    m16_x_load<ACT>(a, 0, items, S, srow, xr);
+  }
 
   // the rows' scales: one contiguous block per row block (gate, up / down)
   constexpr int kBR = M16Rows<MODE>::kBlock;
@@ -318,7 +402,15 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
   for (int r = 0; r < R; ++r) load(min(r, L - 1), r);
 
   // ---- LDS stores (the ring stays in flight), further batches if any
-  m16_x_store<ACT, BITS>(0, items, S, xr, xs, xstride, bsum, Sl);
+  if constexpr (QX) {
+    __syncthreads();                     // row maxima cleared
+    m16_q_amax<MODE>(items, S, xq, rmax);
+    __syncthreads();
+    m16_q_store<MODE, BITS>(items, S, xq, rmax, xs, xstride);
+    if (tid < kM16MaxRows) xsc[tid] = a8_scale(__uint_as_float(rmax[tid]));
+  } else {
+    m16_x_store<ACT, BITS>(0, items, S, xr, xs, xstride, bsum, Sl);
+  }
 #pragma unroll
   for (int i = 0; i < kSclIt; ++i) {
     const int idx = i * kM16Threads + tid;
@@ -326,7 +418,8 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
   }
   for (int idx = kSclIt * kM16Threads + tid; idx < tot; idx += kM16Threads)
     d32[idx < ndw ? idx : blk_dw + (idx - ndw)] = ld_global(idx < ndw ? s0 + idx : s1 + (idx - ndw));
-  for (int base = kM16Threads * kM16StageIt; base < items; base += kM16Threads * kM16StageIt) {
+  for (int base = kM16Threads * kM16StageIt; !QX && base < items;
+       base += kM16Threads * kM16StageIt) {
     int rows[kM16StageIt];
 #pragma unroll
     for (int i = 0; i < kM16StageIt; ++i) {
@@ -336,7 +429,7 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
     m16_x_load<ACT>(a, base, items, S, rows, xr);
     m16_x_store<ACT, BITS>(base, items, S, xr, xs, xstride, bsum, Sl);
   }
-  if (ACT == MOE_A8 && tid < kM16MaxRows)
+  if (ACT == MOE_A8 && !QX && tid < kM16MaxRows)
     xsc[tid] = tid < nt ? ld_global(a.in_s + m16_src_row<MODE>(a, is_sh, e, r_begin, tid)) : 0.0f;
   __syncthreads();
   if (ACT == MOE_A16) {   // per-group sums of the staged rows
@@ -473,7 +566,7 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
 
 // Grid: (shared slots + host bound of tiles) x blocks of units; blocks past
 // the device-side tile count or past an expert's units exit at once.
-template <int MODE, int ACT>
+template <int MODE, int ACT, bool QX>
 __global__ __launch_bounds__(kM16Threads) void proj_m16_kernel(ProjArgs a, int mt, int nblk) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int slot = blockIdx.x / nblk;
@@ -535,11 +628,11 @@ __global__ __launch_bounds__(kM16Threads) void proj_m16_kernel(ProjArgs a, int m
     return;
   }
   if (q.bits == 4 && q.group >= 128)
-    m16_tile<MODE, ACT, 4, true>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
+    m16_tile<MODE, ACT, 4, true, QX>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
   else if (q.bits == 4)
-    m16_tile<MODE, ACT, 4, false>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
+    m16_tile<MODE, ACT, 4, false, QX>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
   else
-    m16_tile<MODE, ACT, 2, false>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
+    m16_tile<MODE, ACT, 2, false, QX>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
 }
 
 int m16_rows(int T) { return T < kM16MaxRows ? T : kM16MaxRows; }
@@ -548,9 +641,18 @@ size_t m16_lds(int act, int mode, int T, int K, int K_sh) {
   const int Kl = K > K_sh ? K : K_sh;
   const size_t x = (size_t)m16_rows(T) * (act == MOE_A16 ? 2 * Kl + 16 : Kl + 8);
   const size_t aux = act == MOE_A16 ? (size_t)2 * kM16MaxRows * (Kl / 32) * 4
-                                    : (size_t)kM16MaxRows * 4;
+                                    : (size_t)2 * kM16MaxRows * 4;
   const size_t rows = mode == 0 ? 2 * M16Rows<0>::kBlock : M16Rows<1>::kBlock;
   return x + aux + rows * (Kl / 32) * 2;
+}
+
+bool m16_quant_ok(int mode, int T, int K, int K_sh) {
+  // down: every workgroup of a tile would quantize the same fp32 h rows
+  // (a division per element); the row quantizer launch measured faster
+  if (mode != 0) return false;
+  const int Kl = K > K_sh ? K : K_sh;
+  const int it = mode == 0 ? M16QRegs<0>::kIt : M16QRegs<1>::kIt;
+  return (long long)m16_rows(T) * (Kl / 32) <= (long long)kM16Threads * it;
 }
 
 bool m16_ok(int act, int mode, int T, int K, int K_sh, int tile_m) {
@@ -570,16 +672,18 @@ hipError_t launch_proj_m16(const ProjArgs& a_in, int act, hipStream_t st) {
   const int mt = m16_rows(a.T);
   const size_t lds = m16_lds(act, a.mode, a.T, a.K, a.K_sh);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
+  // A8 with int8 rows made in the kernel when a.in_q is null
+  const bool qx = act == MOE_A8 && a.in_q == nullptr;
+  if (qx && !m16_quant_ok(a.mode, a.T, a.K, a.K_sh)) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid), b(kM16Threads);
   if (a.mode == 0) {
-    if (act == MOE_A16)
-      proj_m16_kernel<0, MOE_A16><<<(int)grid, kM16Threads, lds, st>>>(a, mt, nblk);
-    else
-      proj_m16_kernel<0, MOE_A8><<<(int)grid, kM16Threads, lds, st>>>(a, mt, nblk);
+    if (act == MOE_A16) proj_m16_kernel<0, MOE_A16, false><<<g, b, lds, st>>>(a, mt, nblk);
+    else if (qx) proj_m16_kernel<0, MOE_A8, true><<<g, b, lds, st>>>(a, mt, nblk);
+    else proj_m16_kernel<0, MOE_A8, false><<<g, b, lds, st>>>(a, mt, nblk);
   } else {
-    if (act == MOE_A16)
-      proj_m16_kernel<1, MOE_A16><<<(int)grid, kM16Threads, lds, st>>>(a, mt, nblk);
-    else
-      proj_m16_kernel<1, MOE_A8><<<(int)grid, kM16Threads, lds, st>>>(a, mt, nblk);
+    if (act == MOE_A16) proj_m16_kernel<1, MOE_A16, false><<<g, b, lds, st>>>(a, mt, nblk);
+    else if (qx) proj_m16_kernel<1, MOE_A8, true><<<g, b, lds, st>>>(a, mt, nblk);
+    else proj_m16_kernel<1, MOE_A8, false><<<g, b, lds, st>>>(a, mt, nblk);
   }
   return hipGetLastError();
 }
