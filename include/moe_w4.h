@@ -143,11 +143,13 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E,
                        int32_t* tiles, int32_t* n_tiles, void* stream);
 
 /* ---------------------------------------------------------------------
- * moe_route_permute -- moe_route_topk followed by moe_permute in one launch
- * (one workgroup), for decode batches where the two steps are each a
- * handful of microseconds of launch and latency (pages: fused operators
- * where a decode step is many small launches).  Same outputs, bit for bit,
- * as the two calls.  Limits: T <= 64, T*k <= 4096, 1 <= E <= 512.
+ * moe_route_permute -- moe_route_topk followed by moe_permute, in one launch
+ * (one workgroup) for T < 16, where the two steps are each a handful of
+ * microseconds of launch and latency (pages: fused operators where a decode
+ * step is many small launches); from 16 tokens on the routing alone keeps a
+ * compute unit busy for longer than a launch costs, so it issues the two
+ * kernels.  Same outputs, bit for bit, as the two calls.  Limits: T <= 64,
+ * T*k <= 4096, 1 <= E <= 512.
  * ------------------------------------------------------------------- */
 moe_status moe_route_permute(const float* logits, int T, int E, int k,
                              int renormalize, int tile_m, int32_t* topk_ids,

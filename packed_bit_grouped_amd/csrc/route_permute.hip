@@ -207,6 +207,14 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k,
                                 int32_t* sorted_pair, int32_t* pair_pos,
                                 int32_t* tiles, int32_t* n_tiles,
                                 hipStream_t st) {
+  // from 16 tokens on the routing is worth more than one compute unit: the
+  // multi-workgroup router, then the sort (same functions, same results)
+  if (T >= kRouteRowMinT) {
+    const hipError_t e = launch_route_topk(logits, T, E, k, renorm, ids, w, st);
+    if (e != hipSuccess) return e;
+    return launch_permute(ids, T * k, E, tile_m, counts, offsets, sorted_pair, pair_pos, tiles,
+                          n_tiles, st);
+  }
   MOE_NV_DISPATCH(NV, route_permute_kernel<NV><<<1, 1024, 0, st>>>(
                           logits, T, E, k, renorm, tile_m, ids, w, counts,
                           offsets, sorted_pair, pair_pos, tiles, n_tiles));
