@@ -225,7 +225,7 @@ def main():
         kname = "dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)"
     elif decode:
         kname = ("proj_m16_kernel<0> (gate/up + SiLU*mul)" if act == "a16" else
-                 "quant_rows_kernel + proj_m16_kernel<0> (int8 x, gate/up + SiLU*mul)")
+                 "proj_m16_kernel<0> (int8 x rows made in the kernel, gate/up + SiLU*mul)")
     else:
         kname = "proj_mfma_kernel<0> + convert_x_kernel (gate/up + SiLU*mul)"
     gk = torch.cuda.CUDAGraph()
