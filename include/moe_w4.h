@@ -196,6 +196,10 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
                               /* tile's activations within 160 KB of LDS,     */
                               /* else MOE_E_UNSUPPORTED                       */
 #define MOE_PATH_MASK 3
+#define MOE_QUANT_SEPARATE 4  /* W4A8: quantize x with the row quantizer    */
+                              /* launch even where the gate/up kernel would */
+                              /* make the int8 rows itself (same codes; a   */
+                              /* check and a fallback)                      */
 
 /* Tile height to pass as moe_permute's tile_m: 128 (the MFMA path's row
  * block) when T*k >= 32*E with A16, else 16.  Both paths accept any

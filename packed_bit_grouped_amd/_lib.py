@@ -19,6 +19,7 @@ ABI_VERSION = 1
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_DEVICE, MOE_E_WORKSPACE = 0, -1, -2, -3, -4
 MOE_A16, MOE_A8 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA16 = 0, 1, 2, 3
+MOE_QUANT_SEPARATE = 4
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 

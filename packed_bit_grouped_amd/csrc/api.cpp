@@ -69,7 +69,7 @@ moe_status check_layer(int act, int T, int H, int I, int E, int k, int n_shared,
   if (k > E) return MOE_E_INVAL;
   if (n_shared > 0 && I_shared <= 0) return MOE_E_INVAL;
   if (tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
-  if (flags & ~MOE_PATH_MASK) return MOE_E_INVAL;
+  if (flags & ~(MOE_PATH_MASK | MOE_QUANT_SEPARATE)) return MOE_E_INVAL;
   if (H % 32 || I % 32 || (n_shared > 0 && I_shared % 32)) return MOE_E_UNSUPPORTED;
   if (E > kPermMaxE) return MOE_E_UNSUPPORTED;
   if ((long long)T * k >= (1LL << 24)) return MOE_E_UNSUPPORTED;
@@ -303,7 +303,8 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   const bool on_m16 = path == MOE_PATH_MFMA16 ||
                       (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs));
   a.in_bf16 = x;
-  if (act == MOE_A8 && !(on_m16 && m16_quant_ok(0, T, H, H))) {
+  if (act == MOE_A8 &&
+      !(on_m16 && !(flags & MOE_QUANT_SEPARATE) && m16_quant_ok(0, T, H, H))) {
     // int8 x rows for the kernels that read them (the 16-row matrix tiles
     // quantize their staged rows themselves when a tile's rows fit)
     int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);

@@ -276,6 +276,19 @@ __device__ __forceinline__ void m16_q_amax(int items, int S, const M16QRegs<MODE
   }
 }
 
+// a8_code(v, s) without a division per element: y = v * (1/s) lies within
+// a few ulps of the IEEE quotient, so the two round to the same integer
+// unless the quotient is within 2^-13 of a half-integer (|y| <= 127.5 and
+// an ulp there is 2^-17); those rare elements take the exact path.
+__device__ __forceinline__ int m16_a8_code(float v, float s, float rs) {
+  if (s == 0.0f) return 0;
+  const float y = v * rs;
+  const float f = y - floorf(y);
+  if (fabsf(f - 0.5f) < 0x1p-13f) return a8_code(v, s);
+  const float q = fminf(fmaxf(rintf(y), -127.0f), 127.0f);
+  return (int)q;
+}
+
 template <int MODE, int BITS>
 __device__ __forceinline__ void m16_q_store(int items, int S, const M16QRegs<MODE>& x,
                                             const uint32_t* rmax, unsigned char* xs, int xstride) {
@@ -285,14 +298,17 @@ __device__ __forceinline__ void m16_q_store(int items, int S, const M16QRegs<MOD
     if (it < items) {
       const int t = it / S, b = it - t * S;
       const float sc = a8_scale(__uint_as_float(rmax[t]));
+      const float rs = sc != 0.0f ? 1.0f / sc : 0.0f;
       uint64_t* dst = reinterpret_cast<uint64_t*>(xs + t * xstride + 32 * b);
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {     // 8-K slices
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          lo |= ((uint32_t)a8_code(m16_q_val<MODE>(x.v[i], 8 * sl + j), sc) & 0xFFu) << (8 * j);
-          hi |= ((uint32_t)a8_code(m16_q_val<MODE>(x.v[i], 8 * sl + 4 + j), sc) & 0xFFu) << (8 * j);
+          lo |= ((uint32_t)m16_a8_code(m16_q_val<MODE>(x.v[i], 8 * sl + j), sc, rs) & 0xFFu)
+                << (8 * j);
+          hi |= ((uint32_t)m16_a8_code(m16_q_val<MODE>(x.v[i], 8 * sl + 4 + j), sc, rs) & 0xFFu)
+                << (8 * j);
         }
         dst[sl] = m16_order_a8<BITS>(lo, hi);
       }

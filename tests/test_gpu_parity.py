@@ -167,6 +167,21 @@ def test_m16_benchmark_layers(cid):
     _check_layer(CONFIGS[cid], flags=3)
 
 
+@pytest.mark.parametrize("name", ["c3", "mid_mixed_a8", "c0_a8", "mixed_shared_a8"])
+def test_m16_a8_kernel_quantizer_matches_row_quantizer(name):
+    """W4A8 gate/up on the 16-row tiles makes the int8 x rows inside the
+    kernel; with MOE_QUANT_SEPARATE the row quantizer launch (bit-exact to
+    the oracle, test_a8_quantizer_bit_exact) makes them instead.  Same codes
+    and scales give the same MFMA inputs, so h and out agree bit for bit."""
+    cfg = CONFIGS[3] if name == "c3" else (MINIS.get(name) or MID[name])
+    dl = _dev(cfg)
+    g1, _ = run_layer_gpu(dl, "a8", 16, 3)
+    g2, _ = run_layer_gpu(dl, "a8", 16, 3 | 4)
+    assert np.array_equal(_valid_h(g1["h32"], cfg), _valid_h(g2["h32"], cfg))
+    assert np.array_equal(g1["out"], g2["out"])
+    assert g1["err"] == 0 and g2["err"] == 0
+
+
 def test_route_ties_and_large_E():
     torch = torch_mod()
     from packed_bit_grouped_amd import _lib as L
