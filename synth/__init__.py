@@ -6,5 +6,5 @@ It holds none of the layer's arithmetic (no routing, no permutation, no
 activation quantization, no projections); both the CPU oracle and the GPU
 library are fed from here and never from each other.
 """
-from .gen import (CONFIGS, LayerConfig, make_layer, config_by_id,  # noqa: F401
+from .gen import (CONFIGS, LAYERS, LayerConfig, make_layer, config_by_id,  # noqa: F401
                   pack_codes, quantize_matrix, bf16_bits_from_f32)

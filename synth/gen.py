@@ -90,6 +90,10 @@ CONFIGS: Dict[int, LayerConfig] = {
 }
 
 
+# The same layers by name.
+LAYERS: Dict[str, LayerConfig] = {c.name: c for c in CONFIGS.values()}
+
+
 def config_by_id(cid: int) -> LayerConfig:
     return CONFIGS[cid]
 

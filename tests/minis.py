@@ -2,9 +2,9 @@
 
 Each is a variant of the benchmark layers that the oracle (and, for the
 smallest, the pure-Python brute force) finishes in seconds."""
-from synth import CONFIGS, LayerConfig
+from synth import LAYERS, LayerConfig
 
-C0 = CONFIGS[0]
+C0 = LAYERS["tiny_w4a16"]
 
 MINIS = {
     # brute-force sized

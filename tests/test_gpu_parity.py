@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import CONFIGS, LayerConfig, make_layer
+from synth import LAYERS, LayerConfig, make_layer
 from tests.gpu_util import (bf16_bits_to_f64, collect, float_gate, h_gate,
                             run_layer_gpu, to_np, torch_mod)
 from tests.minis import MINIS
@@ -137,9 +137,10 @@ def test_mfma_path_rejects_a8_and_odd_shapes():
     assert st == L.MOE_E_UNSUPPORTED
 
 
-@pytest.mark.parametrize("cid", [0, 1, 2, 3])
-def test_benchmark_layers_full(cid):
-    _check_layer(CONFIGS[cid])
+@pytest.mark.parametrize("lname", ["tiny_w4a16", "decode_w4a16_t1", "specdecode_w4a16_t12",
+                                   "decode_w4a8_t64"])
+def test_benchmark_layers_full(lname):
+    _check_layer(LAYERS[lname])
 
 
 # 16-row MFMA tiles (flags 3): every small layer (int4 and int2 experts,
@@ -162,9 +163,9 @@ def test_m16_tile_sizes(tile_m):
     _check_layer(MID["mid_mixed"], tile_m=tile_m, flags=3)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3])
-def test_m16_benchmark_layers(cid):
-    _check_layer(CONFIGS[cid], flags=3)
+@pytest.mark.parametrize("lname", ["decode_w4a16_t1", "specdecode_w4a16_t12", "decode_w4a8_t64"])
+def test_m16_benchmark_layers(lname):
+    _check_layer(LAYERS[lname], flags=3)
 
 
 @pytest.mark.parametrize("name", ["c3", "mid_mixed_a8", "c0_a8", "mixed_shared_a8"])
@@ -173,7 +174,7 @@ def test_m16_a8_kernel_quantizer_matches_row_quantizer(name):
     kernel; with MOE_QUANT_SEPARATE the row quantizer launch (bit-exact to
     the oracle, test_a8_quantizer_bit_exact) makes them instead.  Same codes
     and scales give the same MFMA inputs, so h and out agree bit for bit."""
-    cfg = CONFIGS[3] if name == "c3" else (MINIS.get(name) or MID[name])
+    cfg = LAYERS["decode_w4a8_t64"] if name == "c3" else (MINIS.get(name) or MID[name])
     dl = _dev(cfg)
     g1, _ = run_layer_gpu(dl, "a8", 16, 3)
     g2, _ = run_layer_gpu(dl, "a8", 16, 3 | 4)
@@ -280,7 +281,7 @@ def test_fused_route_gateup_matches_separate_calls(name):
     """moe_w4_route_gateup_silu (one launch for decode batches) writes the
     same routing tables and the same h, bit for bit, as moe_route_permute /
     moe_route_topk + moe_permute followed by moe_w4_gateup_silu."""
-    cfg = {"c0": CONFIGS[0], "c1": CONFIGS[1], **MINIS}[name]
+    cfg = {"c0": LAYERS["tiny_w4a16"], "c1": LAYERS["decode_w4a16_t1"], **MINIS}[name]
     dl = _dev(cfg)
     g1, _ = run_layer_gpu(dl, "a16", 16, fused=True)
     g2, _ = run_layer_gpu(dl, "a16", 16, fused=False)
@@ -347,7 +348,7 @@ def test_a8_partials_bit_exact(name):
     equal the oracle's partials computed from those codes."""
     torch = torch_mod()
     from packed_bit_grouped_amd import _lib as L
-    cfg = CONFIGS[3] if name == "c3" else (MINIS.get(name) or MID[name])
+    cfg = LAYERS["decode_w4a8_t64"] if name == "c3" else (MINIS.get(name) or MID[name])
     layer = _layer(cfg)
     dl = _dev(cfg)
     B = dl.buffers("a8", 16)
@@ -413,7 +414,7 @@ def test_a8_partials_bit_exact(name):
 def test_prefill_layer_sampled_tokens():
     """The prefill layer at full size (4096 tokens, 256 experts, 192 int4 +
     64 int2): integer stages in full, outputs on a token sample."""
-    cfg = CONFIGS[4]
+    cfg = LAYERS["prefill_mixed_t4096"]
     layer = _layer(cfg)
     dl = _dev(cfg)
     tile_m = 64
@@ -440,7 +441,7 @@ def test_prefill_layer_sampled_tokens():
 
 
 def test_repeat_bitwise_identical():
-    dl = _dev(CONFIGS[2])
+    dl = _dev(LAYERS["specdecode_w4a16_t12"])
     g1, _ = run_layer_gpu(dl, "a16", 16)
     g2, _ = run_layer_gpu(dl, "a16", 16)
     assert np.array_equal(g1["out"], g2["out"])
@@ -456,7 +457,7 @@ def test_graph_replay_matches_eager(name):
     matrix-core forms): every replay, with eager work and synchronizations
     in between, reproduces the eager step bit for bit."""
     torch = torch_mod()
-    cfg = {"c1": CONFIGS[1], **MINIS, **MFMA}[name]
+    cfg = {"c1": LAYERS["decode_w4a16_t1"], **MINIS, **MFMA}[name]
     dl = _dev(cfg)
     B = dl.buffers()
     dl.run(B, 0)

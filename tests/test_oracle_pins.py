@@ -18,7 +18,7 @@ from scipy.special import softmax
 
 import oracle
 from oracle import brute
-from synth import CONFIGS, LayerConfig, make_layer, pack_codes, quantize_matrix
+from synth import LAYERS, LayerConfig, make_layer, pack_codes, quantize_matrix
 from synth.gen import Expert, Layer, QMat, bf16_bits_from_f32
 from tests.minis import MINIS
 
@@ -217,7 +217,7 @@ def test_oracle_matches_brute_force(name):
 
 
 def test_config0_layer_shape_and_scale():
-    layer = make_layer(CONFIGS[0])
+    layer = make_layer(LAYERS["tiny_w4a16"])
     o = oracle.oracle_layer(layer)
     assert o["out"].shape == (16, 256)
     assert o["ids"].shape == (16, 2)
@@ -379,7 +379,7 @@ def test_token_sample_path_matches_full_layer():
 def test_zipf_prior_skews_routing():
     """12 tokens with the Zipf(1.1) log-prior: a few experts take several
     tokens and most take none (the skew that layer is meant to have)."""
-    layer = make_layer(CONFIGS[2].replace(H=256), experts_only=[])
+    layer = make_layer(LAYERS["specdecode_w4a16_t12"].replace(H=256), experts_only=[])
     ids, _ = oracle.route_topk(layer.logits, 8)
     counts = np.bincount(ids.ravel(), minlength=128)
     assert 12 <= (counts > 0).sum() <= 48
