@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=["auto", "gemv", "mfma"], default="auto")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="run small bf16 decode layers as one launch (moe_w4_layer's "
+                         "opt-in single-launch form)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="after the run, one device copy of MB MiB (a plain copy kernel of "
                          "known size, the scale for hardware byte counters)")
@@ -121,6 +124,7 @@ def main():
 
     cfg = CONFIGS[args.config]
     flags = {"auto": 0, "gemv": 1, "mfma": 2}[args.path]
+    layer_flags = flags | (L.MOE_LAYER_ONE_LAUNCH if args.one_launch else 0)
     torch.cuda.set_device(0)
     t0 = time.time()
     log(f"[bench] generating {cfg.name} ...")
@@ -131,7 +135,7 @@ def main():
     B = dl.buffers(act)
 
     # routing is identical on every step: learn the touched experts once
-    dl.run(B, flags)
+    dl.run(B, layer_flags)
     torch.cuda.synchronize()
     counts = B.counts.cpu().numpy()
     n_touched = int((counts > 0).sum())
@@ -154,7 +158,7 @@ def main():
             f"rotating over {R} bank copies ({R * bytes_all / 1e9:.2f} GB touched per cycle)")
 
     def step(i):
-        run_layer(banks[i % len(banks)], dl.x, dl.logits, B, cfg.renormalize, flags)
+        run_layer(banks[i % len(banks)], dl.x, dl.logits, B, cfg.renormalize, layer_flags)
 
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
 
@@ -164,8 +168,16 @@ def main():
     fused = (decode and act == "a16" and cfg.T * cfg.k <= 64 and cfg.E <= 512
              and B.tile_m <= 16 and cfg.H <= 2048)
 
+    # with --one-launch, small bf16 decode batches run the whole layer as one
+    # launch when the device holds every workgroup of its grid at once (the
+    # library's rule for moe_w4_layer); that launch is then the dominant kernel
+    one = decode and L.moe_w4_layer_one_launch(B.act, T, H, I, E, k, cfg.n_shared,
+                                               cfg.I_shared, B.tile_m, layer_flags) == 1
+
     def gateup(bk):
-        if fused:
+        if one:
+            run_layer(bk, dl.x, dl.logits, B, cfg.renormalize, layer_flags)
+        elif fused:
             L.moe_w4_route_gateup_silu(B.act, dl.logits, dl.x, T, H, I, E, k,
                                        cfg.renormalize, bk.w13, bk.w13_sh, cfg.n_shared,
                                        cfg.I_shared, B.tile_m, B.ids, B.w, B.counts,
@@ -202,7 +214,8 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(G):
-                run_layer(banks[gi * G + i], dl.x, dl.logits, B, cfg.renormalize, flags)
+                run_layer(banks[gi * G + i], dl.x, dl.logits, B, cfg.renormalize,
+                          layer_flags)
         graphs.append(g)
     reps = args.steps // G
     for i in range(max(1, args.warmup // G)):
@@ -221,7 +234,9 @@ def main():
     # launches over distinct bank copies, timed with events on the stream
     # the graph runs on
     n_k = min(len(banks), 32) if decode else 4
-    if fused:
+    if one:
+        kname = "dec_layer_kernel (route + sort + gate/up + SiLU*mul + down + combine)"
+    elif fused:
         kname = "dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)"
     elif decode:
         kname = ("proj_m16_kernel<0> (gate/up + SiLU*mul)" if act == "a16" else
@@ -235,18 +250,20 @@ def main():
     gk.replay()
     reps = max(1, args.steps // n_k)
     gu_ms = timed(lambda i: gk.replay(), reps) / n_k
-    log(f"[bench] gate/up kernel: {gu_ms * 1e3:.2f} us/launch")
+    log(f"[bench] {'layer' if one else 'gate/up'} kernel: {gu_ms * 1e3:.2f} us/launch")
 
     if decode:
         value = bytes_all / (ms * 1e-3) / 1e9
         unit = "GB/s"
-        ach = bytes_w13 / (gu_ms * 1e-3) / 1e9
+        alg = bytes_all if one else bytes_w13
+        ach = alg / (gu_ms * 1e-3) / 1e9
+        key = ("dec_layer_kernel@" if one else
+               "dec_route_gateup_kernel@" if fused else "gateup_call@") + cfg.name
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS,
-                "traffic": measured_traffic(("dec_route_gateup_kernel@" if fused else
-                                             "gateup_call@") + cfg.name),
+                "traffic": measured_traffic(key),
                 "kernel": kname,
-                "algorithmic_bytes": bytes_w13}
+                "algorithmic_bytes": alg}
     else:
         value = flops / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -277,6 +294,7 @@ def main():
                    "experts_touched": n_touched,
                    "bytes_per_step": bytes_all, "flops_per_step": flops,
                    "bank_copies_rotated": len(banks), "path": args.path,
+                   "layer_form": "one launch" if one else "separate calls",
                    "timing": f"HIP graphs of {G} steps over {G} weight copies, replayed back to back",
                    "ms_per_step_eager": ms_eager},
         "roofline": roof,

@@ -177,7 +177,11 @@ moe_status moe_quant_a8_rows(const void* src, int src_is_f32, int R, int C,
  * memory, 256-byte aligned) may be passed to both calls of a layer.  Its
  * first 4 bytes are an error word the kernels OR bits into (bit 0: an
  * expert descriptor was unusable; bit 1: a tile named an expert outside
- * [0, E)); the caller zeroes it once and reads it when it wants to.
+ * [0, E); bit 2: a grid-wide wait of moe_w4_layer expired, the output of
+ * that call is incomplete).  Bytes 256-4351 hold the flags of
+ * moe_w4_layer's grid-wide barrier, which are all equal again whenever a
+ * call has ended.  The caller zeroes the first 4352 bytes once and reads
+ * the error word when it wants to.
  * Rows of h / y: R = T*k + n_shared*T.
  * ------------------------------------------------------------------- */
 size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
@@ -200,6 +204,9 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
                               /* launch even where the gate/up kernel would */
                               /* make the int8 rows itself (same codes; a   */
                               /* check and a fallback)                      */
+#define MOE_LAYER_ONE_LAUNCH 8 /* moe_w4_layer: one launch for the whole    */
+                              /* layer where the shape allows it (same      */
+                              /* results as the two calls)                  */
 
 /* Tile height to pass as moe_permute's tile_m: 128 (the MFMA path's row
  * block) when T*k >= 32*E with A16, else 16.  Both paths accept any
@@ -281,6 +288,45 @@ moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
                                const int32_t* n_tiles, int tile_m,
                                uint16_t* out, void* workspace,
                                size_t ws_bytes, int flags, void* stream);
+
+/* ---------------------------------------------------------------------
+ * moe_w4_layer -- the whole layer: moe_w4_route_gateup_silu followed by
+ * moe_w4_down_combine, with the outputs of both (same argument meanings;
+ * topk_w and pair_pos are outputs here).
+ * Build log "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", sections
+ * "Remove sync and launch overhead from the token loop" (fewer launches,
+ * no host round trips in a decode step) and "Keep low-bit weights packed,
+ * do the work on the NPU" (the layer's projections straight from packed
+ * weights).  By default it issues the two calls.  With
+ * MOE_LAYER_ONE_LAUNCH, for bf16 activations with T*k <= 64, E <= 128,
+ * H <= 2048, I and I_shared <= 1024 and tiles of at most 16 rows, it is
+ * ONE launch: every workgroup routes the batch itself, the gate/up and
+ * down weight streams are issued together, and the workgroups meet at a
+ * grid-wide barrier once h is complete (taken only when the device can
+ * hold every workgroup of the grid at once; the wait is bounded, see the
+ * error word).  On MI355X the two calls are the faster form at the decode
+ * shapes measured (the shared weight stream and the barrier's round trips
+ * cost more than the second launch), so the single launch is opt-in.
+ * Calls sharing a workspace must be ordered on one stream.
+ * Errors: those of the two calls.
+ * ------------------------------------------------------------------- */
+moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x,
+                        int T, int H, int I, int E, int k, int renormalize,
+                        const moe_qmat* w13, const moe_qmat* w2,
+                        const moe_qmat* w13_shared, const moe_qmat* w2_shared,
+                        int n_shared, int I_shared, int tile_m,
+                        int32_t* topk_ids, float* topk_w, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_pair,
+                        int32_t* pair_pos, int32_t* tiles, int32_t* n_tiles,
+                        void* h, uint16_t* out, void* workspace,
+                        size_t ws_bytes, int flags, void* stream);
+
+/* 1 when moe_w4_layer with these arguments (flags included) issues one
+ * launch on the current device, 0 when it issues the two calls, a
+ * negative moe_status for arguments it would reject (or no usable
+ * device). */
+int moe_w4_layer_one_launch(int act, int T, int H, int I, int E, int k,
+                            int n_shared, int I_shared, int tile_m, int flags);
 
 /* ---------------------------------------------------------------------
  * Test hooks of the A8 mode: the same kernels, additionally writing the

@@ -116,6 +116,8 @@ WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
   size_t off = 0;
   L.err = off;
   off += 256;
+  L.flags = off;
+  off += kLayerFlags * 4;
   L.qx = off;
   if (act == MOE_A8) off += up256((size_t)T * H);
   L.sx = off;
@@ -557,3 +559,116 @@ moe_status moe_dbg_w4a8_down_partials(
 }
 
 }  // extern "C"
+
+// Shapes and flags for which moe_w4_layer issues one launch (before the
+// device's residency check).
+static bool layer_one_shape(int act, int T, int H, int I, int E, int k, int n_shared,
+                            int I_shared, int tile_m, int flags) {
+  const int path = flags & MOE_PATH_MASK;
+  return act == MOE_A16 && T > 0 && (path == MOE_PATH_AUTO || path == MOE_PATH_GEMV) &&
+         !use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
+         dec_layer_ok(T, H, I, I_shared, E, k, n_shared, tile_m,
+                      moe_permute_max_tiles(T, k, E, tile_m), ld_h_of(I, n_shared, I_shared));
+}
+
+int moe_w4_layer_one_launch(int act, int T, int H, int I, int E, int k, int n_shared,
+                            int I_shared, int tile_m, int flags) {
+  const bool one = (flags & MOE_LAYER_ONE_LAUNCH) != 0;
+  flags &= ~MOE_LAYER_ONE_LAUNCH;
+  moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
+  if (st != MOE_OK) return st;
+  if (!one) return 0;
+  if (!layer_one_shape(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags)) return 0;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  return dec_layer_one_launch(T, H, I, I_shared, E, k, n_shared, tile_m,
+                              moe_permute_max_tiles(T, k, E, tile_m),
+                              ld_h_of(I, n_shared, I_shared));
+}
+
+moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, int H, int I,
+                        int E, int k, int renormalize, const moe_qmat* w13, const moe_qmat* w2,
+                        const moe_qmat* w13_shared, const moe_qmat* w2_shared, int n_shared,
+                        int I_shared, int tile_m, int32_t* topk_ids, float* topk_w,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                        int32_t* pair_pos, int32_t* tiles, int32_t* n_tiles, void* h,
+                        uint16_t* out, void* workspace, size_t ws_bytes, int flags,
+                        void* stream) {
+  const bool one = (flags & MOE_LAYER_ONE_LAUNCH) != 0;
+  flags &= ~MOE_LAYER_ONE_LAUNCH;   // the component calls do not take it
+  moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
+  if (st != MOE_OK) return st;
+  if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
+  const int ld_h = ld_h_of(I, n_shared, I_shared);
+  const int max_tiles = moe_permute_max_tiles(T, k, E, tile_m);
+  // every argument of both calls, before either form issues anything
+  if (T > 0) {
+    if (!logits || !x || !w13 || !w2 || !topk_ids || !topk_w || !counts || !offsets ||
+        !sorted_pair || !pair_pos || !tiles || !n_tiles || !h || !out)
+      return MOE_E_INVAL;
+    if (n_shared > 0 && (!w13_shared || !w2_shared)) return MOE_E_INVAL;
+    if (!aligned(x, 16) || !aligned(h, 16) || !aligned(tiles, 16) || !aligned(out, 8))
+      return MOE_E_INVAL;
+  }
+  const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  if (one && layer_one_shape(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags)) {
+    st = check_device();
+    if (st != MOE_OK) return st;
+    char* ws = static_cast<char*>(workspace);
+    ProjArgs ag, ad;
+    std::memset(&ag, 0, sizeof(ag));
+    std::memset(&ad, 0, sizeof(ad));
+    ag.mode = 0;
+    ag.in_bf16 = x;
+    ag.ld_in = H;
+    ag.w = w13;
+    ag.w_sh = w13_shared;
+    ag.K = H;
+    ag.K_sh = H;
+    ag.U = I;
+    ag.U_sh = n_shared > 0 ? I_shared : 0;
+    ad.mode = 1;
+    ad.in_bf16 = static_cast<const uint16_t*>(h);
+    ad.ld_in = ld_h;
+    ad.w = w2;
+    ad.w_sh = w2_shared;
+    ad.K = I;
+    ad.K_sh = n_shared > 0 ? I_shared : I;
+    ad.U = H;
+    ad.U_sh = H;
+    for (ProjArgs* a : {&ag, &ad}) {
+      a->T = T;
+      a->k = k;
+      a->P = T * k;
+      a->E = E;
+      a->n_shared = n_shared;
+      a->offsets = offsets;
+      a->sorted_pair = sorted_pair;
+      a->tiles = tiles;
+      a->n_tiles = n_tiles;
+      a->max_tiles = max_tiles;
+      a->maxt = dec_maxt(T, tile_m);
+      a->err = reinterpret_cast<int32_t*>(ws + L.err);
+    }
+    ag.out = h;
+    ag.ld_out = ld_h;
+    ad.topk_w = topk_w;
+    ad.pair_pos = pair_pos;
+    bool launched = false;
+    const hipError_t e = launch_dec_layer(
+        ag, ad, logits, renormalize, tile_m, topk_ids, topk_w, counts, offsets, sorted_pair,
+        pair_pos, tiles, n_tiles, out, reinterpret_cast<uint32_t*>(ws + L.flags), launched,
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return MOE_E_DEVICE;
+    if (launched) return MOE_OK;
+  }
+  st = moe_w4_route_gateup_silu(act, logits, x, T, H, I, E, k, renormalize, w13, w13_shared,
+                                n_shared, I_shared, tile_m, topk_ids, topk_w, counts, offsets,
+                                sorted_pair, pair_pos, tiles, n_tiles, h, workspace, ws_bytes,
+                                flags, stream);
+  if (st != MOE_OK) return st;
+  return moe_w4_down_combine(act, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared, topk_w,
+                             offsets, sorted_pair, pair_pos, tiles, n_tiles, tile_m, out,
+                             workspace, ws_bytes, flags, stream);
+}

@@ -74,15 +74,32 @@ __device__ __forceinline__ void store_a8_planes(uint32_t* row, const uint32_t (&
 // Stage one 32-K block b of a bf16 activation row into its LDS planes
 // (layout above) and record the block's sum of activations (it removes
 // the code bias of the exact bf16 unpack).
-__device__ __forceinline__ void stage_a16_block(const uint16_t* row, int b, int K, int bits,
-                                                uint32_t* xs_row, float* xsum_row) {
+// Split in two so a caller can issue the loads early and store later.
+__device__ __forceinline__ void load_a16_block(const uint16_t* row, int b, uint32_t (&v)[16]) {
   const u32x4_v* src = reinterpret_cast<const u32x4_v*>(row + b * 32);
-  uint32_t v[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4_v t4 = ld_global(src + i);
     v[4 * i] = t4.x; v[4 * i + 1] = t4.y; v[4 * i + 2] = t4.z; v[4 * i + 3] = t4.w;
   }
+}
+
+// The same loads at device scope (coherent across XCDs without a cache
+// write-back or invalidate): rows written by other workgroups of the same
+// launch.
+__device__ __forceinline__ void load_a16_block_coherent(const uint16_t* row, int b,
+                                                        uint32_t (&v)[16]) {
+  const uint64_t* src = reinterpret_cast<const uint64_t*>(row + b * 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint64_t t = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v[2 * i] = (uint32_t)t;
+    v[2 * i + 1] = (uint32_t)(t >> 32);
+  }
+}
+
+__device__ __forceinline__ void store_a16_block(const uint32_t (&v)[16], int b, int K, int bits,
+                                                uint32_t* xs_row, float* xsum_row) {
   float sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -113,6 +130,13 @@ __device__ __forceinline__ void stage_a16_block(const uint16_t* row, int b, int 
   for (int i = 0; i < 4; ++i)
     dst[(p0 + i) * C_r + c] = make_uint4(pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]);
   xsum_row[b] = sum;
+}
+
+__device__ __forceinline__ void stage_a16_block(const uint16_t* row, int b, int K, int bits,
+                                                uint32_t* xs_row, float* xsum_row) {
+  uint32_t v[16];
+  load_a16_block(row, b, v);
+  store_a16_block(v, b, K, bits, xs_row, xsum_row);
 }
 
 // One 16-byte chunk c of a weight row against every staged token.

@@ -80,6 +80,16 @@ __device__ __forceinline__ float dpp_f(float old, float v) {
       __float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
 }
 
+// Workgroup barrier for data exchanged through LDS only.  Unlike
+// __syncthreads() it does not wait for this wave's outstanding global
+// loads and stores (gfx9 counts both on one counter), so weight streams
+// stay in flight across it; each use still waits for its own loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum over aligned groups of `width` lanes, width in {1, 2, 4, 8, 16}; every
 // lane of a group ends with the group's sum, formed in a fixed order.
 // width 16: mirror, half mirror, xor 2, xor 1; width 8: the last three.

@@ -10,10 +10,12 @@ constexpr int kPermIdBits = 9;      // bits of an expert id below kPermMaxE
 constexpr int kRouteMaxE = 1024;    // route: 16 logits per lane
 constexpr int kFusedRouteMaxT = 64; // fused route+permute: tokens per launch
 constexpr int kFusedRouteMaxP = 4096;  // fused route+permute: pairs per launch
+constexpr int kLayerFlags = 1024;   // one-launch layer: barrier flags (and max grid)
 
 // Workspace layout (byte offsets from the workspace base).
 struct WsLayout {
   size_t err;        // int32 error word
+  size_t flags;      // kLayerFlags uint32 barrier flags of the one-launch layer
   size_t qx;         // A8: int8 [T][H]
   size_t sx;         // A8: fp32 [T]
   size_t qh;         // A8: int8 h rows [R][ld_h] (matrix-core decode path)
@@ -100,6 +102,22 @@ hipError_t launch_dec_route_gateup(const ProjArgs& a, const float* logits, int r
                                    int tile_m, int32_t* ids, float* w, int32_t* counts,
                                    int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                                    int32_t* tiles, int32_t* n_tiles, hipStream_t st);
+// The whole layer (route, permute, gate/up, down, combine) in one launch
+// for bf16 decode batches: every workgroup resident at once, a grid-wide
+// barrier on h.  `launched` is false (and nothing was issued) when the
+// grid would not be resident or the LDS would not fit; the caller then
+// issues the two-call form.  flags: kLayerFlags words, all equal (zeroed
+// once; every launch leaves them equal again).
+bool dec_layer_ok(int T, int H, int I, int I_shared, int E, int k, int n_shared, int tile_m,
+                  int max_tiles, int ld_h);
+// 1 when launch_dec_layer would launch for this shape on the current device.
+int dec_layer_one_launch(int T, int H, int I, int I_shared, int E, int k, int n_shared,
+                         int tile_m, int max_tiles, int ld_h);
+hipError_t launch_dec_layer(const ProjArgs& ag, const ProjArgs& ad, const float* logits,
+                            int renorm, int tile_m, int32_t* ids, float* w, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                            int32_t* tiles, int32_t* n_tiles, uint16_t* out, uint32_t* flags,
+                            bool& launched, hipStream_t st);
 // Tiles of at most 16 rows on 16x16 MFMAs (proj_m16.hip).  A8 inputs are
 // int8 rows (a.in_q, stride a.ld_in) with fp32 row scales (a.in_s): x for
 // gate/up, the quantized h rows for down.

@@ -27,6 +27,8 @@
 //    separate combine launch;
 //  * the products use the exact bf16 unpack of the codes with
 //    v_dot2_f32_bf16 and the per-block activation sums (shared helpers).
+#include <mutex>
+
 #include "gemv_common.h"
 #include "route_common.h"
 
@@ -87,22 +89,49 @@ __device__ __forceinline__ bool dec_tile_lds(const ProjArgs& a, int slot, int n_
   return true;
 }
 
-// Copy n 16-byte words from global memory to LDS with the whole block.
-__device__ __forceinline__ void copy_words(u32x4_v* dst, const void* src, int n) {
-  const u32x4_v* s = reinterpret_cast<const u32x4_v*>(src);
-  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = ld_global(s + i);
-}
-__device__ __forceinline__ void copy_ints(int* dst, const int* src, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = ld_global(src + i);
-}
+// Copies of small global tables into LDS in two halves: fetch() issues
+// this thread's loads (words tid, tid + blockDim, ... up to PER of them)
+// and put() stores them, so the loads of every table a kernel needs, and
+// of anything else issued in between, share one memory round trip.
+// Entries past PER * blockDim are copied by a plain loop inside put().
+template <class W, int PER>
+struct TableCopy {
+  W v[PER];
+  __device__ __forceinline__ void fetch(const W* src, int n) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int i = threadIdx.x + r * kDecThreads;
+      if (i < n) v[r] = ld_global(src + i);
+    }
+  }
+  __device__ __forceinline__ void put(W* dst, const W* src, int n) const {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int i = threadIdx.x + r * kDecThreads;
+      if (i < n) dst[i] = v[r];
+    }
+    for (int i = threadIdx.x + PER * kDecThreads; i < n; i += kDecThreads)
+      dst[i] = ld_global(src + i);
+  }
+};
 
-// Descriptor tables (routed then shared) in LDS: [E + n_shared] moe_qmat.
-__device__ __forceinline__ void copy_descs(moe_qmat* dst, const ProjArgs& a) {
-  constexpr int w = sizeof(moe_qmat) / 16;
-  copy_words(reinterpret_cast<u32x4_v*>(dst), a.w, a.E * w);
-  if (a.n_shared > 0)
-    copy_words(reinterpret_cast<u32x4_v*>(dst + a.E), a.w_sh, a.n_shared * w);
-}
+// Descriptor tables (routed then shared) in LDS: [E + n_shared] moe_qmat,
+// two 16-byte words each.
+template <int PER>
+struct DescCopy {
+  static constexpr int kW = sizeof(moe_qmat) / 16;
+  TableCopy<u32x4_v, PER> routed, shared;
+  __device__ __forceinline__ void fetch(const ProjArgs& a) {
+    routed.fetch(reinterpret_cast<const u32x4_v*>(a.w), a.E * kW);
+    if (a.n_shared > 0) shared.fetch(reinterpret_cast<const u32x4_v*>(a.w_sh), a.n_shared * kW);
+  }
+  __device__ __forceinline__ void put(moe_qmat* dst, const ProjArgs& a) const {
+    routed.put(reinterpret_cast<u32x4_v*>(dst), reinterpret_cast<const u32x4_v*>(a.w), a.E * kW);
+    if (a.n_shared > 0)
+      shared.put(reinterpret_cast<u32x4_v*>(dst + a.E),
+                 reinterpret_cast<const u32x4_v*>(a.w_sh), a.n_shared * kW);
+  }
+};
 
 // Scale word of code chunk c (int2 with 32-wide groups: two scales).
 __device__ __forceinline__ uint32_t dec_scale(const uint16_t* sp, const RowGeom& G, int c) {
@@ -116,57 +145,61 @@ __device__ __forceinline__ uint32_t dec_scale(const uint16_t* sp, const RowGeom&
 // expert.  Wave w: units 16 ub + w and 16 ub + 8 + w, the loads of both
 // issued together; lanes 0-31 hold a unit's gate row, lanes 32-63 its up
 // row.  srow: the sorted pair list in LDS, or null (read from memory).
-template <int MAXT, int CPL>
-__device__ __forceinline__ void gateup_tile(const ProjArgs& a, bool is_sh, int e, int r_begin,
-                                            int r_end, const moe_qmat& q, int ub,
-                                            const int* srow, uint32_t* xs, float* xsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K;
-  const int U = is_sh ? a.U_sh : a.U;
-  const RowGeom G = row_geom(q, K, 0);
-  const int lis = lane & (kDecGuLanes - 1);
-  const bool up = lane >= kDecGuLanes;
+//
+// Split in two: gu_issue starts every weight load of the wave (nothing
+// waits), gu_compute applies the staged activation rows and writes h.
+template <int CPL>
+struct GuRows {
   int unit[2], wr[2];
   bool vrow[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    unit[r] = ub * 2 * kDecWaves + r * kDecWaves + wave;
-    vrow[r] = unit[r] < U;
-    wr[r] = vrow[r] ? unit[r] + (up ? U : 0) : 0;
-  }
-
-  // ---- every weight load of the workgroup, then the activation rows
+  RowGeom G;
   uint4 wv[2][CPL];
   uint32_t sv[2][CPL];
+};
+
+template <int CPL>
+__device__ __forceinline__ void gu_issue(GuRows<CPL>& g, const ProjArgs& a, bool is_sh,
+                                         const moe_qmat& q, int ub) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int U = is_sh ? a.U_sh : a.U;
+  g.G = row_geom(q, a.K, 0);
+  const int lis = lane & (kDecGuLanes - 1);
+  const bool up = lane >= kDecGuLanes;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const uint4* cp = reinterpret_cast<const uint4*>(q.codes + (size_t)wr[r] * G.row_bytes);
-    const uint16_t* sp = q.scales + (size_t)wr[r] * G.ng;
+    g.unit[r] = ub * 2 * kDecWaves + r * kDecWaves + wave;
+    g.vrow[r] = g.unit[r] < U;
+    g.wr[r] = g.vrow[r] ? g.unit[r] + (up ? U : 0) : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint4* cp = reinterpret_cast<const uint4*>(q.codes + (size_t)g.wr[r] * g.G.row_bytes);
+    const uint16_t* sp = q.scales + (size_t)g.wr[r] * g.G.ng;
 #pragma unroll
     for (int b = 0; b < CPL; ++b) {
       const int c = lis + kDecGuLanes * b;
-      if (vrow[r] && c < G.C_r) {
+      if (g.vrow[r] && c < g.G.C_r) {
         const u32x4_v t4 = ld_global_nt(reinterpret_cast<const u32x4_v*>(cp + c));
-        wv[r][b] = make_uint4(t4.x, t4.y, t4.z, t4.w);
-        sv[r][b] = dec_scale(sp, G, c);
+        g.wv[r][b] = make_uint4(t4.x, t4.y, t4.z, t4.w);
+        g.sv[r][b] = dec_scale(sp, g.G, c);
       } else {
-        wv[r][b] = make_uint4(0u, 0u, 0u, 0u);
-        sv[r][b] = 0u;
+        g.wv[r][b] = make_uint4(0u, 0u, 0u, 0u);
+        g.sv[r][b] = 0u;
       }
     }
   }
-  const int xs_row = K / 2, xsum_row = K / 32, nb32 = K / 32;
-  // one pass: the launcher guarantees a tile has at most MAXT rows
-  const int nt = min(MAXT, r_end - r_begin);
-  for (int u = tid; u < nt * nb32; u += kDecThreads) {
-    const int m = u / nb32, b = u - m * nb32;
-    int row = r_begin + m;
-    if (!is_sh) row = (srow ? srow[row] : ld_global(a.sorted_pair + row)) / a.k;
-    stage_a16_block(a.in_bf16 + (size_t)row * a.ld_in, b, K, G.bits, xs + m * xs_row,
-                    xsum + m * xsum_row);
-  }
-  __syncthreads();
+}
 
+// COHERENT: h is stored at device scope (read back by other workgroups of
+// the same launch).
+template <int MAXT, int CPL, bool COHERENT = false>
+__device__ __forceinline__ void gu_compute(const GuRows<CPL>& g, const ProjArgs& a, bool is_sh,
+                                           int e, int r_begin, int nt, const uint32_t* xs,
+                                           const float* xsum) {
+  const int lane = threadIdx.x & 63;
+  const int K = a.K;
+  const int lis = lane & (kDecGuLanes - 1);
+  const int xs_row = K / 2, xsum_row = K / 32;
   const int orow0 = is_sh ? a.P + e * a.T + r_begin : r_begin;
   uint16_t* h = static_cast<uint16_t*>(a.out);
 #pragma unroll
@@ -177,22 +210,51 @@ __device__ __forceinline__ void gateup_tile(const ProjArgs& a, bool is_sh, int e
 #pragma unroll
     for (int b = 0; b < CPL; ++b) {
       const int c = lis + kDecGuLanes * b;
-      if (c < G.C_r)
-        chunk_dot<MOE_A16, MAXT, false>(a, wv[r][b], sv[r][b], c, G, nt, xs, xs_row, xsum,
-                                        xsum_row, acc, lis, vrow[r], wr[r], 0);
+      if (c < g.G.C_r)
+        chunk_dot<MOE_A16, MAXT, false>(a, g.wv[r][b], g.sv[r][b], c, g.G, nt, xs, xs_row, xsum,
+                                        xsum_row, acc, lis, g.vrow[r], g.wr[r], 0);
     }
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
       if (t >= nt) break;
       // rows of 16 lanes, then row 0 into row 1 and row 2 into row 3:
       // lane 16 ends with the gate sum, lane 48 with the up sum
-      float g = group_sum(acc[t], 16);
-      g += dpp_f<kDppRowBcast15, 0xA>(0.0f, g);
-      const float u = __shfl_down(g, 32);
-      if (lane == 16 && vrow[r])
-        h[(size_t)(orow0 + t) * a.ld_out + unit[r]] = (uint16_t)f32_to_bf16(silu_mul(g, u));
+      float gs = group_sum(acc[t], 16);
+      gs += dpp_f<kDppRowBcast15, 0xA>(0.0f, gs);
+      const float u = __shfl_down(gs, 32);
+      if (lane == 16 && g.vrow[r]) {
+        uint16_t* hp = h + (size_t)(orow0 + t) * a.ld_out + g.unit[r];
+        const uint16_t hv = (uint16_t)f32_to_bf16(silu_mul(gs, u));
+        if (COHERENT)
+          __hip_atomic_store(hp, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *hp = hv;
+      }
     }
   }
+}
+
+template <int MAXT, int CPL>
+__device__ __forceinline__ void gateup_tile(const ProjArgs& a, bool is_sh, int e, int r_begin,
+                                            int r_end, const moe_qmat& q, int ub,
+                                            const int* srow, uint32_t* xs, float* xsum) {
+  const int tid = threadIdx.x;
+  const int K = a.K;
+  // ---- every weight load of the workgroup, then the activation rows
+  GuRows<CPL> g;
+  gu_issue<CPL>(g, a, is_sh, q, ub);
+  const int xs_row = K / 2, xsum_row = K / 32, nb32 = K / 32;
+  // one pass: the launcher guarantees a tile has at most MAXT rows
+  const int nt = min(MAXT, r_end - r_begin);
+  for (int u = tid; u < nt * nb32; u += kDecThreads) {
+    const int m = u / nb32, b = u - m * nb32;
+    int row = r_begin + m;
+    if (!is_sh) row = (srow ? srow[row] : ld_global(a.sorted_pair + row)) / a.k;
+    stage_a16_block(a.in_bf16 + (size_t)row * a.ld_in, b, K, g.G.bits, xs + m * xs_row,
+                    xsum + m * xsum_row);
+  }
+  lds_barrier();
+  gu_compute<MAXT, CPL>(g, a, is_sh, e, r_begin, nt, xs, xsum);
 }
 
 // LDS carve-up shared by the gate/up kernels: activation planes, their
@@ -223,9 +285,13 @@ __global__ __launch_bounds__(kDecThreads) void dec_gateup_kernel(ProjArgs a, int
     const u32x4_v t4 = ld_global(reinterpret_cast<const u32x4_v*>(a.tiles) + j);
     tl = make_int4((int)t4.x, (int)t4.y, (int)t4.z, (int)t4.w);
   }
-  copy_descs(descs, a);
-  if (srow_lds) copy_ints(srow, a.sorted_pair, a.P);
-  __syncthreads();
+  DescCopy<1> dc;
+  TableCopy<int, 1> sc;
+  dc.fetch(a);
+  if (srow_lds) sc.fetch(a.sorted_pair, a.P);
+  dc.put(descs, a);
+  if (srow_lds) sc.put(srow, a.sorted_pair, a.P);
+  lds_barrier();
 
   bool is_sh;
   int e, r_begin, r_end;
@@ -282,7 +348,7 @@ constexpr int kFusedMaxP = 64;
 // same outputs as the block-wide sort of the routing kernels.
 template <int NV>
 __device__ void wave_permute(const int* ids, int P, int E, int tile_m, int* srt_l, int4* til_l,
-                             int* ntl_l, const RouteOut* ro) {
+                             int* ntl_l, int* ppos_l, const RouteOut* ro) {
   const int lane = threadIdx.x & 63;
   const bool in = lane < P;
   const int ep = in ? ids[lane] : 0x7fffffff;
@@ -303,6 +369,7 @@ __device__ void wave_permute(const int* ids, int P, int E, int tile_m, int* srt_
   }
   const int n_tiles = __popcll(__ballot(start));
   if (in) srt_l[pos] = lane;
+  if (in && ppos_l) ppos_l[lane] = pos;
   if (start) til_l[tidx] = make_int4(ep, pos, min(pos + tile_m, lt + same), 0);
   if (lane == 0) *ntl_l = n_tiles;
   if (ro) {
@@ -353,15 +420,17 @@ __global__ __launch_bounds__(kDecThreads) void dec_route_gateup_kernel(ProjArgs 
   int* srt = reinterpret_cast<int*>(rw + kFusedMaxP);                  // [64]
   int* ntl = srt + kFusedMaxP;                                         // [1]
 
-  // ---- round trip 1: descriptors and logits; routing and sorting
-  copy_descs(descs, a);
+  // ---- round trip 1: descriptors and logits together; routing and sorting
+  DescCopy<1> dc;
+  dc.fetch(a);
   const bool writer = blockIdx.x == 0;
   static_assert(kFusedMaxP <= 8 * kDecWaves, "every token routed in two passes");
   route_tokens<NV, 2>(logits, a.T, E, a.k, renorm, lane, wave, kDecWaves,
                       writer ? ro.ids : nullptr, writer ? ro.w : nullptr, rid, rw);
-  __syncthreads();
-  if (wave == 0) wave_permute<NV>(rid, P, E, tile_m, srt, til, ntl, writer ? &ro : nullptr);
-  __syncthreads();
+  dc.put(descs, a);
+  lds_barrier();
+  if (wave == 0) wave_permute<NV>(rid, P, E, tile_m, srt, til, ntl, nullptr, writer ? &ro : nullptr);
+  lds_barrier();
 
   bool is_sh;
   int e, r_begin, r_end;
@@ -384,86 +453,94 @@ __global__ __launch_bounds__(kDecThreads) void dec_route_gateup_kernel(ProjArgs 
 // lanes per weight row (one output column per lane group); the per-row
 // results meet in LDS and each token's 8 outputs are combined in the
 // fixed order of the combine: routed j = 0..k-1 (weighted), then shared.
-template <int MAXT, int CPL>
-__global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs a, int R_rows,
-                                                                       uint16_t* __restrict__ out) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ld = a.ld_in;                                                // h row stride
-  const int xs_row = ld / 2, xsum_row = ld / 32;
-  // LDS: tile list, descriptor tables, pair positions and gate weights
-  // first (16-byte aligned), then the staged rows and the results
-  int4* tls = reinterpret_cast<int4*>(smem);                             // [max_tiles]
-  moe_qmat* descs = reinterpret_cast<moe_qmat*>(tls + a.max_tiles);      // [E + n_shared]
-  int* ppos = reinterpret_cast<int*>(descs + a.E + a.n_shared);          // [P]
-  float* gw = reinterpret_cast<float*>(ppos + a.P);                      // [P]
-  int* rbits = reinterpret_cast<int*>(gw + a.P);                         // [R_rows]
-  uint32_t* xs = reinterpret_cast<uint32_t*>(
-      smem + (((size_t)a.max_tiles * 16 + (size_t)(a.E + a.n_shared) * sizeof(moe_qmat) +
-               (size_t)a.P * 8 + (size_t)R_rows * 4 + 15) / 16 * 16));   // [R_rows][ld/2]
-  float* xsum = reinterpret_cast<float*>(xs + (size_t)R_rows * xs_row);  // [R_rows][ld/32]
-  float* yb = xsum + (size_t)R_rows * xsum_row;                          // [R_rows][4]
-  const int H = a.U;
-  const int n0 = blockIdx.x * kDecDnCols;
-  const int lis = lane & (kDecDnLanes - 1), col = lane / kDecDnLanes;
-  const int n = n0 + col;
+//
+// The pieces (dn_issue, dn_stage, dn_run, dn_combine) are shared with the
+// one-launch layer kernel below.
 
-  // ---- round trip 1, all independent: counts and every table
-  const int n_tiles = min(ld_global(a.n_tiles), a.max_tiles);
-  const int total_valid = ld_global(a.offsets + a.E);
-  copy_words(reinterpret_cast<u32x4_v*>(tls), a.tiles, a.max_tiles);
-  copy_descs(descs, a);
-  copy_ints(ppos, a.pair_pos, a.P);
-  copy_ints(reinterpret_cast<int*>(gw), reinterpret_cast<const int*>(a.topk_w), a.P);
-  __syncthreads();
-  const int S = a.n_sh_slots + n_tiles;
+// LDS carve-up of the down part: per-row bits, the staged h rows, their
+// block sums and the per-row results.
+struct DnLds {
+  int* rbits;      // [R_rows]
+  uint32_t* xs;    // [R_rows][ld/2]
+  float* xsum;     // [R_rows][ld/32]
+  float* yb;       // [R_rows][kDecDnCols]
+};
+__device__ __forceinline__ size_t dn_rows_bytes(int R_rows, int ld) {
+  return (size_t)R_rows * ((size_t)ld * 2 + (size_t)(ld / 32) * 4 + kDecDnCols * 4);
+}
+// base: 16-byte aligned; rbits first, then the rows from the next 16 bytes.
+__device__ __forceinline__ DnLds dn_lds(unsigned char* base, int R_rows, int ld) {
+  DnLds d;
+  d.rbits = reinterpret_cast<int*>(base);
+  d.xs = reinterpret_cast<uint32_t*>(base + ((size_t)R_rows * 4 + 15) / 16 * 16);
+  d.xsum = reinterpret_cast<float*>(d.xs + (size_t)R_rows * (ld / 2));
+  d.yb = d.xsum + (size_t)R_rows * (ld / 32);
+  return d;
+}
 
-  // ---- this wave's tiles, kDecDnRounds at a time: every weight load of
-  // the batch (round trip 2, together with the h rows below)
+template <int CPL>
+struct DnSlots {
   bool ok[kDecDnRounds], shr[kDecDnRounds];
   int te[kDecDnRounds], tr0[kDecDnRounds], tr1[kDecDnRounds];
   RowGeom G[kDecDnRounds];
   uint4 wv[kDecDnRounds][CPL];
   uint32_t sv[kDecDnRounds][CPL];
-  auto issue = [&](int batch) {
+};
+
+// This wave's tiles of batch `batch` (kDecDnRounds of them): every weight
+// load of the four columns n0..n0+3, nothing waits.
+template <int CPL>
+__device__ __forceinline__ void dn_issue(DnSlots<CPL>& d, const ProjArgs& a, int batch, int S,
+                                         int n_tiles, const int4* tls, const moe_qmat* descs,
+                                         int n) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lis = lane & (kDecDnLanes - 1);
+  const int H = a.U;
 #pragma unroll
-    for (int i = 0; i < kDecDnRounds; ++i) {
-      const int slot = wave + kDecWaves * (batch * kDecDnRounds + i);
-      ok[i] = slot < S && dec_tile_lds(a, slot, n_tiles, tls, shr[i], te[i], tr0[i], tr1[i]);
-      if (ok[i] && !shr[i] && (unsigned)te[i] >= (unsigned)a.E) {
-        if (lane == 0) atomicOr(a.err, 2);
-        ok[i] = false;
-      }
-      moe_qmat q;
-      if (ok[i]) {
-        q = descs[shr[i] ? a.E + te[i] : te[i]];
-        const int K = shr[i] ? a.K_sh : a.K;
-        if (!qmat_usable(q, H, K)) {
-          if (lane == 0) atomicOr(a.err, 1);
-          ok[i] = false;
-        } else {
-          G[i] = row_geom(q, K, 1);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < CPL; ++b) {
-        const int c = lis + kDecDnLanes * b;
-        if (ok[i] && c < G[i].C_r) {
-          const uint4* cp = reinterpret_cast<const uint4*>(q.codes + (size_t)n * G[i].row_bytes);
-          const u32x4_v t4 = ld_global_nt(reinterpret_cast<const u32x4_v*>(cp + c));
-          wv[i][b] = make_uint4(t4.x, t4.y, t4.z, t4.w);
-          sv[i][b] = dec_scale(q.scales + (size_t)n * G[i].ng, G[i], c);
-        } else {
-          wv[i][b] = make_uint4(0u, 0u, 0u, 0u);
-          sv[i][b] = 0u;
-        }
+  for (int i = 0; i < kDecDnRounds; ++i) {
+    const int slot = wave + kDecWaves * (batch * kDecDnRounds + i);
+    d.ok[i] = slot < S && dec_tile_lds(a, slot, n_tiles, tls, d.shr[i], d.te[i], d.tr0[i], d.tr1[i]);
+    if (d.ok[i] && !d.shr[i] && (unsigned)d.te[i] >= (unsigned)a.E) {
+      if (lane == 0) atomicOr(a.err, 2);
+      d.ok[i] = false;
+    }
+    moe_qmat q;
+    if (d.ok[i]) {
+      q = descs[d.shr[i] ? a.E + d.te[i] : d.te[i]];
+      const int K = d.shr[i] ? a.K_sh : a.K;
+      if (!qmat_usable(q, H, K)) {
+        if (lane == 0) atomicOr(a.err, 1);
+        d.ok[i] = false;
+      } else {
+        d.G[i] = row_geom(q, K, 1);
       }
     }
-  };
-  issue(0);
+#pragma unroll
+    for (int b = 0; b < CPL; ++b) {
+      const int c = lis + kDecDnLanes * b;
+      if (d.ok[i] && c < d.G[i].C_r) {
+        const uint4* cp = reinterpret_cast<const uint4*>(q.codes + (size_t)n * d.G[i].row_bytes);
+        const u32x4_v t4 = ld_global_nt(reinterpret_cast<const u32x4_v*>(cp + c));
+        d.wv[i][b] = make_uint4(t4.x, t4.y, t4.z, t4.w);
+        d.sv[i][b] = dec_scale(q.scales + (size_t)n * d.G[i].ng, d.G[i], c);
+      } else {
+        d.wv[i][b] = make_uint4(0u, 0u, 0u, 0u);
+        d.sv[i][b] = 0u;
+      }
+    }
+  }
+}
 
-  // ---- bits of every staged row: routed rows from their tiles, shared
-  // rows from their expert
+// Bits of every staged row (routed rows from their tiles, shared rows from
+// their expert), then the h rows themselves (routed rows past the valid
+// ones are never read).  Ends with the block in step.
+template <bool COHERENT = false>
+__device__ __forceinline__ void dn_stage(const ProjArgs& a, int S, int n_tiles, const int4* tls,
+                                         const moe_qmat* descs, int R_rows, int total_valid,
+                                         const DnLds& L) {
+  const int tid = threadIdx.x;
+  const int ld = a.ld_in;
+  const int xs_row = ld / 2, xsum_row = ld / 32;
   for (int j = tid; j < S; j += kDecThreads) {
     bool is_sh;
     int e, r0, r1;
@@ -471,58 +548,64 @@ __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs 
     if (!is_sh && (unsigned)e >= (unsigned)a.E) continue;
     const int bits = descs[is_sh ? a.E + e : e].bits;
     const int base = is_sh ? a.P + e * a.T : 0;
-    for (int r = r0; r < r1; ++r) rbits[base + r] = bits;
+    for (int r = r0; r < r1; ++r) L.rbits[base + r] = bits;
   }
-  __syncthreads();
-  // ---- stage the h rows (routed rows past the valid ones are never read)
+  lds_barrier();
   const int nbmax = ld / 32;
   for (int u = tid; u < R_rows * nbmax; u += kDecThreads) {
     const int row = u / nbmax, b = u - row * nbmax;
     const int K = row < a.P ? a.K : a.K_sh;
     if (b >= K / 32 || (row < a.P && row >= total_valid)) continue;
-    stage_a16_block(a.in_bf16 + (size_t)row * ld, b, K, rbits[row], xs + (size_t)row * xs_row,
-                    xsum + (size_t)row * xsum_row);
+    uint32_t v[16];
+    if (COHERENT)
+      load_a16_block_coherent(a.in_bf16 + (size_t)row * ld, b, v);
+    else
+      load_a16_block(a.in_bf16 + (size_t)row * ld, b, v);
+    store_a16_block(v, b, K, L.rbits[row], L.xs + (size_t)row * xs_row,
+                    L.xsum + (size_t)row * xsum_row);
   }
-  __syncthreads();
+  lds_barrier();
+}
 
-  // ---- the tiles: 4 rows (columns n0..n0+3) of each, every token
-  auto run = [&](const int i) {
-    // one pass: the launcher guarantees a tile has at most MAXT rows; a
-    // wave without a tile in this round computes nothing and stores
-    // nothing (no early exit, so both rounds stay one straight block)
-    const int nt = ok[i] ? min(MAXT, tr1[i] - tr0[i]) : 0;
-    const int hrow0 = ok[i] ? (shr[i] ? a.P + te[i] * a.T : 0) + tr0[i] : 0;
-    const int C_r = ok[i] ? G[i].C_r : 0;
-    float acc[MAXT];
+// Round i of the wave's batch: the 4 rows (columns n0..n0+3) of the tile
+// against every token of it.  One pass: the launcher guarantees a tile has
+// at most MAXT rows; a wave without a tile in this round computes nothing
+// and stores nothing (no early exit, so the rounds stay one straight block).
+template <int MAXT, int CPL>
+__device__ __forceinline__ void dn_run(const DnSlots<CPL>& d, int i, const ProjArgs& a,
+                                       const DnLds& L, int n) {
+  const int lane = threadIdx.x & 63;
+  const int lis = lane & (kDecDnLanes - 1), col = lane / kDecDnLanes;
+  const int xs_row = a.ld_in / 2, xsum_row = a.ld_in / 32;
+  const int nt = d.ok[i] ? min(MAXT, d.tr1[i] - d.tr0[i]) : 0;
+  const int hrow0 = d.ok[i] ? (d.shr[i] ? a.P + d.te[i] * a.T : 0) + d.tr0[i] : 0;
+  const int C_r = d.ok[i] ? d.G[i].C_r : 0;
+  float acc[MAXT];
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t) acc[t] = 0.0f;
+  for (int t = 0; t < MAXT; ++t) acc[t] = 0.0f;
 #pragma unroll
-    for (int b = 0; b < CPL; ++b) {
-      const int c = lis + kDecDnLanes * b;
-      if (c < C_r)
-        chunk_dot<MOE_A16, MAXT, false>(a, wv[i][b], sv[i][b], c, G[i], nt,
-                                        xs + (size_t)hrow0 * xs_row, xs_row,
-                                        xsum + (size_t)hrow0 * xsum_row, xsum_row, acc, lis,
-                                        true, n, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-      if (t >= nt) break;
-      const float v = group_sum(acc[t], kDecDnLanes);
-      if (lis == 0) yb[(size_t)(hrow0 + t) * kDecDnCols + col] = v;
-    }
-  };
-  static_assert(kDecDnRounds == 2, "one run() per round below");
-  const int n_batches = (S + kDecWaves * kDecDnRounds - 1) / (kDecWaves * kDecDnRounds);
-  for (int batch = 0; batch < n_batches; ++batch) {
-    if (batch > 0) issue(batch);
-    run(0);
-    run(1);
+  for (int b = 0; b < CPL; ++b) {
+    const int c = lis + kDecDnLanes * b;
+    if (c < C_r)
+      chunk_dot<MOE_A16, MAXT, false>(a, d.wv[i][b], d.sv[i][b], c, d.G[i], nt,
+                                      L.xs + (size_t)hrow0 * xs_row, xs_row,
+                                      L.xsum + (size_t)hrow0 * xsum_row, xsum_row, acc, lis,
+                                      true, n, 0);
   }
-  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t >= nt) break;
+    const float v = group_sum(acc[t], kDecDnLanes);
+    if (lis == 0) L.yb[(size_t)(hrow0 + t) * kDecDnCols + col] = v;
+  }
+}
 
-  // ---- combine: out[t][n] = sum_j w[t][j] * y[pair_pos[t*k+j]][n] + sum_s y_s[t][n]
-  for (int idx = tid; idx < a.T * kDecDnCols; idx += kDecThreads) {
+// out[t][n] = sum_j w[t][j] * y[pair_pos[t*k+j]][n] + sum_s y_s[t][n] for
+// the columns n0..n0+3, in that order.
+__device__ __forceinline__ void dn_combine(const ProjArgs& a, const int* ppos, const float* gw,
+                                           const float* yb, uint16_t* __restrict__ out, int n0) {
+  const int H = a.U;
+  for (int idx = threadIdx.x; idx < a.T * kDecDnCols; idx += kDecThreads) {
     const int t = idx / kDecDnCols, cc = idx - t * kDecDnCols;
     float acc = 0.0f;
     // eight pairs at a time: all LDS reads first, then the fma chain in j
@@ -545,6 +628,244 @@ __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs 
     for (int s = 0; s < a.n_shared; ++s) acc += yb[(size_t)(a.P + s * a.T + t) * kDecDnCols + cc];
     out[(size_t)t * H + n0 + cc] = (uint16_t)f32_to_bf16(acc);
   }
+}
+
+template <int MAXT, int CPL>
+__global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs a, int R_rows,
+                                                                       uint16_t* __restrict__ out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  // LDS: tile list, descriptor tables, pair positions and gate weights
+  // first (16-byte aligned), then the down part's rows
+  int4* tls = reinterpret_cast<int4*>(smem);                             // [max_tiles]
+  moe_qmat* descs = reinterpret_cast<moe_qmat*>(tls + a.max_tiles);      // [E + n_shared]
+  int* ppos = reinterpret_cast<int*>(descs + a.E + a.n_shared);          // [P]
+  float* gw = reinterpret_cast<float*>(ppos + a.P);                      // [P]
+  const DnLds L = dn_lds(smem + ((size_t)a.max_tiles * 16 +
+                                 (size_t)(a.E + a.n_shared) * sizeof(moe_qmat) +
+                                 (size_t)a.P * 8 + 15) / 16 * 16,
+                         R_rows, a.ld_in);
+  const int n0 = blockIdx.x * kDecDnCols;
+  const int n = n0 + (threadIdx.x & 63) / kDecDnLanes;
+
+  // ---- round trip 1, all independent: counts and every table
+  const int n_tiles = min(ld_global(a.n_tiles), a.max_tiles);
+  const int total_valid = ld_global(a.offsets + a.E);
+  const u32x4_v* tsrc = reinterpret_cast<const u32x4_v*>(a.tiles);
+  const int* wsrc = reinterpret_cast<const int*>(a.topk_w);
+  TableCopy<u32x4_v, 1> tc;
+  DescCopy<1> dc;
+  TableCopy<int, 1> pc, wc;
+  tc.fetch(tsrc, a.max_tiles);
+  dc.fetch(a);
+  pc.fetch(a.pair_pos, a.P);
+  wc.fetch(wsrc, a.P);
+  tc.put(reinterpret_cast<u32x4_v*>(tls), tsrc, a.max_tiles);
+  dc.put(descs, a);
+  pc.put(ppos, a.pair_pos, a.P);
+  wc.put(reinterpret_cast<int*>(gw), wsrc, a.P);
+  lds_barrier();
+  const int S = a.n_sh_slots + n_tiles;
+
+  // ---- this wave's tiles, kDecDnRounds at a time: every weight load of
+  // the batch (round trip 2, together with the h rows below)
+  DnSlots<CPL> d;
+  dn_issue<CPL>(d, a, 0, S, n_tiles, tls, descs, n);
+  dn_stage(a, S, n_tiles, tls, descs, R_rows, total_valid, L);
+
+  static_assert(kDecDnRounds == 2, "one dn_run() per round below");
+  const int n_batches = (S + kDecWaves * kDecDnRounds - 1) / (kDecWaves * kDecDnRounds);
+  for (int batch = 0; batch < n_batches; ++batch) {
+    if (batch > 0) dn_issue<CPL>(d, a, batch, S, n_tiles, tls, descs, n);
+    dn_run<MAXT, CPL>(d, 0, a, L, n);
+    dn_run<MAXT, CPL>(d, 1, a, L, n);
+  }
+  lds_barrier();
+  dn_combine(a, ppos, gw, L.yb, out, n0);
+}
+
+// ---------------------------------------------------------------------
+// The whole decode layer in one launch (bf16 activations, T * k <= 64).
+// Workgroup b routes and sorts the batch itself (as above), loads the
+// activation rows of gate/up work item b (tile, unit block), issues the
+// weight loads of that item and of down column block b together, writes
+// its h values and meets every other workgroup at a grid-wide barrier (h
+// complete); then it stages every h row and finishes the down projection
+// and the combine of its four output columns.  The W2 stream overlaps the
+// gate/up work and no second launch waits on the first.
+//
+// The barrier needs every workgroup resident at once: the launcher checks
+// the occupancy before it launches, and the wait is bounded by the
+// constant clock (an expired wait sets bit 2 of the error word and the
+// workgroup skips its down work), so every wave reaches the end.
+
+constexpr long long kBarrierTicks = 2000000;   // 20 ms at the 100 MHz constant clock
+
+struct LayerArgs {
+  const float* logits;
+  int renorm, tile_m;
+  int n_ub;        // gate/up unit blocks per tile
+  int n_gu;        // gate/up work items
+  int n_dn;        // down column blocks
+  int R_rows;      // h rows: P + n_shared * T
+  uint16_t* out;
+  uint32_t* flags; // kLayerFlags barrier flags, all equal between launches
+};
+
+// Grid-wide barrier over n <= kLayerFlags workgroups without atomics:
+// workgroup b flips the flags b, b + n, b + 2n, ... (so every launch flips
+// each flag exactly once and they are all equal again when it ends); a
+// workgroup has passed once every flag holds the flipped value.  One wave
+// polls, 16 flags per lane.  Flags and h are stored and loaded at device
+// scope (they bypass the per-XCD L2 rather than being written back or
+// invalidated there: whole-cache maintenance from hundreds of workgroups
+// costs far more than the barrier itself); every wave waits for its own h
+// stores to be acknowledged before the flags are stored, so a workgroup
+// that sees every flag flipped reads complete h.  Returns false when the
+// wait expired.
+__device__ __forceinline__ bool grid_barrier(uint32_t* flags, int n, int32_t* err,
+                                             int* ok_lds) {
+  const int tid = threadIdx.x;
+  // phase of this launch: every flag still holds the previous launch's value
+  const uint32_t target =
+      1u - __hip_atomic_load(flags + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's h stores (and loads) complete
+  lds_barrier();
+  for (int i = blockIdx.x + tid * n; i < kLayerFlags; i += kDecThreads * n)
+    __hip_atomic_store(flags + i, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < 64) {
+    const long long t0 = wall_clock64();
+    int ok = 1;
+    while (true) {
+      bool mine = true;
+#pragma unroll
+      for (int j = 0; j < kLayerFlags / 64; ++j)
+        mine &= __hip_atomic_load(flags + tid + 64 * j, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) == target;
+      if (__all(mine)) break;
+      if (wall_clock64() - t0 > kBarrierTicks) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (tid == 0) {
+      if (!ok) atomicOr(err, 4);
+      *ok_lds = ok;
+    }
+  }
+  lds_barrier();
+  return *ok_lds != 0;
+}
+
+// Chunks per lane of the one-launch kernel: 2 for gate/up (H <= 2048) and
+// down (I <= 1024); smaller K leaves slots idle.
+constexpr int kLayerCpl = 2;
+
+template <int MAXT, int NV>
+__global__ __launch_bounds__(kDecThreads, 4) void dec_layer_kernel(ProjArgs ag, ProjArgs ad,
+                                                                RouteOut ro, LayerArgs la) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int bar_ok;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = ag.K, E = ag.E, P = ag.P;
+  uint32_t* xs = reinterpret_cast<uint32_t*>(smem);                    // [MAXT][K/2]
+  float* xsum = reinterpret_cast<float*>(xs + MAXT * (K / 2));         // [MAXT][K/32]
+  moe_qmat* d13 = reinterpret_cast<moe_qmat*>(gateup_tables<MAXT>(smem, K));
+  moe_qmat* d2 = d13 + E + ag.n_shared;
+  int4* til = reinterpret_cast<int4*>(d2 + E + ad.n_shared);         // [64]
+  int* rid = reinterpret_cast<int*>(til + kFusedMaxP);               // [64]
+  float* rw = reinterpret_cast<float*>(rid + kFusedMaxP);            // [64]
+  int* srt = reinterpret_cast<int*>(rw + kFusedMaxP);                // [64]
+  int* ppos = srt + kFusedMaxP;                                      // [64]
+  int* ntl = ppos + kFusedMaxP;                                      // [4]
+  const DnLds L = dn_lds(reinterpret_cast<unsigned char*>(ntl + 4), la.R_rows, ad.ld_in);
+
+  // ---- round trip 1: both descriptor tables and the logits together;
+  // routing and sorting
+  DescCopy<1> c13, c2;
+  c13.fetch(ag);
+  c2.fetch(ad);
+  const bool writer = blockIdx.x == 0;
+  static_assert(kFusedMaxP <= 8 * kDecWaves, "every token routed in two passes");
+  route_tokens<NV, 2>(la.logits, ag.T, E, ag.k, la.renorm, lane, wave, kDecWaves,
+                      writer ? ro.ids : nullptr, writer ? ro.w : nullptr, rid, rw);
+  c13.put(d13, ag);
+  c2.put(d2, ad);
+  lds_barrier();
+  if (wave == 0)
+    wave_permute<NV>(rid, P, E, la.tile_m, srt, til, ntl, ppos, writer ? &ro : nullptr);
+  lds_barrier();
+  const int n_tiles = min(*ntl, ag.max_tiles);
+
+  // ---- gate/up work item of this workgroup (uniform over the block)
+  bool gu = (int)blockIdx.x < la.n_gu;
+  bool is_sh = false;
+  int e = 0, r_begin = 0, r_end = 0;
+  const int slot = blockIdx.x / la.n_ub, ub = blockIdx.x - slot * la.n_ub;
+  if (gu) gu = dec_tile_lds(ag, slot, n_tiles, til, is_sh, e, r_begin, r_end);
+  if (gu) gu = ub * 2 * kDecWaves < (is_sh ? ag.U_sh : ag.U);
+  moe_qmat q13;
+  int gbits = 4;
+  if (gu) {
+    q13 = d13[is_sh ? E + e : e];
+    if (!qmat_usable(q13, 2 * (is_sh ? ag.U_sh : ag.U), K)) {
+      if (tid == 0) atomicOr(ag.err, 1);
+      gu = false;
+    } else {
+      gbits = q13.bits;
+    }
+  }
+
+  // ---- round trip 2: the tile's activation rows first (their wait does
+  // not cover the weights), then every weight load of both items
+  const int nb32 = K / 32;
+  const int nt = gu ? min(MAXT, r_end - r_begin) : 0;
+  constexpr int XI = (MAXT * 64 + kDecThreads - 1) / kDecThreads;   // K <= 2048
+  uint32_t xv[XI][16];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int u = tid + i * kDecThreads;
+    if (u < nt * nb32) {
+      const int m = u / nb32, b = u - m * nb32;
+      const int row = is_sh ? r_begin + m : srt[r_begin + m] / ag.k;
+      load_a16_block(ag.in_bf16 + (size_t)row * ag.ld_in, b, xv[i]);
+    }
+  }
+  GuRows<kLayerCpl> g;
+  if (gu) gu_issue<kLayerCpl>(g, ag, is_sh, q13, ub);
+  const bool dn = (int)blockIdx.x < la.n_dn;
+  const int n0 = blockIdx.x * kDecDnCols;
+  const int n = n0 + lane / kDecDnLanes;
+  const int S = ad.n_sh_slots + n_tiles;
+  DnSlots<kLayerCpl> d;
+  if (dn) dn_issue<kLayerCpl>(d, ad, 0, S, n_tiles, til, d2, n);
+
+  // ---- gate/up + SiLU*mul of the item, h to memory
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int u = tid + i * kDecThreads;
+    if (u < nt * nb32) {
+      const int m = u / nb32, b = u - m * nb32;
+      store_a16_block(xv[i], b, K, gbits, xs + m * (K / 2), xsum + m * nb32);
+    }
+  }
+  lds_barrier();
+  if (gu) gu_compute<MAXT, kLayerCpl, true>(g, ag, is_sh, e, r_begin, nt, xs, xsum);
+
+  // ---- every h value of the layer stored
+  if (!grid_barrier(la.flags, gridDim.x, ag.err, &bar_ok) || !dn) return;
+
+  // ---- down + combine of columns n0..n0+3
+  dn_stage<true>(ad, S, n_tiles, til, d2, la.R_rows, P, L);
+  static_assert(kDecDnRounds == 2, "one dn_run() per round below");
+  const int n_batches = (S + kDecWaves * kDecDnRounds - 1) / (kDecWaves * kDecDnRounds);
+  for (int batch = 0; batch < n_batches; ++batch) {
+    if (batch > 0) dn_issue<kLayerCpl>(d, ad, batch, S, n_tiles, til, d2, n);
+    dn_run<MAXT, kLayerCpl>(d, 0, ad, L, n);
+    dn_run<MAXT, kLayerCpl>(d, 1, ad, L, n);
+  }
+  lds_barrier();
+  dn_combine(ad, ppos, rw, L.yb, la.out, n0);
 }
 
 // ---------------------------------------------------------------------
@@ -571,9 +892,9 @@ bool dec_gateup_ok(int T, int H, int tile_m) {
 
 size_t dec_down_lds(int T, int k, int E, int n_shared, int max_tiles, int ld) {
   const size_t P = (size_t)T * k, R_rows = P + (size_t)n_shared * T;
-  const size_t meta = ((size_t)max_tiles * 16 + (size_t)(E + n_shared) * 32 + P * 8 +
-                       R_rows * 4 + 15) / 16 * 16;
-  return meta + R_rows * ((size_t)ld * 2 + (size_t)(ld / 32) * 4 + kDecDnCols * 4);
+  const size_t meta = ((size_t)max_tiles * 16 + (size_t)(E + n_shared) * 32 + P * 8 + 15) / 16 * 16;
+  return meta + (R_rows * 4 + 15) / 16 * 16 +
+         R_rows * ((size_t)ld * 2 + (size_t)(ld / 32) * 4 + kDecDnCols * 4);
 }
 
 bool dec_down_ok(int T, int k, int E, int n_shared, int H, int I, int I_shared, int ld,
@@ -700,6 +1021,140 @@ hipError_t launch_dec_down_combine(const ProjArgs& a_in, uint16_t* out, hipStrea
     case 8: return dn_cpl<8>(a, 2, grid, lds, R_rows, out, st);   // the 1-chunk form spills
     default: return dn_cpl<16>(a, 2, grid, lds, R_rows, out, st);
   }
+}
+
+// One-launch layer: eligibility, LDS and grid.
+bool dec_layer_ok(int T, int H, int I, int I_shared, int E, int k, int n_shared, int tile_m,
+                  int max_tiles, int ld_h) {
+  const int Kd = n_shared > 0 && I_shared > I ? I_shared : I;
+  return E <= 128 && dec_route_gateup_ok(T, H, E, k, tile_m) &&
+         dec_cpl(H, kDecGuLanes) <= kLayerCpl &&
+         dec_cpl(Kd, kDecDnLanes) != 0 && dec_cpl(Kd, kDecDnLanes) <= kLayerCpl &&
+         dec_down_ok(T, k, E, n_shared, H, I, I_shared, ld_h, tile_m, max_tiles) &&
+         max_tiles <= kFusedMaxP;
+}
+
+static size_t dec_layer_lds(int T, int k, int E, int n_shared, int K, int maxt, int ld_h) {
+  const size_t P = (size_t)T * k, R = P + (size_t)n_shared * T;
+  size_t lds = ((size_t)maxt * K * 2 + (size_t)maxt * (K / 32) * 4 + 15) / 16 * 16;
+  lds += 2 * (size_t)(E + n_shared) * sizeof(moe_qmat);
+  lds += (size_t)kFusedMaxP * 16 + 4 * (size_t)kFusedMaxP * 4 + 16;
+  lds += (R * 4 + 15) / 16 * 16 + R * ((size_t)ld_h * 2 + (size_t)(ld_h / 32) * 4 + kDecDnCols * 4);
+  return lds;
+}
+
+// Workgroups of kernel f (dynamic LDS lds) resident on one CU of the
+// current device, and the device's CU count; both cached.
+static bool resident_capacity(const void* f, size_t lds, long long& cap) {
+  struct Entry {
+    const void* f;
+    size_t lds;
+    int dev;
+    long long cap;
+  };
+  static Entry cache[64];
+  static int n_cache = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n_cache; ++i)
+    if (cache[i].f == f && cache[i].lds == lds && cache[i].dev == dev) {
+      cap = cache[i].cap;
+      return true;
+    }
+  int nb = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, kDecThreads, lds) != hipSuccess)
+    return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  cap = (long long)nb * cus;
+  if (n_cache < 64) cache[n_cache++] = Entry{f, lds, dev, cap};
+  return true;
+}
+
+// The kernel instance of a shape: rows per tile pass, and one or two
+// logits per lane (E <= 128: wider routing does not fit the registers of
+// four waves per SIMD).
+template <int MAXT>
+static const void* layer_fn_nv(int E) {
+  return E <= 64 ? reinterpret_cast<const void*>(&dec_layer_kernel<MAXT, 1>)
+                 : reinterpret_cast<const void*>(&dec_layer_kernel<MAXT, 2>);
+}
+static const void* layer_fn(int maxt, int E) {
+  switch (maxt) {
+    case 1: return layer_fn_nv<1>(E);
+    case 2: return layer_fn_nv<2>(E);
+    case 4: return layer_fn_nv<4>(E);
+    case 8: return layer_fn_nv<8>(E);
+    default: return layer_fn_nv<16>(E);
+  }
+}
+
+// Grid, LDS and residency of the one-launch layer for a shape.
+struct LayerPlan {
+  int n_ub, n_gu, n_dn, grid;
+  size_t lds;
+  const void* fn;
+  bool resident;
+};
+static LayerPlan layer_plan(int T, int H, int I, int I_shared, int E, int k, int n_shared,
+                            int tile_m, int max_tiles, int ld_h) {
+  LayerPlan p{};
+  const int maxt = dec_maxt(T, tile_m);
+  const int n_sh_slots = n_shared * ((T + maxt - 1) / maxt);
+  const int Umax = max(I, n_shared > 0 ? I_shared : 0);
+  p.n_ub = (Umax + 2 * kDecWaves - 1) / (2 * kDecWaves);
+  p.n_gu = (n_sh_slots + max_tiles) * p.n_ub;
+  p.n_dn = H / kDecDnCols;
+  p.grid = max(p.n_gu, p.n_dn);
+  p.lds = dec_layer_lds(T, k, E, n_shared, H, maxt, ld_h);
+  p.fn = layer_fn(maxt, E);
+  long long cap = 0;
+  p.resident = p.grid > 0 && p.grid <= kLayerFlags && p.lds <= 160 * 1024 &&
+               resident_capacity(p.fn, p.lds, cap) && cap >= p.grid;
+  return p;
+}
+
+int dec_layer_one_launch(int T, int H, int I, int I_shared, int E, int k, int n_shared,
+                         int tile_m, int max_tiles, int ld_h) {
+  if (!dec_layer_ok(T, H, I, I_shared, E, k, n_shared, tile_m, max_tiles, ld_h)) return 0;
+  return layer_plan(T, H, I, I_shared, E, k, n_shared, tile_m, max_tiles, ld_h).resident ? 1 : 0;
+}
+
+hipError_t launch_dec_layer(const ProjArgs& ag_in, const ProjArgs& ad_in, const float* logits,
+                            int renorm, int tile_m, int32_t* ids, float* w, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                            int32_t* tiles, int32_t* n_tiles, uint16_t* out, uint32_t* flags,
+                            bool& launched, hipStream_t st) {
+  launched = false;
+  ProjArgs ag = ag_in, ad = ad_in;
+  if (ag.P > kFusedMaxP || ag.E > 128 || ag.max_tiles > kFusedMaxP || ad.U % kDecDnCols != 0 ||
+      ag.maxt != dec_maxt(ag.T, tile_m))
+    return hipErrorInvalidValue;
+  const LayerPlan p = layer_plan(ag.T, ag.K, ad.K, ag.U_sh, ag.E, ag.k, ag.n_shared, tile_m,
+                                 ag.max_tiles, ad.ld_in);
+  if (!p.resident) return hipSuccess;
+  for (ProjArgs* a : {&ag, &ad}) {
+    a->sh_tile = a->maxt;
+    a->n_sh_slots = a->n_shared * ((a->T + a->sh_tile - 1) / a->sh_tile);
+  }
+  LayerArgs la;
+  la.logits = logits;
+  la.renorm = renorm;
+  la.tile_m = tile_m;
+  la.n_ub = p.n_ub;
+  la.n_gu = p.n_gu;
+  la.n_dn = p.n_dn;
+  la.R_rows = ag.P + ag.n_shared * ag.T;
+  la.out = out;
+  la.flags = flags;
+  RouteOut ro{ids, w, counts, offsets, sorted_pair, pair_pos, tiles, n_tiles};
+  void* args[] = {&ag, &ad, &ro, &la};
+  const hipError_t e = hipLaunchKernel(p.fn, dim3((unsigned)p.grid), dim3(kDecThreads), args,
+                                       p.lds, st);
+  launched = e == hipSuccess;
+  return e;
 }
 
 }  // namespace moe

@@ -14,9 +14,9 @@ namespace moe {
 // ascending).  The order is carried by one 64-bit key per candidate: the
 // value mapped monotonically to 32 bits (-0 taken as +0) above the inverted
 // index, so one unsigned compare decides, and taken or absent candidates
-// have key 0.  Gate weights: exp(l_j - l_max) over their sum in selection
-// order (softmax over the chosen logits), or over all E logits
-// (renormalize = 0; per-lane sums added across the group).  The r-th choice
+// have key 0.  Gate weights: exp(l_j - l_max) over their sum (softmax over
+// the chosen logits), or over all E logits (renormalize = 0); the sums are
+// per-lane sums added across the group, the same in every lane.  The r-th choice
 // (r < k) goes to ids_out[r] / w_out[r] (global, skipped when null) and to
 // lds_ids[r] / lds_w[r] (skipped when null).
 __device__ __forceinline__ uint32_t route_ord(float v) {
@@ -61,11 +61,11 @@ __device__ __forceinline__ void route_group_vals(const float (&v)[NVV], int E, i
     key_hi[j] = route_ord(v[j]);
     if (r + LANES * j >= E) taken |= 1u << j;
   }
-  float top = 0.0f, denom = 0.0f;
-  float sel_ex[NVV];
+  float top = 0.0f;
+  float sel_v[NVV];
   int sel_id[NVV];
 #pragma unroll
-  for (int j = 0; j < NVV; ++j) { sel_ex[j] = 0.0f; sel_id[j] = 0; }
+  for (int j = 0; j < NVV; ++j) { sel_v[j] = 0.0f; sel_id[j] = 0; }
   for (int rr = 0; rr < k; ++rr) {
     uint32_t hi = 0, lo = 0;
 #pragma unroll
@@ -93,12 +93,19 @@ __device__ __forceinline__ void route_group_vals(const float (&v)[NVV], int E, i
     const float bv = route_unord(hi);
     if (bi % LANES == r) taken |= 1u << (bi / LANES);
     if (rr == 0) top = bv;
-    const float ex = expf(bv - top);
-    denom += ex;
 #pragma unroll
     for (int j = 0; j < NVV; ++j)
-      if (rr == r + LANES * j) { sel_ex[j] = ex; sel_id[j] = bi; }
+      if (rr == r + LANES * j) { sel_v[j] = bv; sel_id[j] = bi; }
   }
+  // gate numerators of this lane's choices, all lanes at once (not one
+  // exponential per round), and their sum over the group
+  float sel_ex[NVV], part = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NVV; ++j) {
+    sel_ex[j] = r + LANES * j < k ? expf(sel_v[j] - top) : 0.0f;
+    part += sel_ex[j];
+  }
+  float denom = LANES == 64 ? wave_sum(part) : group_sum(part, 16);
   if (!renorm) {
     float sm = 0.0f;
 #pragma unroll

@@ -139,11 +139,24 @@ def fused_routing_ok(T, E, k) -> bool:
 
 
 def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
-              flags: int = 0, stream=None, fused: bool = True) -> None:
+              flags: int = 0, stream=None, fused: bool = True,
+              one_call: bool = True) -> None:
     """One layer step: route, permute, gate/up + SiLU*mul, down + combine.
-    With ``fused`` the first three go through moe_w4_route_gateup_silu (one
-    launch for decode batches, else the separate calls)."""
+    With ``fused`` and ``one_call`` the whole step is moe_w4_layer (with
+    MOE_LAYER_ONE_LAUNCH in ``flags``: one launch for small bf16 decode
+    batches); with ``fused`` alone the first three go through
+    moe_w4_route_gateup_silu and the rest through moe_w4_down_combine;
+    otherwise every call is issued separately."""
     T, H, I, E, k = B.T, B.H, B.I, B.E, B.k
+    if not (fused and one_call):
+        flags &= ~L.MOE_LAYER_ONE_LAUNCH   # only moe_w4_layer takes it
+    if fused and one_call:
+        L.moe_w4_layer(B.act, logits, x, T, H, I, E, k, renormalize, bank.w13,
+                       bank.w2, bank.w13_sh, bank.w2_sh, B.n_shared, B.I_shared,
+                       B.tile_m, B.ids, B.w, B.counts, B.offsets, B.sorted_pair,
+                       B.pair_pos, B.tiles, B.n_tiles, B.h, B.out, B.ws,
+                       B.ws_bytes, flags, stream)
+        return
     if fused:
         L.moe_w4_route_gateup_silu(B.act, logits, x, T, H, I, E, k, renormalize,
                                    bank.w13, bank.w13_sh, B.n_shared, B.I_shared,
@@ -198,6 +211,7 @@ class DeviceLayer:
         return LayerBuffers(c.T, c.H, c.I, c.E, c.k, c.n_shared, c.I_shared, a,
                             tile_m, self.x.device)
 
-    def run(self, B: LayerBuffers, flags: int = 0, stream=None, fused: bool = True) -> None:
+    def run(self, B: LayerBuffers, flags: int = 0, stream=None, fused: bool = True,
+            one_call: bool = True) -> None:
         run_layer(self.bank, self.x, self.logits, B, self.cfg.renormalize,
-                  flags, stream, fused)
+                  flags, stream, fused, one_call)

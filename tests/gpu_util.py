@@ -20,11 +20,12 @@ def bf16_bits_to_f64(u16):
     return u.view(np.float32).astype(np.float64)
 
 
-def run_layer_gpu(dl, act=None, tile_m=None, flags=0, stream=None, fused=True):
+def run_layer_gpu(dl, act=None, tile_m=None, flags=0, stream=None, fused=True,
+                  one_call=True):
     """Run one layer step on the device; returns host copies of everything."""
     torch = torch_mod()
     B = dl.buffers(act, tile_m)
-    dl.run(B, flags, stream, fused)
+    dl.run(B, flags, stream, fused, one_call)
     torch.cuda.synchronize()
     return collect(B), B
 

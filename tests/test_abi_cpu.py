@@ -54,24 +54,26 @@ def up256(n):
 
 
 def test_workspace_sizes():
-    # error word + fp32 y rows (+ int8 x and fp32 scales for A8) (+ fp16
-    # activation copies for the A16 matrix core path when H, I, I_shared are
-    # multiples of 128), each region 256-byte aligned
+    # header (error word, then the one-launch layer's 1024 barrier flags) +
+    # fp32 y rows (+ int8 x and fp32 scales for A8) (+ fp16 activation copies
+    # for the A16 matrix core path when H, I, I_shared are multiples of 128),
+    # each region 256-byte aligned
+    HDR = 256 + 1024 * 4
     a16 = up256(max(2 * 1 * 2048 * 2, 9 * 768 * 2))
     assert L.moe_workspace_bytes(0, 1, 2048, 768, 128, 8, 1, 768) == \
-        256 + 9 * 2048 * 4 + a16
+        HDR + 9 * 2048 * 4 + a16
     # A8: int8 x + scales, then int8 h rows (stride max(I, I_shared)) + scales
     a8 = L.moe_workspace_bytes(1, 64, 2048, 768, 128, 8, 0, 0)
-    assert a8 == 256 + 64 * 2048 + 256 + 512 * 768 + 512 * 4 + 512 * 2048 * 4
+    assert a8 == HDR + 64 * 2048 + 256 + 512 * 768 + 512 * 4 + 512 * 2048 * 4
     a8 = L.moe_workspace_bytes(1, 3, 512, 256, 8, 2, 1, 384)
-    assert a8 == 256 + up256(3 * 512) + 256 + up256(9 * 384) + 256 + up256(9 * 512 * 4)
-    assert L.moe_workspace_bytes(0, 0, 2048, 768, 128, 8, 0, 0) == 256
+    assert a8 == HDR + up256(3 * 512) + 256 + up256(9 * 384) + 256 + up256(9 * 512 * 4)
+    assert L.moe_workspace_bytes(0, 0, 2048, 768, 128, 8, 0, 0) == HDR
     # no matrix-core copies when a dimension is not a multiple of 128
-    assert L.moe_workspace_bytes(0, 4, 256, 96, 8, 2, 0, 0) == 256 + up256(8 * 256 * 4)
+    assert L.moe_workspace_bytes(0, 4, 256, 96, 8, 2, 0, 0) == HDR + up256(8 * 256 * 4)
     # shared expert wider than the routed ones sets the h stride
     a16 = up256(max(2 * 3 * 512 * 2, 3 * (2 + 1) * 384 * 2))
     assert L.moe_workspace_bytes(0, 3, 512, 256, 8, 2, 1, 384) == \
-        256 + up256(3 * 3 * 512 * 4) + a16
+        HDR + up256(3 * 3 * 512 * 4) + a16
 
 
 FAKE = 1 << 20   # a non-null pointer value; never dereferenced on the host
@@ -187,3 +189,38 @@ def test_route_permute_validation():
     assert call(tile_m=0) == L.MOE_E_INVAL
     assert call(topk_w=None) == L.MOE_E_INVAL
     assert call() == L.MOE_E_DEVICE
+
+
+def test_layer_validation():
+    """moe_w4_layer checks its arguments on the host: the one-launch shape
+    (bf16 decode batch) and a shape that takes the two-call form."""
+    ok = dict(act=0, logits=FAKE, x=FAKE, T=1, H=2048, I=768, E=128, k=8, renormalize=1,
+              w13=FAKE, w2=FAKE, w13_shared=FAKE, w2_shared=FAKE, n_shared=1,
+              I_shared=768, tile_m=16, topk_ids=FAKE, topk_w=FAKE, counts=FAKE,
+              offsets=FAKE, sorted_pair=FAKE, pair_pos=FAKE, tiles=FAKE, n_tiles=FAKE,
+              h=FAKE, out=FAKE, workspace=FAKE, ws_bytes=1 << 30, flags=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_w4_layer(*a.values(), stream=0, check=False)
+    assert call(renormalize=2) == L.MOE_E_INVAL
+    assert call(act=2) == L.MOE_E_INVAL
+    assert call(k=129) == L.MOE_E_INVAL
+    assert call(flags=16) == L.MOE_E_INVAL
+    assert call(out=None) == L.MOE_E_INVAL
+    assert call(w2_shared=None) == L.MOE_E_INVAL
+    assert call(workspace=None) == L.MOE_E_WORKSPACE
+    assert call(ws_bytes=64) == L.MOE_E_WORKSPACE
+    assert call(H=2047) == L.MOE_E_UNSUPPORTED
+    # valid arguments reach the device check (no GPU here), for the two-call
+    # form and the one-launch form alike
+    assert call() == L.MOE_E_DEVICE
+    assert call(flags=L.MOE_LAYER_ONE_LAUNCH) == L.MOE_E_DEVICE
+    assert call(T=64, act=1, n_shared=0) == L.MOE_E_DEVICE
+    q = L.moe_w4_layer_one_launch
+    one = L.MOE_LAYER_ONE_LAUNCH
+    assert q(0, 1, 2048, 768, 128, 8, 1, 768, 16, one) == L.MOE_E_DEVICE   # needs the device
+    assert q(0, 1, 2048, 768, 128, 8, 1, 768, 16, 0) == 0                  # default: two calls
+    assert q(1, 64, 2048, 768, 128, 8, 0, 0, 16, one) == 0                 # A8: two calls
+    assert q(0, 1, 2048, 768, 256, 8, 1, 768, 16, one) == 0                # E > 128
+    assert q(2, 1, 2048, 768, 128, 8, 1, 768, 16, 0) == L.MOE_E_INVAL

@@ -276,20 +276,68 @@ def test_fused_route_permute_matches_separate_calls():
         assert np.array_equal(outs[0][6][:, :3], o["tiles"])
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "e288", "k1", "mixed_shared", "norenorm"])
+@pytest.mark.parametrize("name", ["c0", "c1", "e288", "k1", "mixed_shared", "norenorm",
+                                  "kE", "e1"])
 def test_fused_route_gateup_matches_separate_calls(name):
-    """moe_w4_route_gateup_silu (one launch for decode batches) writes the
-    same routing tables and the same h, bit for bit, as moe_route_permute /
-    moe_route_topk + moe_permute followed by moe_w4_gateup_silu."""
+    """moe_w4_layer (one launch for bf16 decode batches) and
+    moe_w4_route_gateup_silu + moe_w4_down_combine write the same routing
+    tables, the same h and the same output, bit for bit, as the separate
+    calls (moe_route_permute / moe_route_topk + moe_permute, gate/up, down)."""
+    from packed_bit_grouped_amd import _lib as L
     cfg = {"c0": LAYERS["tiny_w4a16"], "c1": LAYERS["decode_w4a16_t1"], **MINIS}[name]
     dl = _dev(cfg)
-    g1, _ = run_layer_gpu(dl, "a16", 16, fused=True)
+    one = L.MOE_LAYER_ONE_LAUNCH
+    expect_one = name not in ("e288",)
+    assert L.moe_w4_layer_one_launch(0, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.n_shared,
+                                     cfg.I_shared, 16, one) == int(expect_one)
+    g0, B0 = run_layer_gpu(dl, "a16", 16, flags=one, fused=True, one_call=True)
+    g3, _ = run_layer_gpu(dl, "a16", 16, fused=True, one_call=True)
+    g1, _ = run_layer_gpu(dl, "a16", 16, fused=True, one_call=False)
     g2, _ = run_layer_gpu(dl, "a16", 16, fused=False)
-    for key in ("ids", "w", "counts", "offsets", "sorted_pair", "pair_pos", "tiles",
-                "n_tiles", "out"):
-        assert np.array_equal(g1[key], g2[key]), key
-    assert np.array_equal(_valid_h(g1["h"], cfg), _valid_h(g2["h"], cfg))
-    assert g1["err"] == 0
+    for g in (g0, g1, g3):
+        for key in ("ids", "w", "counts", "offsets", "sorted_pair", "pair_pos", "tiles",
+                    "n_tiles", "out"):
+            assert np.array_equal(g[key], g2[key]), key
+        assert np.array_equal(_valid_h(g["h"], cfg), _valid_h(g2["h"], cfg))
+        assert g["err"] == 0
+    # the error word is clear and the grid-wide barrier's flags are all equal
+    hdr = to_np(B0.ws[:4352].view(torch_mod().int32))
+    assert hdr[0] == 0 and len(set(hdr[64:].tolist())) == 1
+
+
+def test_layer_one_launch_repeated_and_mixed_shapes():
+    """Back-to-back one-launch layers on one workspace and stream (every
+    launch leaves the barrier flags equal), interleaved with another shape
+    of another grid size, each bit-identical to its two-call form."""
+    torch = torch_mod()
+    cfgs = [LAYERS["decode_w4a16_t1"], MINIS["mixed_shared"]]
+    dls = [_dev(c) for c in cfgs]
+    refs = [run_layer_gpu(d, "a16", 16, fused=False)[0] for d in dls]
+    ws = None
+    bufs = []
+    for d, c in zip(dls, cfgs):
+        B = d.buffers("a16", 16)
+        if ws is None or B.ws_bytes > ws.numel():
+            ws = torch.zeros(max(B.ws_bytes, ws.numel() if ws is not None else 0),
+                             dtype=torch.uint8, device="cuda")
+        bufs.append(B)
+    for B in bufs:
+        B.ws, B.ws_bytes = ws, ws.numel()
+    from packed_bit_grouped_amd import _lib as L
+    for d, c in zip(dls, cfgs):
+        assert L.moe_w4_layer_one_launch(0, c.T, c.H, c.I, c.E, c.k, c.n_shared, c.I_shared,
+                                         16, L.MOE_LAYER_ONE_LAUNCH) == 1
+    for rep in range(6):
+        i = rep % 2
+        dls[i].run(bufs[i], L.MOE_LAYER_ONE_LAUNCH)
+        if rep % 3 == 2:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    for d, B, ref in zip(dls, bufs, refs):
+        got = collect(B)
+        assert np.array_equal(got["out"], ref["out"])
+    hdr = to_np(ws[:4352].view(torch.int32))
+    assert hdr[0] == 0 and len(set(hdr[64:].tolist())) == 1
 
 
 def test_permute_skips_out_of_range_ids():
@@ -451,21 +499,24 @@ def test_repeat_bitwise_identical():
     assert np.array_equal(g3["out"], g4["out"])
 
 
-@pytest.mark.parametrize("name", ["c1", "mixed_shared", "mfma_mixed"])
-def test_graph_replay_matches_eager(name):
-    """The whole step captured in a HIP graph (decode, split-K GEMV and
-    matrix-core forms): every replay, with eager work and synchronizations
-    in between, reproduces the eager step bit for bit."""
+@pytest.mark.parametrize("name,one", [("c1", False), ("c1", True), ("mixed_shared", False),
+                                      ("mixed_shared", True), ("mfma_mixed", False)])
+def test_graph_replay_matches_eager(name, one):
+    """The whole step captured in a HIP graph (decode, one-launch layer,
+    split-K GEMV and matrix-core forms): every replay, with eager work and
+    synchronizations in between, reproduces the eager step bit for bit."""
     torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    fl = L.MOE_LAYER_ONE_LAUNCH if one else 0
     cfg = {"c1": LAYERS["decode_w4a16_t1"], **MINIS, **MFMA}[name]
     dl = _dev(cfg)
     B = dl.buffers()
-    dl.run(B, 0)
+    dl.run(B, fl)
     torch.cuda.synchronize()
     ref = collect(B)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        dl.run(B, 0)
+        dl.run(B, fl)
     for rep in range(3):
         B.out.zero_()
         B.h.zero_()
@@ -477,7 +528,7 @@ def test_graph_replay_matches_eager(name):
         for key in ("ids", "counts", "offsets", "sorted_pair", "pair_pos", "tiles", "out"):
             assert np.array_equal(got[key], ref[key]), (rep, key)
         assert np.array_equal(_valid_h(got["h"], cfg), _valid_h(ref["h"], cfg)), (rep, "h")
-        dl.run(B, 0)
+        dl.run(B, fl)
         torch.cuda.synchronize()
 
 
