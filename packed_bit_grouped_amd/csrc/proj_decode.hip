@@ -42,6 +42,16 @@ constexpr int kDecDnCols = 64 / kDecDnLanes;   // output columns per workgroup
 constexpr int kDecDnRounds = 2;   // tiles per wave with loads in flight together
 constexpr int kDecSortedLds = 2048;   // pairs whose sorted list is copied to LDS
 
+// Kernel arguments live in memory and reach the scalar cache one 64-byte
+// line at a time; the compiler reads a field where it is first used, so a
+// line first touched in the middle of a kernel costs a memory round trip
+// there.  These read one field of every line of the argument block at the
+// start, where the first loads of the kernel wait anyway.
+__device__ __forceinline__ void touch_args(const ProjArgs& a) {
+  // lines at 0, 64, 128 and 192 bytes of the 224-byte block
+  __asm__ volatile("" ::"s"(a.mode), "s"(a.K), "s"(a.n_tiles), "s"(a.topk_w));
+}
+
 // Tile of slot `slot`: shared slots first (tokens [ti*sh_tile, ...)), then
 // the routed tiles of the permutation.  Returns false for slots past the
 // device-side tile count.
@@ -267,6 +277,7 @@ __device__ __forceinline__ unsigned char* gateup_tables(unsigned char* smem, int
 template <int MAXT, int CPL>
 __global__ __launch_bounds__(kDecThreads) void dec_gateup_kernel(ProjArgs a, int n_ub) {
   extern __shared__ __align__(16) unsigned char smem[];
+  touch_args(a);
   const int tid = threadIdx.x;
   const int slot = blockIdx.x / n_ub, ub = blockIdx.x - slot * n_ub;
   const int K = a.K;
@@ -341,64 +352,89 @@ struct RouteOut {
 constexpr int kFusedMaxP = 64;
 
 // Stable counting sort of P <= 64 pairs by expert with one wave (lane p
-// holds pair p), by direct counting over the pairs with lane reads: sorted
-// position = pairs of a smaller expert + earlier pairs of the same expert;
-// a pair starts a tile when its rank inside its expert is a multiple of
-// tile_m, and the tile's index is the number of starts before it.  The
-// same outputs as the block-wide sort of the routing kernels.
+// holds pair p; expert ids below 2^kPermIdBits).  One radix pass over the
+// id bits with ballots gives each pair the set of pairs sorted before it
+// (a smaller expert, or the same expert and a smaller pair index); its
+// position is that set's size.  A pair starts a tile when its rank inside
+// its expert is a multiple of tile_m, and the tile's index is the number
+// of tile starts sorted before it.  Straight-line lane-mask arithmetic: a
+// loop over the pairs with lane reads costs about a microsecond of
+// dependent instructions in a single wave.  The same outputs as the
+// block-wide sort of the routing kernels; the writer's per-expert counts
+// and offsets come from wave_counts.
 template <int NV>
 __device__ void wave_permute(const int* ids, int P, int E, int tile_m, int* srt_l, int4* til_l,
                              int* ntl_l, int* ppos_l, const RouteOut* ro) {
   const int lane = threadIdx.x & 63;
   const bool in = lane < P;
-  const int ep = in ? ids[lane] : 0x7fffffff;
-  int lt = 0, same = 0, before = 0;
-  for (int q = 0; q < P; ++q) {
-    const int eq = __builtin_amdgcn_readlane(ep, q);
-    lt += eq < ep;
-    same += eq == ep;
-    before += (eq == ep) & (q < lane);
+  const int ep = in ? ids[lane] : 0;
+  // eq: valid pairs whose id agrees with mine on the bits seen so far;
+  // lt: pairs already known to have a smaller id
+  uint64_t eq = __ballot(in), lt = 0;
+#pragma unroll
+  for (int b = kPermIdBits - 1; b >= 0; --b) {
+    const bool bit = (ep >> b) & 1;
+    const uint64_t ones = __ballot(in && bit);
+    lt = bit ? (lt | (eq & ~ones)) : lt;
+    eq = bit ? (eq & ones) : (eq & ~ones);
   }
-  const int pos = lt + before;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));   // lanes < lane
+  const uint64_t ahead = lt | (eq & below);                           // sorted before me
+  const int n_lt = __popcll(lt), same = __popcll(eq), before = __popcll(eq & below);
+  const int pos = n_lt + before;
   const bool start = in && before % tile_m == 0;
-  int tidx = 0;
-  for (int q = 0; q < P; ++q) {
-    const int sq = __builtin_amdgcn_readlane((int)start, q);
-    const int pq = __builtin_amdgcn_readlane(pos, q);
-    tidx += sq & (pq < pos);
-  }
-  const int n_tiles = __popcll(__ballot(start));
+  const uint64_t starts = __ballot(start);
+  const int tidx = __popcll(starts & ahead);
+  const int n_tiles = __popcll(starts);
+  const int4 tile = make_int4(ep, pos, min(pos + tile_m, n_lt + same), 0);
   if (in) srt_l[pos] = lane;
   if (in && ppos_l) ppos_l[lane] = pos;
-  if (start) til_l[tidx] = make_int4(ep, pos, min(pos + tile_m, lt + same), 0);
+  if (start) til_l[tidx] = tile;
   if (lane == 0) *ntl_l = n_tiles;
   if (ro) {
     if (in) {
       ro->sorted_pair[pos] = lane;
       ro->pair_pos[lane] = pos;
     }
-    if (start)
-      reinterpret_cast<int4*>(ro->tiles)[tidx] =
-          make_int4(ep, pos, min(pos + tile_m, lt + same), 0);
+    if (start) reinterpret_cast<int4*>(ro->tiles)[tidx] = tile;
     if (lane == 0) {
       *ro->n_tiles = n_tiles;
       ro->offsets[E] = P;
     }
-    // counts and offsets of every expert
-#pragma unroll
-    for (int jv = 0; jv < NV; ++jv) {
-      const int ex = lane + 64 * jv;
-      int c = 0, o = 0;
-      for (int q = 0; q < P; ++q) {
-        const int eq = __builtin_amdgcn_readlane(ep, q);
-        c += eq == ex;
-        o += eq < ex;
-      }
-      if (ex < E) {
-        ro->counts[ex] = c;
-        ro->offsets[ex] = o;
-      }
-    }
+  }
+}
+
+// Per-expert pair counts and offsets (pairs of a smaller expert) of the
+// experts [64 j, 64 j + 64), by one wave reading the ids from LDS; run by
+// the writer workgroup's otherwise idle waves while wave 0 sorts.
+__device__ void wave_counts(const int* ids, int P, int E, int j, const RouteOut& ro) {
+  const int ex = (threadIdx.x & 63) + 64 * j;
+  int c = 0, o = 0;
+  for (int q = 0; q < P; ++q) {
+    const int eq = ids[q];
+    c += eq == ex;
+    o += eq < ex;
+  }
+  if (ex < E) {
+    ro.counts[ex] = c;
+    ro.offsets[ex] = o;
+  }
+}
+
+// The sort and, in the writer workgroup, the counts: wave 0 sorts, waves
+// 1.. count experts [64 (w - 1), 64 w); experts past the waves' reach are
+// counted by wave 0 after its sort.
+template <int NV>
+__device__ __forceinline__ void block_permute(const int* ids, int P, int E, int tile_m, int* srt_l,
+                                              int4* til_l, int* ntl_l, int* ppos_l, bool writer,
+                                              const RouteOut& ro) {
+  const int wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    wave_permute<NV>(ids, P, E, tile_m, srt_l, til_l, ntl_l, ppos_l, writer ? &ro : nullptr);
+    if (writer)
+      for (int j = kDecWaves - 1; j < NV; ++j) wave_counts(ids, P, E, j, ro);
+  } else if (writer && wave - 1 < NV) {
+    wave_counts(ids, P, E, wave - 1, ro);
   }
 }
 
@@ -408,6 +444,9 @@ __global__ __launch_bounds__(kDecThreads) void dec_route_gateup_kernel(ProjArgs 
                                                                        const float* logits,
                                                                        int renorm, int tile_m) {
   extern __shared__ __align__(16) unsigned char smem[];
+  // the argument block: ProjArgs, then the routing outputs and scalars
+  touch_args(a);
+  __asm__ volatile("" ::"s"(ro.sorted_pair), "s"(logits));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = blockIdx.x / n_ub, ub = blockIdx.x - slot * n_ub;
   const int K = a.K, E = a.E, P = a.P;
@@ -429,7 +468,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_route_gateup_kernel(ProjArgs 
                       writer ? ro.ids : nullptr, writer ? ro.w : nullptr, rid, rw);
   dc.put(descs, a);
   lds_barrier();
-  if (wave == 0) wave_permute<NV>(rid, P, E, tile_m, srt, til, ntl, nullptr, writer ? &ro : nullptr);
+  block_permute<NV>(rid, P, E, tile_m, srt, til, ntl, nullptr, writer, ro);
   lds_barrier();
 
   bool is_sh;
@@ -634,6 +673,7 @@ template <int MAXT, int CPL>
 __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs a, int R_rows,
                                                                        uint16_t* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char smem[];
+  touch_args(a);
   // LDS: tile list, descriptor tables, pair positions and gate weights
   // first (16-byte aligned), then the down part's rows
   int4* tls = reinterpret_cast<int4*>(smem);                             // [max_tiles]
@@ -766,6 +806,10 @@ __global__ __launch_bounds__(kDecThreads, 4) void dec_layer_kernel(ProjArgs ag, 
                                                                 RouteOut ro, LayerArgs la) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int bar_ok;
+  // the argument block: both ProjArgs, the routing outputs, LayerArgs
+  touch_args(ag);
+  touch_args(ad);
+  __asm__ volatile("" ::"s"(ro.ids), "s"(ro.n_tiles), "s"(la.logits), "s"(la.flags));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = ag.K, E = ag.E, P = ag.P;
   uint32_t* xs = reinterpret_cast<uint32_t*>(smem);                    // [MAXT][K/2]
@@ -792,8 +836,7 @@ __global__ __launch_bounds__(kDecThreads, 4) void dec_layer_kernel(ProjArgs ag, 
   c13.put(d13, ag);
   c2.put(d2, ad);
   lds_barrier();
-  if (wave == 0)
-    wave_permute<NV>(rid, P, E, la.tile_m, srt, til, ntl, ppos, writer ? &ro : nullptr);
+  block_permute<NV>(rid, P, E, la.tile_m, srt, til, ntl, ppos, writer, ro);
   lds_barrier();
   const int n_tiles = min(*ntl, ag.max_tiles);
 
