@@ -9,6 +9,9 @@ need no GPU):
 
 * unpack / decode_bf16 / decode_fp16: hand-written byte and bit-pattern
   fixtures (tests/golden) and a round trip through the generator's packer.
+* router_logits: pure-Python sums on small inputs; a one-hot token gives
+  the router row exactly; scaling x by 2^m scales the logits exactly; the
+  prior adds per expert.
 * route_topk: numpy's stable argsort and scipy's softmax; sum-to-one;
   k = E equals a full softmax; pure-Python brute force.
 * permute: numpy bincount / cumsum / stable argsort; inverse identity.

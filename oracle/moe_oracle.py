@@ -26,7 +26,7 @@ import numpy as np
 
 __all__ = [
     "decode_bf16", "decode_fp16", "unpack_codes", "dequantize",
-    "route_topk", "permute", "quant_rows_a8", "silu", "round_to_bf16",
+    "router_logits", "route_topk", "permute", "quant_rows_a8", "silu", "round_to_bf16",
     "x_float", "expert_rows", "gateup_a16", "gateup_a8", "down_a16",
     "down_a8", "a8_group_partials", "combine", "oracle_layer",
     "oracle_token_outputs", "touched_experts",
@@ -115,6 +115,27 @@ def x_float(x_bf16) -> np.ndarray:
 # moved out of Python -- sections "Keep low-bit weights packed ..." and
 # "Remove sync and launch overhead from the token loop")
 # --------------------------------------------------------------------------
+
+def router_logits(x_bf16, router_w, bias=None) -> np.ndarray:
+    """Router logits of every token: the dot product of the token's
+    activations with each expert's router column, plus an optional
+    per-expert additive prior, in float64 (pages: tokens are scored and
+    routed on the device -- section "Keep low-bit weights packed, do the
+    work on the NPU").
+
+    x_bf16 uint16 [T][H] (bf16 bit patterns), router_w float32 [H][E],
+    bias float [E] or None.  Every input value is decoded exactly; the
+    result is the exact sum up to float64 rounding.  Returns float64 [T][E].
+    """
+    x = decode_bf16(x_bf16)
+    w = np.asarray(router_w, dtype=np.float32).astype(np.float64)
+    if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[0]:
+        raise ValueError("need x [T][H] and router_w [H][E]")
+    lg = x @ w
+    if bias is not None:
+        lg = lg + np.asarray(bias, dtype=np.float64)[None, :]
+    return lg
+
 
 def route_topk(logits, k: int, renormalize: int = 1):
     """Top-k softmax gating.

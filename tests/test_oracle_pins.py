@@ -384,3 +384,58 @@ def test_zipf_prior_skews_routing():
     counts = np.bincount(ids.ravel(), minlength=128)
     assert 12 <= (counts > 0).sum() <= 48
     assert counts.max() >= 6
+
+
+# ---------------------------------------------------------------------------
+# router logits (on-device scoring of the tokens)
+# ---------------------------------------------------------------------------
+
+def _bf16(a):
+    return bf16_bits_from_f32(np.asarray(a, dtype=np.float32))
+
+
+def test_router_logits_match_python_sums():
+    rng = np.random.default_rng(11)
+    T, H, E = 3, 37, 5
+    xb = _bf16(rng.standard_normal((T, H)))
+    w = (rng.standard_normal((H, E)) * 0.02).astype(np.float32)
+    bias = rng.standard_normal(E)
+    lg = oracle.router_logits(xb, w, bias)
+    xs = [[float(v) for v in row] for row in
+          ((xb.astype(np.uint32) << 16).view(np.float32))]
+    for t in range(T):
+        for e in range(E):
+            ref = math.fsum(xs[t][h] * float(w[h, e]) for h in range(H)) + float(bias[e])
+            assert abs(lg[t, e] - ref) <= 1e-15 * (1 + abs(ref))
+
+
+def test_router_logits_one_hot_token_gives_router_row():
+    rng = np.random.default_rng(12)
+    H, E = 64, 9
+    w = (rng.standard_normal((H, E)) * 0.02).astype(np.float32)
+    x = np.zeros((H, H), dtype=np.float32)
+    x[np.arange(H), np.arange(H)] = 1.0
+    lg = oracle.router_logits(_bf16(x), w)
+    assert np.array_equal(lg, w.astype(np.float64))
+    # a transposed operand or a dropped row would break this
+    x2 = np.zeros((1, H), dtype=np.float32)
+    x2[0, 5], x2[0, 40] = 2.0, -0.5
+    assert np.array_equal(oracle.router_logits(_bf16(x2), w)[0],
+                          2.0 * w[5].astype(np.float64) - 0.5 * w[40].astype(np.float64))
+
+
+def test_router_logits_scale_exactly_with_the_input():
+    rng = np.random.default_rng(13)
+    xb = _bf16(rng.standard_normal((4, 128)))
+    w = (rng.standard_normal((128, 16)) * 0.02).astype(np.float32)
+    x2 = ((xb.astype(np.uint32) << 16).view(np.float32) * np.float32(4.0))
+    assert np.array_equal(oracle.router_logits(_bf16(x2), w), 4.0 * oracle.router_logits(xb, w))
+
+
+def test_router_logits_reproduce_the_benchmark_logits():
+    """The generator stores fp32(x . W_r + prior) for every layer; the
+    oracle's logits round to the same fp32 values."""
+    for cfg in (LAYERS["tiny_w4a16"], LAYERS["specdecode_w4a16_t12"]):
+        layer = make_layer(cfg)
+        lg = oracle.router_logits(layer.x_bf16, layer.router_w, layer.bias)
+        assert np.array_equal(lg.astype(np.float32), layer.logits)
