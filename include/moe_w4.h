@@ -104,6 +104,35 @@ typedef struct moe_qmat {
 } moe_qmat;                 /* 32 bytes */
 
 /* ---------------------------------------------------------------------
+ * moe_router_topk -- the router on the device: logits from the token
+ * activations and the router weights, then moe_route_topk on them.
+ * Build log "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", section "Keep
+ * low-bit weights packed, do the work on the NPU" (tokens are scored and
+ * routed on the device).
+ *   x         bf16 [T][H]
+ *   router_w  fp32 [H][E] (row h holds every expert's weight for input h)
+ *   prior     fp32 [E] added to every token's logits, or null
+ *   logits    fp32 [T][E] (out): sum over h of x[t][h] * router_w[h][e] in
+ *             fp32, in a fixed order (increasing h inside each chunk of H,
+ *             then the chunks in order; the chunking depends only on T, H
+ *             and E), then + prior[e]
+ *   topk_ids, topk_w (out): as moe_route_topk on those logits
+ *   workspace moe_router_workspace_bytes(T, H, E) bytes of device memory,
+ *             16-byte aligned (may be null when that is 0)
+ * Limits: those of moe_route_topk, T * H, H * E and T * E below 2^31.
+ * Errors: MOE_E_INVAL (arguments), MOE_E_UNSUPPORTED (limits),
+ * MOE_E_WORKSPACE, MOE_E_DEVICE.  The fp32 logits can differ from exact
+ * ones by the rounding of the sum, so near-ties may select differently
+ * from an exact router; the routing of the returned logits is exact.
+ * ------------------------------------------------------------------- */
+size_t moe_router_workspace_bytes(int T, int H, int E);
+moe_status moe_router_topk(const uint16_t* x, int T, int H,
+                           const float* router_w, const float* prior, int E,
+                           int k, int renormalize, float* logits,
+                           int32_t* topk_ids, float* topk_w, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * moe_route_topk -- router top-k and softmax gating on the device
  * (pages: tokens are routed to experts on the device; routing moved out of
  * the host loop).

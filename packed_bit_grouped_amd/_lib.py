@@ -30,6 +30,10 @@ _SIGS = {
     "moe_status_str": (ctypes.c_char_p, [c_int]),
     "moe_route_topk": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p,
                                c_void_p, c_void_p]),
+    "moe_router_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
+    "moe_router_topk": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_int,
+                                c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                c_void_p]),
     "moe_permute": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p]),
@@ -177,6 +181,17 @@ def moe_route_topk(logits, T, E, k, renormalize, topk_ids, topk_w,
                    stream=None, check=True):
     return _call("moe_route_topk", _ptr(logits), T, E, k, renormalize,
                  _ptr(topk_ids), _ptr(topk_w), _stream(stream), check=check)
+
+
+def moe_router_workspace_bytes(T, H, E) -> int:
+    return load().moe_router_workspace_bytes(T, H, E)
+
+
+def moe_router_topk(x, T, H, router_w, prior, E, k, renormalize, logits, topk_ids,
+                    topk_w, workspace, ws_bytes, stream=None, check=True):
+    return _call("moe_router_topk", _ptr(x), T, H, _ptr(router_w), _ptr(prior), E, k,
+                 renormalize, _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
+                 ws_bytes, _stream(stream), check=check)
 
 
 def moe_permute(topk_ids, T, k, E, tile_m, counts, offsets, sorted_pair,

@@ -191,6 +191,36 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k,
                                     topk_w, static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_router_workspace_bytes(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  return router_workspace_bytes(T, H, E);
+}
+
+moe_status moe_router_topk(const uint16_t* x, int T, int H, const float* router_w,
+                           const float* prior, int E, int k, int renormalize, float* logits,
+                           int32_t* topk_ids, float* topk_w, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  if (T < 0 || H <= 0 || E <= 0 || k <= 0 || k > E) return MOE_E_INVAL;
+  if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
+  if (E > kRouteMaxE) return MOE_E_UNSUPPORTED;
+  if ((long long)T * H >= (1LL << 31) || (long long)H * E >= (1LL << 31) ||
+      (long long)T * E >= (1LL << 31))
+    return MOE_E_UNSUPPORTED;
+  if ((T + 15) / 16 > 65535) return MOE_E_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !router_w || !logits || !topk_ids || !topk_w) return MOE_E_INVAL;
+  const size_t need = router_workspace_bytes(T, H, E);
+  if (need > 0 && (!workspace || !aligned(workspace, 16) || ws_bytes < need))
+    return MOE_E_WORKSPACE;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = launch_router_logits(x, T, H, router_w, E, prior, logits,
+                                            static_cast<float*>(workspace), s);
+  if (e != hipSuccess) return MOE_E_DEVICE;
+  return from_hip(launch_route_topk(logits, T, E, k, renormalize, topk_ids, topk_w, s));
+}
+
 moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E,
                        int tile_m, int32_t* counts, int32_t* offsets,
                        int32_t* sorted_pair, int32_t* pair_pos,

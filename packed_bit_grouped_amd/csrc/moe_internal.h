@@ -69,6 +69,12 @@ struct ProjArgs {
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k,
                              int renorm, int32_t* ids, float* w, hipStream_t st);
+// Router logits = x . W (+ prior), fp32 in a fixed order; part: the
+// workspace of router_workspace_bytes (null when that is 0).
+size_t router_workspace_bytes(int T, int H, int E);
+hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* W, int E,
+                                const float* prior, float* logits, float* part,
+                                hipStream_t st);
 hipError_t launch_permute(const int32_t* ids, int P, int E, int tile_m,
                           int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos,

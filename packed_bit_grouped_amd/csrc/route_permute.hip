@@ -182,6 +182,116 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(
     else { constexpr int NVV = 16; __VA_ARGS__; }               \
   } while (0)
 
+// ---------------------------------------------------------------------
+// Router logits on the device: logits[t][e] = sum_h x[t][h] * W[h][e]
+// (+ prior[e]), fp32, summed in a fixed order: within a chunk of H in
+// increasing h, then the chunks in increasing order.  Workgroup (chunk,
+// token group, expert group): 16 tokens x 256 experts (one per thread) x
+// one H chunk; the chunk's activations are staged in LDS 128 h at a time
+// as [h][token] fp32, so each step is one coalesced 1 KB row of W and 16
+// FMAs against four broadcast LDS reads.  Small batches split H over up
+// to ceil(H / 128) chunks (partial sums to the workspace, then
+// router_reduce_kernel) so that the launch fills the chip; large ones use
+// one chunk and write the logits directly.
+constexpr int kRtTok = 16, kRtExp = 256, kRtStep = 128;
+
+__global__ __launch_bounds__(kRtExp) void router_logits_kernel(
+    const uint16_t* __restrict__ x, int T, int H, const float* __restrict__ W, int E,
+    const float* __restrict__ prior, int hc, int n_chunks, float* __restrict__ out) {
+  __shared__ __align__(16) float xs[kRtStep * kRtTok];   // [h][token]
+  const int tid = threadIdx.x;
+  const int e = blockIdx.z * kRtExp + tid;
+  const int t0 = blockIdx.y * kRtTok, nt = min(kRtTok, T - t0);
+  const int h_begin = blockIdx.x * hc, h_end = min(H, h_begin + hc);
+  float acc[kRtTok];
+#pragma unroll
+  for (int t = 0; t < kRtTok; ++t) acc[t] = 0.0f;
+  for (int h0 = h_begin; h0 < h_end; h0 += kRtStep) {
+    const int hn = min(kRtStep, h_end - h0);
+    for (int i = tid; i < kRtStep * kRtTok; i += kRtExp) {
+      const int t = i / kRtStep, hh = i - t * kRtStep;
+      xs[hh * kRtTok + t] =
+          (t < nt && hh < hn) ? bf16_to_f32(x[(size_t)(t0 + t) * H + h0 + hh]) : 0.0f;
+    }
+    __syncthreads();
+    if (e < E) {
+      const float* wp = W + (size_t)h0 * E + e;
+#pragma unroll 8
+      for (int hh = 0; hh < hn; ++hh) {
+        const float wv = wp[(size_t)hh * E];
+        const float4* xr = reinterpret_cast<const float4*>(xs + hh * kRtTok);
+#pragma unroll
+        for (int q = 0; q < kRtTok / 4; ++q) {
+          const float4 xv = xr[q];
+          acc[4 * q + 0] = fmaf(xv.x, wv, acc[4 * q + 0]);
+          acc[4 * q + 1] = fmaf(xv.y, wv, acc[4 * q + 1]);
+          acc[4 * q + 2] = fmaf(xv.z, wv, acc[4 * q + 2]);
+          acc[4 * q + 3] = fmaf(xv.w, wv, acc[4 * q + 3]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (e >= E) return;
+  const float pe = (n_chunks == 1 && prior) ? prior[e] : 0.0f;
+#pragma unroll
+  for (int t = 0; t < kRtTok; ++t) {
+    if (t >= nt) break;
+    const size_t o = n_chunks == 1 ? (size_t)(t0 + t) * E + e
+                                   : ((size_t)blockIdx.x * T + t0 + t) * E + e;
+    out[o] = acc[t] + pe;
+  }
+}
+
+// Chunk partials [n_chunks][T][E] -> logits [T][E], chunks in order, then
+// the prior.
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part,
+                                                            int T, int E, int n_chunks,
+                                                            const float* __restrict__ prior,
+                                                            float* __restrict__ logits) {
+  const size_t n = (size_t)T * E;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    float v = 0.0f;
+    for (int c = 0; c < n_chunks; ++c) v += part[(size_t)c * n + i];
+    logits[i] = prior ? v + prior[i % E] : v;
+  }
+}
+
+// Chunks of H for a batch (the launch should hold about 256 workgroups),
+// and their length (a multiple of 32).
+void router_chunks(int T, int H, int E, int& n_chunks, int& hc) {
+  const long long groups = (long long)((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp);
+  long long n = (256 + groups - 1) / groups;
+  const long long n_max = (H + kRtStep - 1) / kRtStep;
+  n = n < 1 ? 1 : n > n_max ? n_max : n;
+  hc = (int)(((H + n - 1) / n + 31) / 32 * 32);
+  n_chunks = (H + hc - 1) / hc;
+}
+
+size_t router_workspace_bytes(int T, int H, int E) {
+  int n, hc;
+  router_chunks(T, H, E, n, hc);
+  return n > 1 ? (size_t)n * T * E * sizeof(float) : 0;
+}
+
+hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* W, int E,
+                                const float* prior, float* logits, float* part,
+                                hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  int n_chunks, hc;
+  router_chunks(T, H, E, n_chunks, hc);
+  const dim3 grid(n_chunks, (T + kRtTok - 1) / kRtTok, (E + kRtExp - 1) / kRtExp);
+  router_logits_kernel<<<grid, kRtExp, 0, st>>>(x, T, H, W, E, prior, hc, n_chunks,
+                                                n_chunks == 1 ? logits : part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_chunks == 1) return e;
+  const size_t n = (size_t)T * E;
+  const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  router_reduce_kernel<<<blocks, 256, 0, st>>>(part, T, E, n_chunks, prior, logits);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k,
                              int renorm, int32_t* ids, float* w,
                              hipStream_t st) {

@@ -224,3 +224,29 @@ def test_layer_validation():
     assert q(1, 64, 2048, 768, 128, 8, 0, 0, 16, one) == 0                 # A8: two calls
     assert q(0, 1, 2048, 768, 256, 8, 1, 768, 16, one) == 0                # E > 128
     assert q(2, 1, 2048, 768, 128, 8, 1, 768, 16, 0) == L.MOE_E_INVAL
+
+
+def test_router_validation_and_workspace():
+    """moe_router_topk checks its arguments on the host; small batches
+    split H over chunks and need a workspace for the partial sums."""
+    # one token: H = 2048 in 16 chunks of 128 -> 16 * 1 * 128 partials
+    assert L.moe_router_workspace_bytes(1, 2048, 128) == 16 * 128 * 4
+    assert L.moe_router_workspace_bytes(4096, 4096, 256) == 0   # one chunk
+    assert L.moe_router_workspace_bytes(0, 2048, 128) == 0
+    ok = dict(x=FAKE, T=1, H=2048, router_w=FAKE, prior=None, E=128, k=8, renormalize=1,
+              logits=FAKE, topk_ids=FAKE, topk_w=FAKE, workspace=FAKE, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_router_topk(*a.values(), stream=0, check=False)
+    assert call(k=0) == L.MOE_E_INVAL
+    assert call(k=129) == L.MOE_E_INVAL
+    assert call(renormalize=3) == L.MOE_E_INVAL
+    assert call(H=0) == L.MOE_E_INVAL
+    assert call(E=1025, k=2) == L.MOE_E_UNSUPPORTED
+    assert call(logits=None) == L.MOE_E_INVAL
+    assert call(workspace=None) == L.MOE_E_WORKSPACE
+    assert call(ws_bytes=16) == L.MOE_E_WORKSPACE
+    assert call(T=0, x=None) == L.MOE_OK
+    assert call() == L.MOE_E_DEVICE
+    assert call(T=4096, H=4096, E=256, workspace=None, ws_bytes=0) == L.MOE_E_DEVICE
