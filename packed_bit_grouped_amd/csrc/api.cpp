@@ -206,7 +206,7 @@ moe_status moe_router_topk(const uint16_t* x, int T, int H, const float* router_
   if ((long long)T * H >= (1LL << 31) || (long long)H * E >= (1LL << 31) ||
       (long long)T * E >= (1LL << 31))
     return MOE_E_UNSUPPORTED;
-  if ((T + 15) / 16 > 65535) return MOE_E_UNSUPPORTED;
+  if ((T + 63) / 64 > 65535) return MOE_E_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !router_w || !logits || !topk_ids || !topk_w) return MOE_E_INVAL;
   const size_t need = router_workspace_bytes(T, H, E);

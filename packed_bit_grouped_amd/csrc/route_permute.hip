@@ -186,60 +186,87 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(
 // Router logits on the device: logits[t][e] = sum_h x[t][h] * W[h][e]
 // (+ prior[e]), fp32, summed in a fixed order: within a chunk of H in
 // increasing h, then the chunks in increasing order.  Workgroup (chunk,
-// token group, expert group): 16 tokens x 256 experts (one per thread) x
-// one H chunk; the chunk's activations are staged in LDS 128 h at a time
-// as [h][token] fp32, so each step is one coalesced 1 KB row of W and 16
-// FMAs against four broadcast LDS reads.  Small batches split H over up
-// to ceil(H / 128) chunks (partial sums to the workspace, then
-// router_reduce_kernel) so that the launch fills the chip; large ones use
-// one chunk and write the logits directly.
-constexpr int kRtTok = 16, kRtExp = 256, kRtStep = 128;
+// token tile, expert tile) = 64 tokens x 64 experts; each thread owns a
+// 4 x 4 block of outputs.  H advances 32 rows per step through LDS ([h]
+// [token] and [h][expert] fp32, double-buffered): the next step's loads
+// are in flight while the current step's 32 x 16 fused multiply-adds run.
+// Small batches split H into chunks (partial sums to the workspace, then
+// router_reduce_kernel) so that the launch has about 256 workgroups.
+constexpr int kRtT = 64, kRtE = 64, kRtK = 32, kRtThreads = 256;
+constexpr int kRtLd = (kRtK * kRtT) / kRtThreads;   // loads per thread per step and operand
 
-__global__ __launch_bounds__(kRtExp) void router_logits_kernel(
+__global__ __launch_bounds__(kRtThreads) void router_logits_kernel(
     const uint16_t* __restrict__ x, int T, int H, const float* __restrict__ W, int E,
     const float* __restrict__ prior, int hc, int n_chunks, float* __restrict__ out) {
-  __shared__ __align__(16) float xs[kRtStep * kRtTok];   // [h][token]
+  __shared__ __align__(16) float xs[2][kRtK * kRtT];   // [h][token]
+  __shared__ __align__(16) float ws[2][kRtK * kRtE];   // [h][expert]
   const int tid = threadIdx.x;
-  const int e = blockIdx.z * kRtExp + tid;
-  const int t0 = blockIdx.y * kRtTok, nt = min(kRtTok, T - t0);
+  const int t0 = blockIdx.y * kRtT, e0 = blockIdx.z * kRtE;
   const int h_begin = blockIdx.x * hc, h_end = min(H, h_begin + hc);
-  float acc[kRtTok];
+  const int n_steps = (h_end - h_begin + kRtK - 1) / kRtK;
+  // staging: x element i -> (token i / 32, h i % 32); W element i ->
+  // (h i / 64, expert i % 64); consecutive threads read consecutive memory
+  float xr[kRtLd], wr[kRtLd];
+  auto load = [&](int st) {
+    const int h0 = h_begin + st * kRtK;
 #pragma unroll
-  for (int t = 0; t < kRtTok; ++t) acc[t] = 0.0f;
-  for (int h0 = h_begin; h0 < h_end; h0 += kRtStep) {
-    const int hn = min(kRtStep, h_end - h0);
-    for (int i = tid; i < kRtStep * kRtTok; i += kRtExp) {
-      const int t = i / kRtStep, hh = i - t * kRtStep;
-      xs[hh * kRtTok + t] =
-          (t < nt && hh < hn) ? bf16_to_f32(x[(size_t)(t0 + t) * H + h0 + hh]) : 0.0f;
+    for (int j = 0; j < kRtLd; ++j) {
+      const int i = tid + j * kRtThreads;
+      const int xt = i / kRtK, xh = i % kRtK;
+      const int wh = i / kRtE, we = i % kRtE;
+      xr[j] = (t0 + xt < T && h0 + xh < h_end)
+                  ? bf16_to_f32(x[(size_t)(t0 + xt) * H + h0 + xh]) : 0.0f;
+      wr[j] = (h0 + wh < h_end && e0 + we < E) ? W[(size_t)(h0 + wh) * E + e0 + we] : 0.0f;
     }
-    __syncthreads();
-    if (e < E) {
-      const float* wp = W + (size_t)h0 * E + e;
-#pragma unroll 8
-      for (int hh = 0; hh < hn; ++hh) {
-        const float wv = wp[(size_t)hh * E];
-        const float4* xr = reinterpret_cast<const float4*>(xs + hh * kRtTok);
+  };
+  auto store = [&](int b) {
 #pragma unroll
-        for (int q = 0; q < kRtTok / 4; ++q) {
-          const float4 xv = xr[q];
-          acc[4 * q + 0] = fmaf(xv.x, wv, acc[4 * q + 0]);
-          acc[4 * q + 1] = fmaf(xv.y, wv, acc[4 * q + 1]);
-          acc[4 * q + 2] = fmaf(xv.z, wv, acc[4 * q + 2]);
-          acc[4 * q + 3] = fmaf(xv.w, wv, acc[4 * q + 3]);
-        }
-      }
+    for (int j = 0; j < kRtLd; ++j) {
+      const int i = tid + j * kRtThreads;
+      xs[b][(i % kRtK) * kRtT + i / kRtK] = xr[j];
+      ws[b][i] = wr[j];
     }
+  };
+  const int tg = tid / (kRtE / 4), eg = tid % (kRtE / 4);   // 4 tokens x 4 experts
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+  if (n_steps > 0) {
+    load(0);
+    store(0);
     __syncthreads();
   }
-  if (e >= E) return;
-  const float pe = (n_chunks == 1 && prior) ? prior[e] : 0.0f;
+  for (int st = 0; st < n_steps; ++st) {
+    const int b = st & 1;
+    if (st + 1 < n_steps) load(st + 1);
+#pragma unroll 8
+    for (int h = 0; h < kRtK; ++h) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xs[b][h * kRtT + 4 * tg]);
+      const float4 wv = *reinterpret_cast<const float4*>(&ws[b][h * kRtE + 4 * eg]);
+      const float xa[4] = {xv.x, xv.y, xv.z, xv.w}, wa[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-  for (int t = 0; t < kRtTok; ++t) {
-    if (t >= nt) break;
-    const size_t o = n_chunks == 1 ? (size_t)(t0 + t) * E + e
-                                   : ((size_t)blockIdx.x * T + t0 + t) * E + e;
-    out[o] = acc[t] + pe;
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(xa[a], wa[c], acc[a][c]);
+    }
+    if (st + 1 < n_steps) store(b ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int t = t0 + 4 * tg + a;
+    if (t >= T) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = e0 + 4 * eg + c;
+      if (e >= E) continue;
+      if (n_chunks == 1)
+        out[(size_t)t * E + e] = prior ? acc[a][c] + prior[e] : acc[a][c];
+      else
+        out[((size_t)blockIdx.x * T + t) * E + e] = acc[a][c];
+    }
   }
 }
 
@@ -252,8 +279,16 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restr
   const size_t n = (size_t)T * E;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
+    // 16 loads in flight at a time, summed in chunk order
     float v = 0.0f;
-    for (int c = 0; c < n_chunks; ++c) v += part[(size_t)c * n + i];
+    for (int c0 = 0; c0 < n_chunks; c0 += 16) {
+      float p[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p[j] = c0 + j < n_chunks ? part[(size_t)(c0 + j) * n + i] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (c0 + j < n_chunks) v += p[j];
+    }
     logits[i] = prior ? v + prior[i % E] : v;
   }
 }
@@ -261,11 +296,11 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restr
 // Chunks of H for a batch (the launch should hold about 256 workgroups),
 // and their length (a multiple of 32).
 void router_chunks(int T, int H, int E, int& n_chunks, int& hc) {
-  const long long groups = (long long)((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp);
+  const long long groups = (long long)((T + kRtT - 1) / kRtT) * ((E + kRtE - 1) / kRtE);
   long long n = (256 + groups - 1) / groups;
-  const long long n_max = (H + kRtStep - 1) / kRtStep;
+  const long long n_max = (H + kRtK - 1) / kRtK;
   n = n < 1 ? 1 : n > n_max ? n_max : n;
-  hc = (int)(((H + n - 1) / n + 31) / 32 * 32);
+  hc = (int)(((H + n - 1) / n + kRtK - 1) / kRtK * kRtK);
   n_chunks = (H + hc - 1) / hc;
 }
 
@@ -281,9 +316,9 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* W,
   if (T == 0) return hipSuccess;
   int n_chunks, hc;
   router_chunks(T, H, E, n_chunks, hc);
-  const dim3 grid(n_chunks, (T + kRtTok - 1) / kRtTok, (E + kRtExp - 1) / kRtExp);
-  router_logits_kernel<<<grid, kRtExp, 0, st>>>(x, T, H, W, E, prior, hc, n_chunks,
-                                                n_chunks == 1 ? logits : part);
+  const dim3 grid(n_chunks, (T + kRtT - 1) / kRtT, (E + kRtE - 1) / kRtE);
+  router_logits_kernel<<<grid, kRtThreads, 0, st>>>(x, T, H, W, E, prior, hc, n_chunks,
+                                                    n_chunks == 1 ? logits : part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_chunks == 1) return e;
   const size_t n = (size_t)T * E;

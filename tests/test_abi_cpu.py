@@ -229,8 +229,8 @@ def test_layer_validation():
 def test_router_validation_and_workspace():
     """moe_router_topk checks its arguments on the host; small batches
     split H over chunks and need a workspace for the partial sums."""
-    # one token: H = 2048 in 16 chunks of 128 -> 16 * 1 * 128 partials
-    assert L.moe_router_workspace_bytes(1, 2048, 128) == 16 * 128 * 4
+    # one token, 2 expert tiles: H = 2048 in 64 chunks of 32 -> 64 * 1 * 128 partials
+    assert L.moe_router_workspace_bytes(1, 2048, 128) == 64 * 128 * 4
     assert L.moe_router_workspace_bytes(4096, 4096, 256) == 0   # one chunk
     assert L.moe_router_workspace_bytes(0, 2048, 128) == 0
     ok = dict(x=FAKE, T=1, H=2048, router_w=FAKE, prior=None, E=128, k=8, renormalize=1,

@@ -38,10 +38,10 @@ def _run(xb, W, prior, k, renorm=1):
 
 def _chunks(T, H, E):
     """The library's split of H for a batch (its header: the chunking
-    depends only on T, H and E): about 256 workgroups of 16 tokens x 256
-    experts, chunks of at least 128, a multiple of 32 long."""
-    groups = -(-T // 16) * -(-E // 256)
-    n = min(max(-(-256 // groups), 1), -(-H // 128))
+    depends only on T, H and E): about 256 workgroups of 64 tokens x 64
+    experts, chunks a multiple of 32 long."""
+    groups = -(-T // 64) * -(-E // 64)
+    n = min(max(-(-256 // groups), 1), -(-H // 32))
     hc = -(-(-(-H // n)) // 32) * 32
     return -(-H // hc), hc
 
