@@ -237,9 +237,10 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
                               /* layer where the shape allows it (same      */
                               /* results as the two calls)                  */
 
-/* Tile height to pass as moe_permute's tile_m: 128 (the MFMA path's row
- * block) when T*k >= 32*E with A16, else 16.  Both paths accept any
- * tile_m; the MFMA path walks longer tiles in 128-row chunks. */
+/* Tile height to pass as moe_permute's tile_m: 160 (the MFMA path's row
+ * chunk: an expert with up to 160 pairs streams its weights once) when
+ * T*k >= 32*E with A16, else 16.  Both paths accept any tile_m; the MFMA
+ * path walks longer tiles in 160-row chunks. */
 int moe_preferred_tile_m(int act, int T, int E, int k);
 
 /* ---------------------------------------------------------------------

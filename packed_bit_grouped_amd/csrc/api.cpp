@@ -167,7 +167,7 @@ int moe_permute_max_tiles(int T, int k, int E, int tile_m) {
 }
 
 int moe_preferred_tile_m(int act, int T, int E, int k) {
-  if (act == MOE_A16 && (long long)T * k >= 32LL * E) return 128;
+  if (act == MOE_A16 && (long long)T * k >= 32LL * E) return 160;
   return 16;
 }
 

@@ -45,7 +45,8 @@ typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
 
 constexpr int kMThreads = 256;    // 4 waves, one per SIMD
-constexpr int kBM = 128;            // activation rows per tile chunk
+constexpr int kBM = 128;            // weight units per workgroup (gate/up), shared-expert tile rows
+constexpr int kRowsMax = 160;       // activation rows per tile chunk (5 row blocks of 32)
 constexpr int kRing = 4;            // steps in flight (register ring slots)
 constexpr int kKS = 64;             // K per pipeline step
 constexpr int kChunks = kKS / 8;    // 16-byte fp16 chunks per row and step
@@ -262,7 +263,7 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
     for (int i = 0; i < MB; ++i) ar.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ars, aoff[i], o, 0);
   };
   auto store_a = [&](int buf, const AStep<MB>& ar) {
-    u32x4_v* d = As + buf * kChunks * kBM + m_own * kChunks + (ci_own ^ (m_own & 7));
+    u32x4_v* d = As + buf * kChunks * kRowsMax + m_own * kChunks + (ci_own ^ (m_own & 7));
 #pragma unroll
     for (int i = 0; i < MB; ++i) d[32 * kChunks * i] = ar.a[i];
   };
@@ -282,7 +283,7 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
     // group scales of this step (64 stg + 32 kh lies in group (..) >> gsh)
     const int gi = (min(stg, n_st - 1) * kKS + kh * 32) >> w.gsh;
     const uint32_t sc0 = w.sc[0][gi], sc1 = w.sc[1][gi];
-    const u32x4_v* Ab = As + buf * kChunks * kBM + ln * kChunks;
+    const u32x4_v* Ab = As + buf * kChunks * kRowsMax + ln * kChunks;
     // the whole step's A fragments first: one LDS round trip per step
     u32x4_v af[4][MB];
 #pragma unroll
@@ -447,10 +448,10 @@ __device__ __forceinline__ void mfma_tile(const ProjArgs& a, const TileCtx& c, u
     w.sc[1] = ssc + (64 * wave + ln + 32) * ng;
   }
 
-  for (int mc = c.r_begin; mc < c.r_end; mc += kBM) {
-    const int nrows = min(kBM, c.r_end - mc);
+  for (int mc = c.r_begin; mc < c.r_end; mc += kRowsMax) {
+    const int nrows = min(kRowsMax, c.r_end - mc);
     __syncthreads();   // previous chunk's readers of tok / As are done
-    if (tid < kBM) {
+    if (tid < kRowsMax) {
       const int mm = tid < nrows ? tid : 0;   // padding rows re-read row 0 (discarded)
       int r;
       if (MODE == 0) r = c.is_sh ? mc + mm : a.sorted_pair[mc + mm] / a.k;
@@ -458,7 +459,8 @@ __device__ __forceinline__ void mfma_tile(const ProjArgs& a, const TileCtx& c, u
       tok[tid] = r;
     }
     __syncthreads();
-    if (nrows > 64) mfma_chunk<MODE, BITS, 4>(a, c, w, As, tok, mc, nrows);
+    if (nrows > 128) mfma_chunk<MODE, BITS, 5>(a, c, w, As, tok, mc, nrows);
+    else if (nrows > 64) mfma_chunk<MODE, BITS, 4>(a, c, w, As, tok, mc, nrows);
     else if (nrows > 32) mfma_chunk<MODE, BITS, 2>(a, c, w, As, tok, mc, nrows);
     else mfma_chunk<MODE, BITS, 1>(a, c, w, As, tok, mc, nrows);
   }
@@ -469,9 +471,9 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
 void proj_mfma_kernel(ProjArgs a, const uint16_t* x16_4,
                                                               const uint16_t* x16_2) {
   extern __shared__ __align__(16) unsigned char smem[];
-  u32x4_v* As = reinterpret_cast<u32x4_v*>(smem);                  // [2][kBM][kChunks]
-  int* tok = reinterpret_cast<int*>(smem + 2 * kChunks * kBM * 16);  // [kBM]
-  uint16_t* ssc = reinterpret_cast<uint16_t*>(tok + kBM);             // [256][K / group]
+  u32x4_v* As = reinterpret_cast<u32x4_v*>(smem);                        // [2][kRowsMax][kChunks]
+  int* tok = reinterpret_cast<int*>(smem + 2 * kChunks * kRowsMax * 16);  // [kRowsMax]
+  uint16_t* ssc = reinterpret_cast<uint16_t*>(tok + kRowsMax);             // [256][K / group]
   const int tid = threadIdx.x;
 
   // ---- block -> (tile slot, unit block).  Block b runs on XCD b mod 8; each
@@ -560,7 +562,7 @@ hipError_t launch_proj_mfma(const ProjArgs& a_in, uint16_t* a16_4, uint16_t* a16
   // A tile, row table, and the scales of 256 weight rows at the smallest
   // group (32)
   const int Kmax = a.K_sh > a.K ? a.K_sh : a.K;
-  const size_t lds = (size_t)2 * kChunks * kBM * 16 + kBM * sizeof(int) +
+  const size_t lds = (size_t)2 * kChunks * kRowsMax * 16 + kRowsMax * sizeof(int) +
                      (size_t)2 * kBM * (Kmax / 32) * 2;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   if (a.mode == 0)
