@@ -150,13 +150,15 @@ __device__ __forceinline__ void chunk_dot(const ProjArgs& a, const uint4 wv, con
   if (ACT == MOE_A16) {
     if (G.bits == 4) {
       uint32_t wb[16];
+      // code c -> bf16 136 + c: field (c ^ 8) OR-ed into 128 = 0x4300, written
+      // as one AND and one XOR (the offset 8 folded into the constant)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w = W[j] ^ 0x88888888u;
-        wb[4 * j + 0] = (w & 0x000F000Fu) | 0x43004300u;
-        wb[4 * j + 1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-        wb[4 * j + 2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-        wb[4 * j + 3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+        const uint32_t w = W[j];
+        wb[4 * j + 0] = (w & 0x000F000Fu) ^ 0x43084308u;
+        wb[4 * j + 1] = ((w >> 4) & 0x000F000Fu) ^ 0x43084308u;
+        wb[4 * j + 2] = ((w >> 8) & 0x000F000Fu) ^ 0x43084308u;
+        wb[4 * j + 3] = ((w >> 12) & 0x000F000Fu) ^ 0x43084308u;
       }
       const float s = fp16_to_f32(sv & 0xFFFFu);
 #pragma unroll
@@ -178,9 +180,9 @@ __device__ __forceinline__ void chunk_dot(const ProjArgs& a, const uint4 wv, con
       uint32_t wb[32];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w = W[j] ^ 0xAAAAAAAAu;
+        const uint32_t w = W[j];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wb[8 * j + i] = ((w >> (2 * i)) & 0x00030003u) | 0x43004300u;
+        for (int i = 0; i < 8; ++i) wb[8 * j + i] = ((w >> (2 * i)) & 0x00030003u) ^ 0x43024302u;
       }
       const float s0 = fp16_to_f32(sv & 0xFFFFu);
       const float s1 = G.group == 32 ? fp16_to_f32(sv >> 16) : s0;
