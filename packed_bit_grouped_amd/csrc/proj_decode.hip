@@ -148,6 +148,16 @@ __device__ __forceinline__ uint32_t dec_scale(const uint16_t* sp, const RowGeom&
   return (G.bits == 2 && G.group == 32) ? ld_global(reinterpret_cast<const uint32_t*>(sp + 2 * c))
                                         : (uint32_t)ld_global(sp + (c * G.CK) / G.group);
 }
+// The same without a branch (two 16-bit loads, then a select), for the
+// gate/up weight issue: loads issued under conditions leave the compiler
+// unsure how many are still in flight after them, and it then waits for
+// all of them before the activation staging that follows.
+__device__ __forceinline__ uint32_t dec_scale_flat(const uint16_t* sp, const RowGeom& G, int c) {
+  const bool two = G.bits == 2 && G.group == 32;
+  const int i0 = two ? 2 * c : (c * G.CK) / G.group;
+  const uint32_t lo = ld_global(sp + i0), hi = ld_global(sp + (two ? i0 + 1 : i0));
+  return two ? (lo | (hi << 16)) : lo;
+}
 
 // ---------------------------------------------------------------------
 // gate/up + SiLU*mul.  Grid: (n_sh_slots + max_tiles) * n_ub workgroups;
@@ -181,6 +191,8 @@ __device__ __forceinline__ void gu_issue(GuRows<CPL>& g, const ProjArgs& a, bool
     g.vrow[r] = g.unit[r] < U;
     g.wr[r] = g.vrow[r] ? g.unit[r] + (up ? U : 0) : 0;
   }
+  // every load unconditional (an idle slot reads chunk 0 of its row, which
+  // exists, and keeps zeros), so the compiler's wait counts stay exact
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const uint4* cp = reinterpret_cast<const uint4*>(q.codes + (size_t)g.wr[r] * g.G.row_bytes);
@@ -188,14 +200,12 @@ __device__ __forceinline__ void gu_issue(GuRows<CPL>& g, const ProjArgs& a, bool
 #pragma unroll
     for (int b = 0; b < CPL; ++b) {
       const int c = lis + kDecGuLanes * b;
-      if (g.vrow[r] && c < g.G.C_r) {
-        const u32x4_v t4 = ld_global_nt(reinterpret_cast<const u32x4_v*>(cp + c));
-        g.wv[r][b] = make_uint4(t4.x, t4.y, t4.z, t4.w);
-        g.sv[r][b] = dec_scale(sp, g.G, c);
-      } else {
-        g.wv[r][b] = make_uint4(0u, 0u, 0u, 0u);
-        g.sv[r][b] = 0u;
-      }
+      const bool ok = g.vrow[r] && c < g.G.C_r;
+      const int cc = ok ? c : 0;
+      const u32x4_v t4 = ld_global_nt(reinterpret_cast<const u32x4_v*>(cp + cc));
+      const uint32_t sv = dec_scale_flat(sp, g.G, cc);
+      g.wv[r][b] = ok ? make_uint4(t4.x, t4.y, t4.z, t4.w) : make_uint4(0u, 0u, 0u, 0u);
+      g.sv[r][b] = ok ? sv : 0u;
     }
   }
 }
@@ -250,18 +260,34 @@ __device__ __forceinline__ void gateup_tile(const ProjArgs& a, bool is_sh, int e
                                             const int* srow, uint32_t* xs, float* xsum) {
   const int tid = threadIdx.x;
   const int K = a.K;
-  // ---- every weight load of the workgroup, then the activation rows
+  // ---- the tile's activation rows first, then every weight load of the
+  // workgroup: the staging waits only for the activations, and each wave
+  // starts its products as its own weights arrive
+  const int xs_row = K / 2, xsum_row = K / 32, nb32 = K / 32;
+  // one pass: the launcher guarantees a tile has at most MAXT rows (and K
+  // at most 2048: 64 blocks per row)
+  const int nt = min(MAXT, r_end - r_begin);
+  constexpr int XI = (MAXT * 64 + kDecThreads - 1) / kDecThreads;
+  uint32_t xv[XI][16];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int u = tid + i * kDecThreads;
+    if (u < nt * nb32) {
+      const int m = u / nb32, b = u - m * nb32;
+      int row = r_begin + m;
+      if (!is_sh) row = (srow ? srow[row] : ld_global(a.sorted_pair + row)) / a.k;
+      load_a16_block(a.in_bf16 + (size_t)row * a.ld_in, b, xv[i]);
+    }
+  }
   GuRows<CPL> g;
   gu_issue<CPL>(g, a, is_sh, q, ub);
-  const int xs_row = K / 2, xsum_row = K / 32, nb32 = K / 32;
-  // one pass: the launcher guarantees a tile has at most MAXT rows
-  const int nt = min(MAXT, r_end - r_begin);
-  for (int u = tid; u < nt * nb32; u += kDecThreads) {
-    const int m = u / nb32, b = u - m * nb32;
-    int row = r_begin + m;
-    if (!is_sh) row = (srow ? srow[row] : ld_global(a.sorted_pair + row)) / a.k;
-    stage_a16_block(a.in_bf16 + (size_t)row * a.ld_in, b, K, g.G.bits, xs + m * xs_row,
-                    xsum + m * xsum_row);
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int u = tid + i * kDecThreads;
+    if (u < nt * nb32) {
+      const int m = u / nb32, b = u - m * nb32;
+      store_a16_block(xv[i], b, K, g.G.bits, xs + m * xs_row, xsum + m * xsum_row);
+    }
   }
   lds_barrier();
   gu_compute<MAXT, CPL>(g, a, is_sh, e, r_begin, nt, xs, xsum);
