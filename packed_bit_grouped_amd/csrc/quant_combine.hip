@@ -41,7 +41,8 @@ hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
 
 // out[t][n] = bf16( sum_j w[t][j] * y[pair_pos[t*k+j]][n] + sum_s y[P+s*T+t][n] ),
 // accumulated in fp32 in that fixed order (deterministic).  Four outputs
-// per thread with 16-byte loads.
+// per thread with 16-byte loads; the y rows of eight pairs are loaded
+// before the first of their multiply-adds, so they are in flight together.
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y, int ld_y, const float* __restrict__ topk_w,
     const int32_t* __restrict__ pair_pos, int T, int k, int H, int P,
@@ -50,15 +51,28 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int pp = pair_pos[t * k + j];
-    if (pp < 0) continue;
-    const float wj = topk_w[t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + (size_t)pp * ld_y + n);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int pp[8];
+    float wj[8];
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = j0 + u < k;
+      pp[u] = in ? pair_pos[t * k + j0 + u] : -1;
+      wj[u] = in ? topk_w[t * k + j0 + u] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = pp[u] >= 0 ? *reinterpret_cast<const float4*>(y + (size_t)pp[u] * ld_y + n)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (pp[u] < 0) continue;
+      acc.x = fmaf(wj[u], v[u].x, acc.x);
+      acc.y = fmaf(wj[u], v[u].y, acc.y);
+      acc.z = fmaf(wj[u], v[u].z, acc.z);
+      acc.w = fmaf(wj[u], v[u].w, acc.w);
+    }
   }
   for (int s = 0; s < n_shared; ++s) {
     const float4 v =
