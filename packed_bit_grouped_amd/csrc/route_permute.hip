@@ -86,13 +86,15 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int tile_m,
     if ((unsigned)e < (unsigned)E) atomicAdd(&sm.hist[wave * kPermMaxE + e], 1);
   }
   __syncthreads();
+  // per expert: the 16 wave counts read together (the waves' start
+  // positions are written below, once the expert's offset is known)
   int cnt = 0;
+  int wc[kPermWaves];
   if (tid < E) {
-    for (int w = 0; w < kPermWaves; ++w) {
-      const int c = sm.hist[w * kPermMaxE + tid];
-      sm.hist[w * kPermMaxE + tid] = cnt;
-      cnt += c;
-    }
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) wc[w] = sm.hist[w * kPermMaxE + tid];
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) cnt += wc[w];
   }
   const int excl = block_exclusive_scan(cnt, sm.tmp);
   const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
@@ -100,7 +102,13 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int tile_m,
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = excl;
-    for (int w = 0; w < kPermWaves; ++w) sm.hist[w * kPermMaxE + tid] += excl;
+    // wave w's first position: the offset plus the counts of waves 0..w-1
+    int run = excl;
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) {
+      sm.hist[w * kPermMaxE + tid] = run;
+      run += wc[w];
+    }
     for (int i = 0; i < ntile; ++i) {
       const int r0 = excl + i * tile_m;
       int4 tl;
