@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_W4_ABI_VERSION 1
+#define MOE_W4_ABI_VERSION 2
 
 /* Version of the compiled library.  The Python binding refuses to load a
  * library whose version differs from the header it was written for. */
@@ -192,6 +192,9 @@ int moe_permute_max_tiles(int T, int k, int E, int tile_m);
 /* ---------------------------------------------------------------------
  * moe_quant_a8_rows -- the dynamic int8 row quantizer of the A8 mode, as a
  * standalone call (the projections run the same device code internally).
+ * Build log "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", section "Keep
+ * low-bit weights packed, do the work on the NPU" (a dedicated W4A8
+ * execution: int8 activations against the packed int4 weights).
  *   src   [R][ld] bf16 (src_is_f32 = 0) or fp32 (src_is_f32 = 1); the
  *         first C entries of each row are quantized
  *   q     int8 [R][C] (out), s fp32 [R] (out)
@@ -236,6 +239,11 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
 #define MOE_LAYER_ONE_LAUNCH 8 /* moe_w4_layer: one launch for the whole    */
                               /* layer where the shape allows it (same      */
                               /* results as the two calls)                  */
+#define MOE_OUT_F32 16        /* moe_w4_down_combine / moe_w4_layer: out is */
+                              /* fp32 [T][H] (16-byte aligned) holding the  */
+                              /* combined sum before any rounding to bf16;  */
+                              /* without it out is bf16, the round-to-      */
+                              /* nearest-even of exactly that value         */
 
 /* Tile height to pass as moe_permute's tile_m: 160 (the MFMA path's row
  * chunk: an expert with up to 160 pairs streams its weights once) when
@@ -246,6 +254,12 @@ int moe_preferred_tile_m(int act, int T, int E, int k);
 /* ---------------------------------------------------------------------
  * moe_w4_gateup_silu -- grouped gate/up projection of every routed pair
  * and every shared-expert token, fused with SiLU(g) * u.
+ * Build log "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", section "Keep
+ * low-bit weights packed, do the work on the NPU" (grouped expert
+ * projections on packed weights with fused gate/up handling, blocked
+ * reduction, routing and tile reuse, W4A8 execution) and section "GLM is
+ * my next, harder model" (a blocked-dequant matrix kernel over mixed
+ * int2/int4 experts).
  *   x          bf16 [T][H]
  *   w13        device table of E moe_qmat, each [2I][H] (gate rows 0..I-1,
  *              up rows I..2I-1)
@@ -257,6 +271,12 @@ int moe_preferred_tile_m(int act, int T, int E, int k);
  *              s*T + t is shared expert s and token t.
  *              A16: bf16 [R][ld_h] (h rounded to bf16).
  *              A8 : fp32 [R][ld_h].
+ * Precision of the matrix-core path (MOE_PATH_MFMA, chosen automatically
+ * for prefill shapes): x enters the MFMAs as fp16 (bf16 -> fp16 rounding
+ * toward zero: exact for |x| in [2^-14, 65504], saturating above 65504,
+ * losing low bits below 2^-14) against code * scale rounded once to fp16;
+ * fp32 accumulation.  Inputs with |x| or |h| above 65504 need
+ * MOE_PATH_GEMV or MOE_PATH_MFMA16.
  * ------------------------------------------------------------------- */
 moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H,
                               int I, int E, int k, const moe_qmat* w13,
@@ -294,6 +314,11 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits,
 /* ---------------------------------------------------------------------
  * moe_w4_down_combine -- grouped down projection of every h row and the
  * weighted combine into the token outputs.
+ * Build log "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", section "Keep
+ * low-bit weights packed, do the work on the NPU" (grouped expert
+ * projections straight from packed weights, blocked reduction, W4A8
+ * execution; the routed experts' outputs are joined by their gate
+ * weights).
  *   h          as written by moe_w4_gateup_silu (same act); A8 rows are
  *              quantized to int8 per row inside this call
  *   w2         device table of E moe_qmat, each [H][I]
@@ -302,6 +327,8 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits,
  *   pair_pos   from moe_permute
  *   out        bf16 [T][H] (out): out[t] = sum_j topk_w[t][j] * y(pair
  *              t*k+j) + sum_s y(shared s, t), summed in fp32 in that order
+ *              and rounded to bf16; with MOE_OUT_F32 in flags, fp32 [T][H]
+ *              holding that sum unrounded
  * Decode batches with bf16 activations (tiles of at most 16 rows, I <= 1024,
  * every h row of the layer fitting in 64 KB of LDS) combine inside the
  * down kernel: a workgroup owns a range of output columns of every token.
@@ -316,7 +343,7 @@ moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
                                const int32_t* sorted_pair,
                                const int32_t* pair_pos, const int32_t* tiles,
                                const int32_t* n_tiles, int tile_m,
-                               uint16_t* out, void* workspace,
+                               void* out, void* workspace,
                                size_t ws_bytes, int flags, void* stream);
 
 /* ---------------------------------------------------------------------
@@ -348,7 +375,7 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x,
                         int32_t* topk_ids, float* topk_w, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_pair,
                         int32_t* pair_pos, int32_t* tiles, int32_t* n_tiles,
-                        void* h, uint16_t* out, void* workspace,
+                        void* h, void* out, void* workspace,
                         size_t ws_bytes, int flags, void* stream);
 
 /* 1 when moe_w4_layer with these arguments (flags included) issues one
@@ -359,20 +386,29 @@ int moe_w4_layer_one_launch(int act, int T, int H, int I, int E, int k,
                             int n_shared, int I_shared, int tile_m, int flags);
 
 /* ---------------------------------------------------------------------
- * Test hooks of the A8 mode: the same kernels, additionally writing the
- * exact int32 per-group partial sums they accumulate.
+ * Test hooks of the A8 mode (build log "Two 96 GB Ascend cards run Qwen3.8
+ * Flash-Next", section "Keep low-bit weights packed, do the work on the
+ * NPU": dedicated W4A8 execution).  They take the path that
+ * moe_w4_gateup_silu / moe_w4_down_combine take for the same shape and
+ * flags (MOE_PATH_AUTO: the product's choice, e.g. the 16-row matrix
+ * tiles with int8 rows made in the kernel; MOE_PATH_GEMV or
+ * MOE_PATH_MFMA16 to force one; MOE_PATH_MFMA is A16 only and returns
+ * MOE_E_UNSUPPORTED) and run those kernels, compiled with the store of
+ * the exact int32 per-group partial sums they accumulate added before
+ * the sums are scaled:
  *   gate/up: partials [R][2*ld_h][ng_ld], entry (r, n, c) = sum over the
  *            K indices of group c of qx[t][K] * code[n][K]
  *   down   : partials [R][H][ng_ld], from this call's own int8 h codes
  * ng_ld >= K / group of every expert used; entries past an expert's
- * group count are left untouched.
+ * group count are left untouched.  h and out are written as by the
+ * product calls.
  * ------------------------------------------------------------------- */
 moe_status moe_dbg_w4a8_gateup_partials(
     const uint16_t* x, int T, int H, int I, int E, int k,
     const moe_qmat* w13, const moe_qmat* w13_shared, int n_shared,
     int I_shared, const int32_t* offsets, const int32_t* sorted_pair,
     const int32_t* tiles, const int32_t* n_tiles, int tile_m, void* h,
-    void* workspace, size_t ws_bytes, int32_t* partials, int ng_ld,
+    void* workspace, size_t ws_bytes, int flags, int32_t* partials, int ng_ld,
     void* stream);
 
 moe_status moe_dbg_w4a8_down_partials(
@@ -380,7 +416,7 @@ moe_status moe_dbg_w4a8_down_partials(
     const moe_qmat* w2_shared, int n_shared, int I_shared,
     const float* topk_w, const int32_t* offsets, const int32_t* sorted_pair,
     const int32_t* pair_pos, const int32_t* tiles, const int32_t* n_tiles,
-    int tile_m, uint16_t* out, void* workspace, size_t ws_bytes,
+    int tile_m, void* out, void* workspace, size_t ws_bytes, int flags,
     int32_t* partials, int ng_ld, void* stream);
 
 #ifdef __cplusplus

@@ -240,13 +240,21 @@ def silu(g):
 
 
 def round_to_bf16(v) -> np.ndarray:
-    """float64 -> nearest bf16 value (8 significant bits, ties to even),
-    returned as float64.  Used for the A16 intermediate h: with 16-bit
-    activations the down projection consumes h in bf16 (a reading; the
-    unrounded variant is available as h_exact)."""
+    """float64 -> nearest bf16 value, ties to even, returned as float64.
+
+    bf16 keeps 8 significant bits for normal values (|v| >= 2^-126), so the
+    spacing of representable values around v = m * 2^e (0.5 <= |m| < 1) is
+    2^(e - 8); below 2^-126 the subnormals are spaced 2^-133 apart.  v is
+    divided by that spacing (exact: a power of two), rounded half to even
+    and scaled back; a result of magnitude 2^128 or more is infinite.
+    Used for the A16 intermediate h: with 16-bit activations the down
+    projection consumes h in bf16 (a reading; the unrounded variant is
+    available as h_exact)."""
     v = np.asarray(v, dtype=np.float64)
-    m, e = np.frexp(v)                     # v = m * 2^e, 0.5 <= |m| < 1
-    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    _, e = np.frexp(v)                     # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e, -125) - 8            # log2 of the spacing at v
+    r = np.ldexp(np.rint(np.ldexp(v, -q)), q)
+    return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)
 
 
 def expert_rows(perm, E: int, T: int, n_shared: int):

@@ -14,13 +14,14 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_DEVICE, MOE_E_WORKSPACE = 0, -1, -2, -3, -4
 MOE_A16, MOE_A8 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA16 = 0, 1, 2, 3
 MOE_QUANT_SEPARATE = 4
 MOE_LAYER_ONE_LAUNCH = 8
+MOE_OUT_F32 = 16
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -76,14 +77,14 @@ _SIGS = {
                                              c_int, c_int, c_void_p, c_void_p,
                                              c_int, c_int, c_void_p, c_void_p,
                                              c_void_p, c_void_p, c_int,
-                                             c_void_p, c_void_p, c_size_t,
+                                             c_void_p, c_void_p, c_size_t, c_int,
                                              c_void_p, c_int, c_void_p]),
     "moe_dbg_w4a8_down_partials": (c_int, [c_void_p, c_int, c_int, c_int,
                                            c_int, c_int, c_void_p, c_void_p,
                                            c_int, c_int, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_int, c_void_p,
-                                           c_void_p, c_size_t, c_void_p,
+                                           c_void_p, c_size_t, c_int, c_void_p,
                                            c_int, c_void_p]),
 }
 
@@ -272,20 +273,20 @@ def moe_w4_layer_one_launch(act, T, H, I, E, k, n_shared=0, I_shared=0, tile_m=1
 def moe_dbg_w4a8_gateup_partials(x, T, H, I, E, k, w13, w13_shared, n_shared,
                                  I_shared, offsets, sorted_pair, tiles, n_tiles,
                                  tile_m, h, workspace, ws_bytes, partials, ng_ld,
-                                 stream=None, check=True):
+                                 flags=0, stream=None, check=True):
     return _call("moe_dbg_w4a8_gateup_partials", _ptr(x), T, H, I, E, k,
                  _ptr(w13), _ptr(w13_shared), n_shared, I_shared, _ptr(offsets),
                  _ptr(sorted_pair), _ptr(tiles), _ptr(n_tiles), tile_m, _ptr(h),
-                 _ptr(workspace), ws_bytes, _ptr(partials), ng_ld,
+                 _ptr(workspace), ws_bytes, flags, _ptr(partials), ng_ld,
                  _stream(stream), check=check)
 
 
 def moe_dbg_w4a8_down_partials(h, T, H, I, E, k, w2, w2_shared, n_shared,
                                I_shared, topk_w, offsets, sorted_pair, pair_pos,
                                tiles, n_tiles, tile_m, out, workspace, ws_bytes,
-                               partials, ng_ld, stream=None, check=True):
+                               partials, ng_ld, flags=0, stream=None, check=True):
     return _call("moe_dbg_w4a8_down_partials", _ptr(h), T, H, I, E, k,
                  _ptr(w2), _ptr(w2_shared), n_shared, I_shared, _ptr(topk_w),
                  _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos), _ptr(tiles),
                  _ptr(n_tiles), tile_m, _ptr(out), _ptr(workspace), ws_bytes,
-                 _ptr(partials), ng_ld, _stream(stream), check=check)
+                 flags, _ptr(partials), ng_ld, _stream(stream), check=check)

@@ -69,7 +69,7 @@ moe_status check_layer(int act, int T, int H, int I, int E, int k, int n_shared,
   if (k > E) return MOE_E_INVAL;
   if (n_shared > 0 && I_shared <= 0) return MOE_E_INVAL;
   if (tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
-  if (flags & ~(MOE_PATH_MASK | MOE_QUANT_SEPARATE)) return MOE_E_INVAL;
+  if (flags & ~(MOE_PATH_MASK | MOE_QUANT_SEPARATE | MOE_OUT_F32)) return MOE_E_INVAL;
   if (H % 32 || I % 32 || (n_shared > 0 && I_shared % 32)) return MOE_E_UNSUPPORTED;
   if (E > kPermMaxE) return MOE_E_UNSUPPORTED;
   if ((long long)T * k >= (1LL << 24)) return MOE_E_UNSUPPORTED;
@@ -288,7 +288,7 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return MOE_E_WORKSPACE;
   if (partials && ng_ld <= 0) return MOE_E_INVAL;
   const int path = flags & MOE_PATH_MASK;
-  const bool m16 = !partials && m16_ok(act, 0, T, H, H, tile_m);
+  const bool m16 = m16_ok(act, 0, T, H, H, tile_m);
   if (path == MOE_PATH_MFMA16 && !m16) return MOE_E_UNSUPPORTED;
   if (path == MOE_PATH_MFMA && !mfma_shape_ok(act, T, H, I, k, n_shared, I_shared))
     return MOE_E_UNSUPPORTED;
@@ -362,7 +362,7 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
                             int n_shared, int I_shared, const float* topk_w,
                             const int32_t* offsets, const int32_t* sorted_pair,
                             const int32_t* pair_pos, const int32_t* tiles,
-                            const int32_t* n_tiles, int tile_m, uint16_t* out,
+                            const int32_t* n_tiles, int tile_m, void* out,
                             void* workspace, size_t ws_bytes, int flags,
                             int32_t* partials, int ng_ld, void* stream) {
   moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
@@ -372,12 +372,14 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
       !n_tiles || !out)
     return MOE_E_INVAL;
   if (n_shared > 0 && !w2_shared) return MOE_E_INVAL;
-  if (!aligned(h, 16) || !aligned(out, 8) || !aligned(tiles, 16)) return MOE_E_INVAL;
+  const int out_f32 = (flags & MOE_OUT_F32) ? 1 : 0;
+  if (!aligned(h, 16) || !aligned(out, out_f32 ? 16 : 8) || !aligned(tiles, 16))
+    return MOE_E_INVAL;
   const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
   if (!workspace || !aligned(workspace, 256) || ws_bytes < L.total) return MOE_E_WORKSPACE;
   if (partials && ng_ld <= 0) return MOE_E_INVAL;
   const int path = flags & MOE_PATH_MASK;
-  const bool m16 = !partials && m16_ok(act, 1, T, I, n_shared > 0 ? I_shared : I, tile_m);
+  const bool m16 = m16_ok(act, 1, T, I, n_shared > 0 ? I_shared : I, tile_m);
   if (path == MOE_PATH_MFMA16 && !m16) return MOE_E_UNSUPPORTED;
   if (path == MOE_PATH_MFMA && !mfma_shape_ok(act, T, H, I, k, n_shared, I_shared))
     return MOE_E_UNSUPPORTED;
@@ -422,7 +424,7 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
     e = launch_proj_mfma(a, reinterpret_cast<uint16_t*>(ws + L.a16), nullptr, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
-                                   n_shared, out, s));
+                                   n_shared, out, out_f32, s));
   }
   if (act == MOE_A8) a.in_f32 = static_cast<const float*>(h);
   else a.in_bf16 = static_cast<const uint16_t*>(h);
@@ -446,7 +448,7 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
     e = launch_proj_m16(a, act, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
-                                   n_shared, out, s));
+                                   n_shared, out, out_f32, s));
   }
   a.maxt = gemv_maxt(T, tile_m);
   a.sh_tile = a.maxt;
@@ -455,12 +457,13 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
     a.maxt = dec_maxt(T, tile_m);
     a.topk_w = topk_w;
     a.pair_pos = pair_pos;
+    a.out_f32 = out_f32;
     return from_hip(launch_dec_down_combine(a, out, s));
   }
   e = launch_proj_gemv(a, act, gemv_grid(a), s);
   if (e != hipSuccess) return MOE_E_DEVICE;
   return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
-                                 n_shared, out, s));
+                                 n_shared, out, out_f32, s));
 }
 
 moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H, int I,
@@ -554,7 +557,7 @@ moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
                                const int32_t* sorted_pair,
                                const int32_t* pair_pos, const int32_t* tiles,
                                const int32_t* n_tiles, int tile_m,
-                               uint16_t* out, void* workspace,
+                               void* out, void* workspace,
                                size_t ws_bytes, int flags, void* stream) {
   return down_impl(act, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared,
                    topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles,
@@ -566,12 +569,13 @@ moe_status moe_dbg_w4a8_gateup_partials(
     const moe_qmat* w13, const moe_qmat* w13_shared, int n_shared,
     int I_shared, const int32_t* offsets, const int32_t* sorted_pair,
     const int32_t* tiles, const int32_t* n_tiles, int tile_m, void* h,
-    void* workspace, size_t ws_bytes, int32_t* partials, int ng_ld,
+    void* workspace, size_t ws_bytes, int flags, int32_t* partials, int ng_ld,
     void* stream) {
   if (!partials) return MOE_E_INVAL;
+  if ((flags & MOE_PATH_MASK) == MOE_PATH_MFMA) return MOE_E_UNSUPPORTED;   // A16 only
   return gateup_impl(MOE_A8, x, T, H, I, E, k, w13, w13_shared, n_shared,
                      I_shared, offsets, sorted_pair, tiles, n_tiles, tile_m, h,
-                     workspace, ws_bytes, MOE_PATH_GEMV, partials, ng_ld, stream);
+                     workspace, ws_bytes, flags, partials, ng_ld, stream);
 }
 
 moe_status moe_dbg_w4a8_down_partials(
@@ -579,12 +583,13 @@ moe_status moe_dbg_w4a8_down_partials(
     const moe_qmat* w2_shared, int n_shared, int I_shared,
     const float* topk_w, const int32_t* offsets, const int32_t* sorted_pair,
     const int32_t* pair_pos, const int32_t* tiles, const int32_t* n_tiles,
-    int tile_m, uint16_t* out, void* workspace, size_t ws_bytes,
+    int tile_m, void* out, void* workspace, size_t ws_bytes, int flags,
     int32_t* partials, int ng_ld, void* stream) {
   if (!partials) return MOE_E_INVAL;
+  if ((flags & MOE_PATH_MASK) == MOE_PATH_MFMA) return MOE_E_UNSUPPORTED;   // A16 only
   return down_impl(MOE_A8, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared,
                    topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles,
-                   tile_m, out, workspace, ws_bytes, MOE_PATH_GEMV, partials,
+                   tile_m, out, workspace, ws_bytes, flags, partials,
                    ng_ld, stream);
 }
 
@@ -622,7 +627,7 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, 
                         int I_shared, int tile_m, int32_t* topk_ids, float* topk_w,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                         int32_t* pair_pos, int32_t* tiles, int32_t* n_tiles, void* h,
-                        uint16_t* out, void* workspace, size_t ws_bytes, int flags,
+                        void* out, void* workspace, size_t ws_bytes, int flags,
                         void* stream) {
   const bool one = (flags & MOE_LAYER_ONE_LAUNCH) != 0;
   flags &= ~MOE_LAYER_ONE_LAUNCH;   // the component calls do not take it
@@ -637,7 +642,8 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, 
         !sorted_pair || !pair_pos || !tiles || !n_tiles || !h || !out)
       return MOE_E_INVAL;
     if (n_shared > 0 && (!w13_shared || !w2_shared)) return MOE_E_INVAL;
-    if (!aligned(x, 16) || !aligned(h, 16) || !aligned(tiles, 16) || !aligned(out, 8))
+    if (!aligned(x, 16) || !aligned(h, 16) || !aligned(tiles, 16) ||
+        !aligned(out, (flags & MOE_OUT_F32) ? 16 : 8))
       return MOE_E_INVAL;
   }
   const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
@@ -685,6 +691,7 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, 
     ag.ld_out = ld_h;
     ad.topk_w = topk_w;
     ad.pair_pos = pair_pos;
+    ad.out_f32 = (flags & MOE_OUT_F32) ? 1 : 0;
     bool launched = false;
     const hipError_t e = launch_dec_layer(
         ag, ad, logits, renormalize, tile_m, topk_ids, topk_w, counts, offsets, sorted_pair,

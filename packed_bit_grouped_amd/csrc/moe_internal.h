@@ -62,6 +62,7 @@ struct ProjArgs {
   // sorted row of every pair
   const float* topk_w;
   const int32_t* pair_pos;
+  int out_f32;                 // the combined output is fp32 (else bf16)
   int32_t* partials;           // A8 test hook (null otherwise)
   int ng_ld;
   int part_rows;               // row stride (in weight rows) of partials
@@ -101,7 +102,7 @@ bool dec_gateup_ok(int T, int H, int tile_m);
 bool dec_down_ok(int T, int k, int E, int n_shared, int H, int I, int I_shared, int ld,
                  int tile_m, int max_tiles);
 hipError_t launch_dec_gateup(const ProjArgs& a, hipStream_t st);
-hipError_t launch_dec_down_combine(const ProjArgs& a, uint16_t* out, hipStream_t st);
+hipError_t launch_dec_down_combine(const ProjArgs& a, void* out, hipStream_t st);
 // Route + permute + gate/up in one launch (T * k <= 64, E <= 512).
 bool dec_route_gateup_ok(int T, int H, int E, int k, int tile_m);
 hipError_t launch_dec_route_gateup(const ProjArgs& a, const float* logits, int renorm,
@@ -122,7 +123,7 @@ int dec_layer_one_launch(int T, int H, int I, int I_shared, int E, int k, int n_
 hipError_t launch_dec_layer(const ProjArgs& ag, const ProjArgs& ad, const float* logits,
                             int renorm, int tile_m, int32_t* ids, float* w, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                            int32_t* tiles, int32_t* n_tiles, uint16_t* out, uint32_t* flags,
+                            int32_t* tiles, int32_t* n_tiles, void* out, uint32_t* flags,
                             bool& launched, hipStream_t st);
 // Tiles of at most 16 rows on 16x16 MFMAs (proj_m16.hip).  A8 inputs are
 // int8 rows (a.in_q, stride a.ld_in) with fp32 row scales (a.in_s): x for
@@ -132,8 +133,9 @@ bool m16_ok(int act, int mode, int T, int K, int K_sh, int tile_m);
 // h, a.in_q null) when they fit one staging batch.
 bool m16_quant_ok(int mode, int T, int K, int K_sh);
 hipError_t launch_proj_m16(const ProjArgs& a, int act, hipStream_t st);
+// out: bf16 [T][H], or fp32 [T][H] when out_f32
 hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
                           const int32_t* pair_pos, int T, int k, int H, int P,
-                          int n_shared, uint16_t* out, hipStream_t st);
+                          int n_shared, void* out, int out_f32, hipStream_t st);
 
 }  // namespace moe

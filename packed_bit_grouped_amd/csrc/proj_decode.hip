@@ -668,7 +668,7 @@ __device__ __forceinline__ void dn_run(const DnSlots<CPL>& d, int i, const ProjA
 // out[t][n] = sum_j w[t][j] * y[pair_pos[t*k+j]][n] + sum_s y_s[t][n] for
 // the columns n0..n0+3, in that order.
 __device__ __forceinline__ void dn_combine(const ProjArgs& a, const int* ppos, const float* gw,
-                                           const float* yb, uint16_t* __restrict__ out, int n0) {
+                                           const float* yb, void* __restrict__ out, int n0) {
   const int H = a.U;
   for (int idx = threadIdx.x; idx < a.T * kDecDnCols; idx += kDecThreads) {
     const int t = idx / kDecDnCols, cc = idx - t * kDecDnCols;
@@ -691,13 +691,14 @@ __device__ __forceinline__ void dn_combine(const ProjArgs& a, const int* ppos, c
         if (pp[u] >= 0) acc = fmaf(wj[u], yv[u], acc);
     }
     for (int s = 0; s < a.n_shared; ++s) acc += yb[(size_t)(a.P + s * a.T + t) * kDecDnCols + cc];
-    out[(size_t)t * H + n0 + cc] = (uint16_t)f32_to_bf16(acc);
+    if (a.out_f32) static_cast<float*>(out)[(size_t)t * H + n0 + cc] = acc;
+    else static_cast<uint16_t*>(out)[(size_t)t * H + n0 + cc] = (uint16_t)f32_to_bf16(acc);
   }
 }
 
 template <int MAXT, int CPL>
 __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs a, int R_rows,
-                                                                       uint16_t* __restrict__ out) {
+                                                                       void* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char smem[];
   touch_args(a);
   // LDS: tile list, descriptor tables, pair positions and gate weights
@@ -773,7 +774,7 @@ struct LayerArgs {
   int n_gu;        // gate/up work items
   int n_dn;        // down column blocks
   int R_rows;      // h rows: P + n_shared * T
-  uint16_t* out;
+  void* out;       // bf16 or fp32 (ad.out_f32)
   uint32_t* flags; // kLayerFlags barrier flags, all equal between launches
 };
 
@@ -794,7 +795,21 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* flags, int n, int32_t* er
   // phase of this launch: every flag still holds the previous launch's value
   const uint32_t target =
       1u - __hip_atomic_load(flags + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Ordering (h before the flags, flags before the h reads) without L2
+  // write-back or invalidation: every h store and h load of this launch is
+  // an agent-scope access (it goes through to the memory side, which all
+  // XCDs share), and so are the flag accesses.  (1) The compiler may not
+  // move a memory access across the signal fences below.  (2) The wait
+  // for every outstanding memory operation of the wave returns only once
+  // its h stores are acknowledged at agent scope, so they are visible to
+  // every workgroup before any flag store of the workgroup is issued
+  // (the LDS barrier orders the waves of the workgroup).  (3) A poller
+  // leaves the loop only after its flag loads have returned the target
+  // (the exit depends on their values), and its h loads are issued after
+  // that, at agent scope, so they read the stored h.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);   // this wave's h stores (and loads) complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   lds_barrier();
   for (int i = blockIdx.x + tid * n; i < kLayerFlags; i += kDecThreads * n)
     __hip_atomic_store(flags + i, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -820,6 +835,7 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* flags, int n, int32_t* er
     }
   }
   lds_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // no h load above the wait
   return *ok_lds != 0;
 }
 
@@ -1064,7 +1080,7 @@ hipError_t launch_dec_route_gateup(const ProjArgs& a_in, const float* logits, in
 
 template <int MAXT>
 static hipError_t dn_cpl(const ProjArgs& a, int cpl, dim3 grid, size_t lds, int R_rows,
-                         uint16_t* out, hipStream_t st) {
+                         void* out, hipStream_t st) {
   switch (cpl) {
     case 1: dec_down_combine_kernel<MAXT, 1><<<grid, kDecThreads, lds, st>>>(a, R_rows, out); break;
     default: dec_down_combine_kernel<MAXT, 2><<<grid, kDecThreads, lds, st>>>(a, R_rows, out); break;
@@ -1072,7 +1088,7 @@ static hipError_t dn_cpl(const ProjArgs& a, int cpl, dim3 grid, size_t lds, int 
   return hipGetLastError();
 }
 
-hipError_t launch_dec_down_combine(const ProjArgs& a_in, uint16_t* out, hipStream_t st) {
+hipError_t launch_dec_down_combine(const ProjArgs& a_in, void* out, hipStream_t st) {
   ProjArgs a = a_in;
   const int Kmax = a.n_shared > 0 && a.K_sh > a.K ? a.K_sh : a.K;
   const int cpl = dec_cpl(Kmax, kDecDnLanes);
@@ -1194,7 +1210,7 @@ int dec_layer_one_launch(int T, int H, int I, int I_shared, int E, int k, int n_
 hipError_t launch_dec_layer(const ProjArgs& ag_in, const ProjArgs& ad_in, const float* logits,
                             int renorm, int tile_m, int32_t* ids, float* w, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                            int32_t* tiles, int32_t* n_tiles, uint16_t* out, uint32_t* flags,
+                            int32_t* tiles, int32_t* n_tiles, void* out, uint32_t* flags,
                             bool& launched, hipStream_t st) {
   launched = false;
   ProjArgs ag = ag_in, ad = ad_in;

@@ -276,12 +276,15 @@ __device__ __forceinline__ void m16_q_amax(int items, int S, const M16QRegs<MODE
   }
 }
 
-// a8_code(v, s) without a division per element: y = v * (1/s) lies within
-// a few ulps of the IEEE quotient, so the two round to the same integer
+// a8_code(v, s) without a division per element: for a normal reciprocal,
+// y = v * (1/s) lies within a few ulps of the IEEE quotient, so the two round to the same integer
 // unless the quotient is within 2^-13 of a half-integer (|y| <= 127.5 and
 // an ulp there is 2^-17); those rare elements take the exact path.
 __device__ __forceinline__ int m16_a8_code(float v, float s, float rs) {
   if (s == 0.0f) return 0;
+  // a scale below 2^-128 has no finite reciprocal (v * inf would give inf
+  // or NaN): those rows take the exact division
+  if (!(rs <= 0x1.fffffep127f)) return a8_code(v, s);
   const float y = v * rs;
   const float f = y - floorf(y);
   if (fabsf(f - 0.5f) < 0x1p-13f) return a8_code(v, s);
@@ -328,7 +331,7 @@ __device__ __forceinline__ float m16_scale(const uint16_t* ssc, int lrow, int ng
   return fp16_to_f32(ssc[lrow * ng + g]);
 }
 
-template <int MODE, int ACT, int BITS, bool WIDE, bool QX>
+template <int MODE, int ACT, int BITS, bool WIDE, bool QX, bool PART>
 __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, bool is_sh, int e,
                                          int r_begin, int nt, int U, int K, int u0, int mt,
                                          const int (&srow)[kM16StageIt], unsigned char* smem) {
@@ -502,6 +505,26 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
         D[j] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
       }
     } else {
+      if constexpr (PART) {
+        // the exact int32 sums of the group (the MFMA sums hold 16 v or
+        // 64 v per code, so an arithmetic shift divides exactly)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int wr = MODE == 0 ? (j == 0 ? 0 : U) + u0 + wave * 16 + n
+                                   : u0 + wave * 64 + 16 * j + n;
+          if (wr - (MODE == 0 && j == 1 ? U : 0) < U) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = 4 * qd + i;
+              if (t < nt) {
+                const int orow = (is_sh ? a.P + e * a.T : 0) + r_begin + t;
+                a.partials[((size_t)orow * a.part_rows + wr) * a.ng_ld + g] =
+                    Di[j][i] >> (BITS == 4 ? 4 : 6);
+              }
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const float sc = m16_scale(ssc, lrow[j], ng, g) * a8_unit;
@@ -582,7 +605,7 @@ __device__ __forceinline__ void m16_tile(const ProjArgs& a, const moe_qmat& q, b
 
 // Grid: (shared slots + host bound of tiles) x blocks of units; blocks past
 // the device-side tile count or past an expert's units exit at once.
-template <int MODE, int ACT, bool QX>
+template <int MODE, int ACT, bool QX, bool PART>
 __global__ __launch_bounds__(kM16Threads) void proj_m16_kernel(ProjArgs a, int mt, int nblk) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int slot = blockIdx.x / nblk;
@@ -644,11 +667,11 @@ __global__ __launch_bounds__(kM16Threads) void proj_m16_kernel(ProjArgs a, int m
     return;
   }
   if (q.bits == 4 && q.group >= 128)
-    m16_tile<MODE, ACT, 4, true, QX>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
+    m16_tile<MODE, ACT, 4, true, QX, PART>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
   else if (q.bits == 4)
-    m16_tile<MODE, ACT, 4, false, QX>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
+    m16_tile<MODE, ACT, 4, false, QX, PART>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
   else
-    m16_tile<MODE, ACT, 2, false, QX>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
+    m16_tile<MODE, ACT, 2, false, QX, PART>(a, q, is_sh, e, r_begin, nt, U, K, u0, mt, srow, smem);
 }
 
 int m16_rows(int T) { return T < kM16MaxRows ? T : kM16MaxRows; }
@@ -692,14 +715,20 @@ hipError_t launch_proj_m16(const ProjArgs& a_in, int act, hipStream_t st) {
   const bool qx = act == MOE_A8 && a.in_q == nullptr;
   if (qx && !m16_quant_ok(a.mode, a.T, a.K, a.K_sh)) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid), b(kM16Threads);
+  // A8 test hook: the same kernels, also storing the exact group sums
+  const bool part = act == MOE_A8 && a.partials != nullptr;
   if (a.mode == 0) {
-    if (act == MOE_A16) proj_m16_kernel<0, MOE_A16, false><<<g, b, lds, st>>>(a, mt, nblk);
-    else if (qx) proj_m16_kernel<0, MOE_A8, true><<<g, b, lds, st>>>(a, mt, nblk);
-    else proj_m16_kernel<0, MOE_A8, false><<<g, b, lds, st>>>(a, mt, nblk);
+    if (act == MOE_A16) proj_m16_kernel<0, MOE_A16, false, false><<<g, b, lds, st>>>(a, mt, nblk);
+    else if (qx && part) proj_m16_kernel<0, MOE_A8, true, true><<<g, b, lds, st>>>(a, mt, nblk);
+    else if (qx) proj_m16_kernel<0, MOE_A8, true, false><<<g, b, lds, st>>>(a, mt, nblk);
+    else if (part) proj_m16_kernel<0, MOE_A8, false, true><<<g, b, lds, st>>>(a, mt, nblk);
+    else proj_m16_kernel<0, MOE_A8, false, false><<<g, b, lds, st>>>(a, mt, nblk);
   } else {
-    if (act == MOE_A16) proj_m16_kernel<1, MOE_A16, false><<<g, b, lds, st>>>(a, mt, nblk);
-    else if (qx) proj_m16_kernel<1, MOE_A8, true><<<g, b, lds, st>>>(a, mt, nblk);
-    else proj_m16_kernel<1, MOE_A8, false><<<g, b, lds, st>>>(a, mt, nblk);
+    if (act == MOE_A16) proj_m16_kernel<1, MOE_A16, false, false><<<g, b, lds, st>>>(a, mt, nblk);
+    else if (qx && part) proj_m16_kernel<1, MOE_A8, true, true><<<g, b, lds, st>>>(a, mt, nblk);
+    else if (qx) proj_m16_kernel<1, MOE_A8, true, false><<<g, b, lds, st>>>(a, mt, nblk);
+    else if (part) proj_m16_kernel<1, MOE_A8, false, true><<<g, b, lds, st>>>(a, mt, nblk);
+    else proj_m16_kernel<1, MOE_A8, false, false><<<g, b, lds, st>>>(a, mt, nblk);
   }
   return hipGetLastError();
 }

@@ -46,7 +46,7 @@ hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y, int ld_y, const float* __restrict__ topk_w,
     const int32_t* __restrict__ pair_pos, int T, int k, int H, int P,
-    int n_shared, uint16_t* __restrict__ out) {
+    int n_shared, void* __restrict__ out, int out_f32) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= H) return;
@@ -82,19 +82,23 @@ __global__ __launch_bounds__(256) void combine_kernel(
     acc.z += v.z;
     acc.w += v.w;
   }
-  uint2 o;
-  o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
-  o.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
-  *reinterpret_cast<uint2*>(out + (size_t)t * H + n) = o;
+  if (out_f32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H + n) = acc;
+  } else {
+    uint2 o;
+    o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
+    o.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * H + n) = o;
+  }
 }
 
 hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
                           const int32_t* pair_pos, int T, int k, int H, int P,
-                          int n_shared, uint16_t* out, hipStream_t st) {
+                          int n_shared, void* out, int out_f32, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const dim3 grid((H / 4 + 255) / 256, T);
   combine_kernel<<<grid, 256, 0, st>>>(y, ld_y, topk_w, pair_pos, T, k, H, P,
-                                       n_shared, out);
+                                       n_shared, out, out_f32);
   return hipGetLastError();
 }
 

@@ -102,7 +102,7 @@ class LayerBuffers:
     """Every per-step buffer of one layer shape, allocated once."""
 
     def __init__(self, T, H, I, E, k, n_shared=0, I_shared=0, act=L.MOE_A16,
-                 tile_m=None, device="cuda"):
+                 tile_m=None, device="cuda", out_f32=False):
         torch = _torch()
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
         self.n_shared, self.I_shared, self.act = n_shared, I_shared, act
@@ -123,10 +123,14 @@ class LayerBuffers:
         self.tiles = torch.empty((self.max_tiles, 4), **i32)
         self.n_tiles = torch.zeros(1, **i32)
         hdt = torch.int16 if act == L.MOE_A16 else torch.float32
-        self.h = torch.empty((max(self.R, 1), self.ld_h), dtype=hdt, device=dev)
+        # zeroed once: the columns past a shorter expert's I are never written
+        self.h = torch.zeros((max(self.R, 1), self.ld_h), dtype=hdt, device=dev)
         self.ws_bytes = L.moe_workspace_bytes(act, T, H, I, E, k, n_shared, I_shared)
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
-        self.out = torch.empty((max(T, 1), H), dtype=torch.int16, device=dev)
+        # bf16 bit patterns, or fp32 (the unrounded sum, MOE_OUT_F32)
+        self.out_flags = L.MOE_OUT_F32 if out_f32 else 0
+        self.out = torch.empty((max(T, 1), H), dtype=torch.float32 if out_f32 else torch.int16,
+                               device=dev)
 
     def error_word(self) -> int:
         return int(self.ws[:4].view(_torch().int32).item())
@@ -148,6 +152,7 @@ def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
     moe_w4_route_gateup_silu and the rest through moe_w4_down_combine;
     otherwise every call is issued separately."""
     T, H, I, E, k = B.T, B.H, B.I, B.E, B.k
+    flags |= B.out_flags
     if not (fused and one_call):
         flags &= ~L.MOE_LAYER_ONE_LAUNCH   # only moe_w4_layer takes it
     if fused and one_call:
@@ -205,11 +210,11 @@ class DeviceLayer:
         bank = upload_bank(layer.experts, layer.shared, dev)
         return cls(layer.cfg, x, logits, bank)
 
-    def buffers(self, act=None, tile_m=None) -> LayerBuffers:
+    def buffers(self, act=None, tile_m=None, out_f32=False) -> LayerBuffers:
         c = self.cfg
         a = {"a16": L.MOE_A16, "a8": L.MOE_A8}[act or c.act]
         return LayerBuffers(c.T, c.H, c.I, c.E, c.k, c.n_shared, c.I_shared, a,
-                            tile_m, self.x.device)
+                            tile_m, self.x.device, out_f32)
 
     def run(self, B: LayerBuffers, flags: int = 0, stream=None, fused: bool = True,
             one_call: bool = True) -> None:

@@ -7,4 +7,5 @@ activation quantization, no projections); both the CPU oracle and the GPU
 library are fed from here and never from each other.
 """
 from .gen import (CONFIGS, LAYERS, LayerConfig, make_layer, config_by_id,  # noqa: F401
-                  pack_codes, quantize_matrix, bf16_bits_from_f32)
+                  pack_codes, quantize_matrix, bf16_bits_from_f32,
+                  with_random_codes, with_x_rows)

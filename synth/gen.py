@@ -300,6 +300,33 @@ def make_layer(cfg: LayerConfig, seed: int = 0, workers: Optional[int] = None,
     return layer
 
 
+def with_random_codes(layer: Layer, seed: int = 0) -> Layer:
+    """The same layer with every packed code byte (routed and shared
+    experts, both matrices) replaced by uniformly random bytes, scales
+    kept.  Every bit pattern then occurs, including the codes the
+    quantizer never emits (int4 -8, int2 -2)."""
+    def rnd(qm: QMat, tag: int, i: int, m: int) -> QMat:
+        rng = _rng(seed, layer.cfg.key, 100 + tag, i, m)
+        codes = rng.integers(0, 256, size=qm.codes.shape, dtype=np.uint8)
+        return QMat(codes, qm.scales.copy(), qm.bits, qm.group, qm.N, qm.K)
+
+    experts = [Expert(rnd(ex.w13, 0, i, 0), rnd(ex.w2, 0, i, 1))
+               for i, ex in enumerate(layer.experts)]
+    shared = [Expert(rnd(ex.w13, 1, i, 0), rnd(ex.w2, 1, i, 1))
+              for i, ex in enumerate(layer.shared)]
+    return dataclasses.replace(layer, experts=experts, shared=shared)
+
+
+def with_x_rows(layer: Layer, rows: Dict[int, np.ndarray]) -> Layer:
+    """The same layer with token rows of x replaced: rows maps a token to
+    float32 values [H] (stored as bf16, round to nearest even).  The router
+    logits are kept as they are (they are an input of the layer)."""
+    x = layer.x_bf16.copy()
+    for t, v in rows.items():
+        x[t] = bf16_bits_from_f32(np.asarray(v, dtype=np.float32).reshape(1, -1))[0]
+    return dataclasses.replace(layer, x_bf16=x)
+
+
 def _cfg_hash(cfg: LayerConfig) -> str:
     import hashlib
     return hashlib.sha1(repr(dataclasses.astuple(cfg)).encode()).hexdigest()[:10]

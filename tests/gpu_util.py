@@ -21,10 +21,12 @@ def bf16_bits_to_f64(u16):
 
 
 def run_layer_gpu(dl, act=None, tile_m=None, flags=0, stream=None, fused=True,
-                  one_call=True):
-    """Run one layer step on the device; returns host copies of everything."""
+                  one_call=True, out_f32=False):
+    """Run one layer step on the device; returns host copies of everything
+    (out as float64 values: of the bf16 output, or with out_f32 of the fp32
+    output the library writes under MOE_OUT_F32)."""
     torch = torch_mod()
-    B = dl.buffers(act, tile_m)
+    B = dl.buffers(act, tile_m, out_f32)
     dl.run(B, flags, stream, fused, one_call)
     torch.cuda.synchronize()
     return collect(B), B
@@ -38,7 +40,9 @@ def collect(B):
         "counts": to_np(B.counts), "offsets": to_np(B.offsets),
         "sorted_pair": to_np(B.sorted_pair)[:B.P], "pair_pos": to_np(B.pair_pos)[:B.P],
         "tiles": to_np(B.tiles)[:nt], "n_tiles": nt,
-        "out": bf16_bits_to_f64(to_np(B.out)[:B.T]),
+        "out": (to_np(B.out)[:B.T].astype(np.float64) if B.out_flags else
+                bf16_bits_to_f64(to_np(B.out)[:B.T])),
+        "out_bits": None if B.out_flags else to_np(B.out)[:B.T].astype(np.uint16),
         "err": int(B.ws[:4].view(torch.int32).item()),
     }
     if B.act == 0:
@@ -78,3 +82,37 @@ def h_gate(got, ref, act):
         bound = np.maximum(bound, 2.0 ** -7 * np.abs(ref))
     worst = float((d / np.maximum(bound, 1e-300)).max()) if d.size else 0.0
     return (rl2 <= 5e-3 and worst <= 1.0), rl2, worst
+
+
+def bf16_rne_bits(f32):
+    """fp32 values -> bf16 bit patterns, round to nearest even (finite input)."""
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def worst_error(got, ref):
+    """(flat index, ref value, got value) of the largest absolute error."""
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    i = int(np.argmax(np.abs(got - ref))) if ref.size else 0
+    return i, float(ref[i]) if ref.size else 0.0, float(got[i]) if ref.size else 0.0
+
+
+def check_out(g_bf16, g_f32, ref, tag=""):
+    """The output gate, on the computation and on the stored result:
+    the fp32 output (the combined sum before rounding) meets rel-L2 <=
+    5e-3 and max-abs <= 2e-2 * rms(ref), and the bf16 output is exactly
+    its round-to-nearest-even.  (The bf16 rounding itself can exceed
+    2e-2 * rms: its half-unit is 2^-9..2^-8 of |out|, e.g. 2^-7 = 0.0078
+    for |out| in [2, 4), so it is checked as this identity instead.)"""
+    ok, rl2, mabs, rms = float_gate(g_f32["out"], ref)
+    i, rv, gv = worst_error(g_f32["out"], ref)
+    print(f"[parity] {tag} out fp32 rel-L2 {rl2:.2e} max-abs {mabs:.2e} (gate {2e-2 * rms:.2e}) "
+          f"worst at {i}: ref {rv:.6g} got {gv:.6g}", flush=True)
+    assert ok, ("out", rl2, mabs, rms, i, rv, gv)
+    want = bf16_rne_bits(g_f32["out"].astype(np.float32))
+    assert np.array_equal(g_bf16["out_bits"], want), "bf16 output is not the RNE of the fp32 output"
+    ok2, rl2b, mabsb, _ = float_gate(g_bf16["out"], ref)
+    print(f"[parity] {tag} out bf16 rel-L2 {rl2b:.2e} max-abs {mabsb:.2e}", flush=True)
+    assert rl2b <= 5e-3

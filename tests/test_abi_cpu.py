@@ -128,7 +128,7 @@ def test_gateup_validation():
     assert _gateup(workspace=None) == L.MOE_E_WORKSPACE
     assert _gateup(workspace=FAKE + 64) == L.MOE_E_WORKSPACE  # 256-byte alignment
     assert _gateup(flags=8) == L.MOE_E_INVAL
-    assert _gateup(flags=16) == L.MOE_E_INVAL
+    assert _gateup(flags=32) == L.MOE_E_INVAL
     assert _gateup(flags=L.MOE_QUANT_SEPARATE | L.MOE_PATH_MFMA16, act=1) == L.MOE_E_DEVICE
     # forced 16-row MFMA tiles: tiles of at most 16 rows, activations in LDS
     assert _gateup(flags=L.MOE_PATH_MFMA16, tile_m=32) == L.MOE_E_UNSUPPORTED
@@ -155,6 +155,9 @@ def test_down_validation():
     assert call(topk_w=None) == L.MOE_E_INVAL
     assert call(pair_pos=None) == L.MOE_E_INVAL
     assert call(out=FAKE + 2) == L.MOE_E_INVAL
+    assert call(out=FAKE + 8, flags=L.MOE_OUT_F32) == L.MOE_E_INVAL   # fp32 out: 16 bytes
+    assert call(out=FAKE + 8) == L.MOE_E_DEVICE
+    assert call(flags=L.MOE_OUT_F32) == L.MOE_E_DEVICE
     assert call(ws_bytes=100) == L.MOE_E_WORKSPACE
     assert call(T=0, h=None) == L.MOE_OK
     assert call(flags=L.MOE_PATH_MFMA16, tile_m=17) == L.MOE_E_UNSUPPORTED
@@ -172,6 +175,16 @@ def test_debug_hooks_need_partials():
     assert L.moe_dbg_w4a8_gateup_partials(
         FAKE, 4, 256, 128, 8, 2, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, 16,
         FAKE, FAKE, 1 << 30, None, 8, stream=0, check=False) == L.MOE_E_INVAL
+    # the hooks take the product's path choice; the matrix-core prefill path is A16 only
+    for flags, want in ((L.MOE_PATH_MFMA, L.MOE_E_UNSUPPORTED), (L.MOE_PATH_AUTO, L.MOE_E_DEVICE),
+                        (L.MOE_PATH_GEMV, L.MOE_E_DEVICE), (L.MOE_PATH_MFMA16, L.MOE_E_DEVICE)):
+        assert L.moe_dbg_w4a8_gateup_partials(
+            FAKE, 4, 256, 128, 8, 2, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, 16,
+            FAKE, FAKE, 1 << 30, FAKE, 8, flags=flags, stream=0, check=False) == want
+        assert L.moe_dbg_w4a8_down_partials(
+            FAKE, 4, 256, 128, 8, 2, FAKE, None, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, 16, FAKE, FAKE, 1 << 30, FAKE, 8, flags=flags, stream=0,
+            check=False) == want
 
 
 def test_route_permute_validation():
@@ -206,7 +219,7 @@ def test_layer_validation():
     assert call(renormalize=2) == L.MOE_E_INVAL
     assert call(act=2) == L.MOE_E_INVAL
     assert call(k=129) == L.MOE_E_INVAL
-    assert call(flags=16) == L.MOE_E_INVAL
+    assert call(flags=32) == L.MOE_E_INVAL
     assert call(out=None) == L.MOE_E_INVAL
     assert call(w2_shared=None) == L.MOE_E_INVAL
     assert call(workspace=None) == L.MOE_E_WORKSPACE

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from synth import LAYERS, LayerConfig, make_layer
-from tests.gpu_util import (bf16_bits_to_f64, collect, float_gate, h_gate,
+from tests.gpu_util import (bf16_bits_to_f64, check_out, collect, float_gate, h_gate,
                             run_layer_gpu, to_np, torch_mod)
 from tests.minis import MINIS
 
@@ -88,15 +88,13 @@ def _check_layer(cfg, act=None, tile_m=16, flags=0):
     act = act or cfg.act
     dl = _dev(cfg)
     g, B = run_layer_gpu(dl, act, tile_m, flags)
+    g32, _ = run_layer_gpu(dl, act, tile_m, flags, out_f32=True)
     o = oracle.oracle_layer(_layer(cfg), act=act, tile_m=tile_m)
     _check_integer_stages(g, o, cfg)
     gh, oh = (g["h"], o["h"]) if act == "a16" else (g["h32"], o["h32"])
     ok, rl2, worst = h_gate(_valid_h(gh, cfg), _valid_h(oh, cfg), act)
     assert ok, ("h", rl2, worst)
-    ok, rl2, mabs, rms = float_gate(g["out"], o["out"])
-    print(f"[parity] {cfg.name} {act}: out rel-L2 {rl2:.2e} max-abs {mabs:.2e} "
-          f"(gate {2e-2 * rms:.2e})", flush=True)
-    assert ok, ("out", rl2, mabs, rms)
+    check_out(g, g32, o["out"], f"{cfg.name} {act} flags={flags}")
     return g, o, dl, B
 
 
@@ -388,17 +386,32 @@ def test_a8_quantizer_bit_exact():
         assert np.array_equal(to_np(s), os_)
 
 
-@pytest.mark.parametrize("name", ["c3", "mid_mixed_a8", "mid_g128_a8_shared", "mixed_shared_a8"])
-def test_a8_partials_bit_exact(name):
+A8_PARTIAL_CASES = [(n, f, False) for n in ("c3", "mid_mixed_a8", "mid_g128_a8_shared",
+                                             "mixed_shared_a8", "mid_g256", "e288")
+                    for f in (0, 1)] + \
+                   [("mixed_shared_a8", 0, True), ("mid_mixed_a8", 0, True),
+                    ("mid_g128_a8_shared", 1, True), ("c3", 0, True)]
+
+
+@pytest.mark.parametrize("name,flags,raw", A8_PARTIAL_CASES)
+def test_a8_partials_bit_exact(name, flags, raw):
     """Stage 1: int32 per-group partials of int8 x against int codes equal
     the oracle's exactly.  Stage 2: the down call's int8 h codes equal the
     oracle quantizer applied to the GPU's fp32 h, and its int32 partials
-    equal the oracle's partials computed from those codes."""
+    equal the oracle's partials computed from those codes.  flags 0 runs
+    the kernels the product runs for the shape (the 16-row int8 matrix
+    tiles, with the int8 x rows made in the gate/up kernel), flags 1 the
+    split-K GEMV; raw: code bytes drawn uniformly (int4 -8, int2 -2)."""
     torch = torch_mod()
     from packed_bit_grouped_amd import _lib as L
+    from packed_bit_grouped_amd.layer import DeviceLayer
+    from synth import with_random_codes
     cfg = LAYERS["decode_w4a8_t64"] if name == "c3" else (MINIS.get(name) or MID[name])
     layer = _layer(cfg)
-    dl = _dev(cfg)
+    if raw:
+        layer = with_random_codes(layer, seed=3)
+    print(f"[parity] partials {cfg.name} flags={flags} raw={raw}", flush=True)
+    dl = DeviceLayer.from_synth(layer)
     B = dl.buffers("a8", 16)
     c = cfg
     L.moe_route_topk(dl.logits, c.T, c.E, c.k, c.renormalize, B.ids, B.w)
@@ -411,11 +424,11 @@ def test_a8_partials_bit_exact(name):
     L.moe_dbg_w4a8_gateup_partials(dl.x, c.T, c.H, c.I, c.E, c.k, dl.bank.w13,
                                    dl.bank.w13_sh, c.n_shared, c.I_shared, B.offsets,
                                    B.sorted_pair, B.tiles, B.n_tiles, B.tile_m, B.h,
-                                   B.ws, B.ws_bytes, p1, ng1)
+                                   B.ws, B.ws_bytes, p1, ng1, flags=flags)
     L.moe_dbg_w4a8_down_partials(B.h, c.T, c.H, c.I, c.E, c.k, dl.bank.w2, dl.bank.w2_sh,
                                  c.n_shared, c.I_shared, B.w, B.offsets, B.sorted_pair,
                                  B.pair_pos, B.tiles, B.n_tiles, B.tile_m, B.out, B.ws,
-                                 B.ws_bytes, p2, ng2)
+                                 B.ws_bytes, p2, ng2, flags=flags)
     torch.cuda.synchronize()
     g = collect(B)
     ids, _ = oracle.route_topk(layer.logits, c.k, c.renormalize)
@@ -454,9 +467,14 @@ def test_a8_partials_bit_exact(name):
         ex = layer.experts[e] if s is None else layer.shared[s]
         ng = ex.w2.K // ex.w2.group
         assert np.array_equal(P2[rows, :, :ng], Pg), ("stage2", e, s)
+    assert g["err"] == 0
+    # the hooks compute what the product calls compute
+    g2, _ = run_layer_gpu(dl, "a8", 16, flags)
+    assert np.array_equal(g2["h32"][:c.T * c.k], g["h32"][:c.T * c.k])
+    assert np.array_equal(g2["out"], g["out"])
+    g32, _ = run_layer_gpu(dl, "a8", 16, flags, out_f32=True)
     o = oracle.oracle_layer(layer, act="a8", tile_m=16)
-    ok, rl2, mabs, rms = float_gate(g["out"], o["out"])
-    assert ok, (rl2, mabs, rms)
+    check_out(g2, g32, o["out"], f"partials {cfg.name}")
 
 
 def test_prefill_layer_sampled_tokens():
@@ -467,6 +485,7 @@ def test_prefill_layer_sampled_tokens():
     dl = _dev(cfg)
     tile_m = 64
     g, B = run_layer_gpu(dl, "a16", tile_m)
+    g32, _ = run_layer_gpu(dl, "a16", tile_m, out_f32=True)
     ids, w = oracle.route_topk(layer.logits, cfg.k)
     perm = oracle.permute(ids, cfg.E, tile_m)
     assert np.array_equal(g["ids"], ids)
@@ -477,15 +496,66 @@ def test_prefill_layer_sampled_tokens():
     assert g["err"] == 0
     toks = list(np.random.default_rng(4).choice(cfg.T, 24, replace=False)) + [0, cfg.T - 1]
     s = oracle.oracle_token_outputs(layer, toks)
-    ok, rl2, mabs, rms = float_gate(g["out"][toks], s["out"])
-    print(f"[parity] prefill sample: rel-L2 {rl2:.2e} max-abs {mabs:.2e}", flush=True)
-    assert ok, (rl2, mabs, rms)
+    sub = lambda d: {"out": d["out"][toks],
+                     "out_bits": None if d["out_bits"] is None else d["out_bits"][toks]}
+    check_out(sub(g), sub(g32), s["out"], "prefill sample")
     # h rows of the sampled tokens' pairs (bf16 on both sides)
     for n, t in enumerate(toks[:6]):
         for j in range(cfg.k):
             r = perm["pair_pos"][t * cfg.k + j]
             ok, rl2, worst = h_gate(g["h"][r, :cfg.I], s["h"][(t, j)], "a16")
             assert ok, ("h", t, j, rl2, worst)
+
+
+_C4 = {}
+
+
+def _c4_oracle():
+    """The fp64 oracle of the whole prefill layer, once per test session
+    (printed stage by stage: it runs for a minute or two)."""
+    if not _C4:
+        import time
+        cfg = LAYERS["prefill_mixed_t4096"]
+        layer = _layer(cfg)
+        t0 = time.time()
+        ids, w = oracle.route_topk(layer.logits, cfg.k)
+        perm = oracle.permute(ids, cfg.E, 160)
+        h, _ = oracle.gateup_a16(layer, perm)
+        print(f"[parity] prefill oracle: gate/up done at {time.time() - t0:.0f} s", flush=True)
+        y = oracle.down_a16(layer, perm, h)
+        print(f"[parity] prefill oracle: down done at {time.time() - t0:.0f} s", flush=True)
+        out = oracle.combine(layer, perm, w, y)
+        del y
+        _C4.update(ids=ids, w=w, h=h, out=out)
+    return _C4
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("tile_m", [160, 64])
+def test_prefill_layer_full(tile_m):
+    """The prefill layer at full size (4096 tokens, 256 experts, 192 int4 +
+    64 int2) against the oracle on every output: the routing tables bit for
+    bit, all 32,768 x 1536 values of h and all 4096 x 4096 outputs, at the
+    tile height the library prefers (160, the matrix-core chunk) and at 64."""
+    cfg = LAYERS["prefill_mixed_t4096"]
+    o = _c4_oracle()
+    dl = _dev(cfg)
+    g, B = run_layer_gpu(dl, "a16", tile_m)
+    g32, _ = run_layer_gpu(dl, "a16", tile_m, out_f32=True)
+    perm = oracle.permute(o["ids"], cfg.E, tile_m)
+    assert np.array_equal(g["ids"], o["ids"])
+    assert np.allclose(g["w"], o["w"], rtol=2e-6, atol=1e-7)
+    for key in ("counts", "offsets", "sorted_pair", "pair_pos"):
+        assert np.array_equal(g[key], perm[key]), key
+    assert np.array_equal(g["tiles"][:, :3], perm["tiles"])
+    assert g["err"] == 0
+    P = cfg.T * cfg.k
+    ok, rl2, worst = h_gate(g["h"][:P, :cfg.I], o["h"][:P, :cfg.I], "a16")
+    print(f"[parity] prefill tile_m={tile_m}: h rel-L2 {rl2:.2e} worst/bound {worst:.2f}",
+          flush=True)
+    assert ok, ("h", rl2, worst)
+    assert np.array_equal(g32["h"], g["h"])
+    check_out(g, g32, o["out"], f"prefill tile_m={tile_m}")
 
 
 def test_repeat_bitwise_identical():

@@ -49,6 +49,34 @@ def test_golden_bit_patterns():
     assert oracle.decode_fp16(np.array(g["bits"], np.uint16)).tolist() == g["values"]
 
 
+BF16_ROUND = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                         "bf16_rounding.json")))
+
+
+def test_golden_bf16_rounding():
+    """round_to_bf16 on hand-worked cases: ties to even (down and up), the
+    carry into the exponent, sign symmetry, the smallest normal, subnormal
+    ties, and the overflow of the halfway point above the largest finite
+    value.  Each fixture input is checked to equal its stated sum of powers
+    of two, and each expected value to equal its stated bit pattern."""
+    from fractions import Fraction
+    cases = BF16_ROUND["cases"]
+    for c in cases:
+        expr = c["in"].replace("^", "**").replace("2**", "Fraction(2)**")
+        assert Fraction(c["v"]) == eval(expr, {"Fraction": Fraction}), c["in"]
+        out = math.inf if c["out"] == "inf" else c["out"]
+        b = c["bits"]
+        e, f = (b >> 7) & 0xFF, b & 0x7F
+        dec = (math.inf if e == 0xFF else
+               math.ldexp(f, -133) if e == 0 else math.ldexp(128 + f, e - 134))
+        assert math.copysign(dec, -1.0 if b >> 15 else 1.0) == out, c["in"]
+    v = np.array([c["v"] for c in cases])
+    want = np.array([math.inf if c["out"] == "inf" else c["out"] for c in cases])
+    got = oracle.round_to_bf16(v)
+    assert np.array_equal(got, want), [(c["in"], g) for c, g, w in zip(cases, got, want) if g != w]
+    assert np.array_equal(oracle.round_to_bf16(-v), -want)
+
+
 def test_decoders_match_hardware_conversions():
     # every fp16 pattern against numpy's own binary16, every bf16 pattern
     # against the float32 whose top half it is
