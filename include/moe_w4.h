@@ -378,6 +378,38 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x,
                         void* h, void* out, void* workspace,
                         size_t ws_bytes, int flags, void* stream);
 
+/* ---------------------------------------------------------------------
+ * moe_w4_layer_noalloc -- moe_w4_layer with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a library-owned device array of MOE_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) per GPU, held from the first call on that GPU until the process
+ * ends; the call itself allocates nothing and frees nothing.
+ *   arguments  as moe_w4_layer (same meanings, flags included)
+ *   err_out    int32 [1] device pointer or null: when given, the call
+ *              clears the array's error word first and copies it here at
+ *              the end (bits as in the workspace error word above)
+ * Shapes whose workspace (moe_workspace_bytes) exceeds the array return
+ * MOE_E_WORKSPACE before anything is launched: decode batches fit (the
+ * 64-token W4A8 layer needs about 5 MB), a 4096-token prefill chunk does
+ * not and needs moe_w4_layer with a caller workspace.
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (other streams,
+ * other threads) race on it and must be ordered by the caller.
+ * ------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_w4_layer_noalloc(int act, const float* logits, const uint16_t* x,
+                                int T, int H, int I, int E, int k,
+                                int renormalize, const moe_qmat* w13,
+                                const moe_qmat* w2, const moe_qmat* w13_shared,
+                                const moe_qmat* w2_shared, int n_shared,
+                                int I_shared, int tile_m, int32_t* topk_ids,
+                                float* topk_w, int32_t* counts,
+                                int32_t* offsets, int32_t* sorted_pair,
+                                int32_t* pair_pos, int32_t* tiles,
+                                int32_t* n_tiles, void* h, void* out,
+                                int32_t* err_out, int flags, void* stream);
+
 /* 1 when moe_w4_layer with these arguments (flags included) issues one
  * launch on the current device, 0 when it issues the two calls, a
  * negative moe_status for arguments it would reject (or no usable

@@ -22,6 +22,7 @@ MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA16 = 0, 1, 2, 3
 MOE_QUANT_SEPARATE = 4
 MOE_LAYER_ONE_LAUNCH = 8
 MOE_OUT_F32 = 16
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -71,6 +72,12 @@ _SIGS = {
                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                              c_int, c_void_p]),
+    "moe_w4_layer_noalloc": (c_int, [c_int, c_void_p, c_void_p, c_int, c_int, c_int,
+                                     c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                     c_void_p]),
     "moe_w4_layer_one_launch": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int,
                                         c_int, c_int, c_int, c_int]),
     "moe_dbg_w4a8_gateup_partials": (c_int, [c_void_p, c_int, c_int, c_int,
@@ -262,6 +269,18 @@ def moe_w4_layer(act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared
                  _ptr(counts), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
                  _ptr(tiles), _ptr(n_tiles), _ptr(h), _ptr(out), _ptr(workspace),
                  ws_bytes, flags, _stream(stream), check=check)
+
+
+def moe_w4_layer_noalloc(act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared,
+                         w2_shared, n_shared, I_shared, tile_m, topk_ids, topk_w, counts,
+                         offsets, sorted_pair, pair_pos, tiles, n_tiles, h, out, err_out=None,
+                         flags=0, stream=None, check=True):
+    return _call("moe_w4_layer_noalloc", act, _ptr(logits), _ptr(x), T, H, I, E, k,
+                 renormalize, _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared),
+                 n_shared, I_shared, tile_m, _ptr(topk_ids), _ptr(topk_w),
+                 _ptr(counts), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
+                 _ptr(tiles), _ptr(n_tiles), _ptr(h), _ptr(out), _ptr(err_out),
+                 flags, _stream(stream), check=check)
 
 
 def moe_w4_layer_one_launch(act, T, H, I, E, k, n_shared=0, I_shared=0, tile_m=16,

@@ -263,3 +263,27 @@ def test_router_validation_and_workspace():
     assert call(T=0, x=None) == L.MOE_OK
     assert call() == L.MOE_E_DEVICE
     assert call(T=4096, H=4096, E=256, workspace=None, ws_bytes=0) == L.MOE_E_DEVICE
+
+
+def test_noalloc_validation():
+    """moe_w4_layer_noalloc checks the shape and that its workspace fits the
+    library's static scratch array on the host, before touching a device."""
+    ok = dict(act=0, logits=FAKE, x=FAKE, T=1, H=2048, I=768, E=128, k=8, renormalize=1,
+              w13=FAKE, w2=FAKE, w13_shared=FAKE, w2_shared=FAKE, n_shared=1,
+              I_shared=768, tile_m=16, topk_ids=FAKE, topk_w=FAKE, counts=FAKE,
+              offsets=FAKE, sorted_pair=FAKE, pair_pos=FAKE, tiles=FAKE, n_tiles=FAKE,
+              h=FAKE, out=FAKE, err_out=None, flags=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_w4_layer_noalloc(*a.values(), stream=0, check=False)
+    assert call(act=3) == L.MOE_E_INVAL
+    assert call(T=-1) == L.MOE_E_INVAL
+    # a 4096-token prefill chunk needs far more than the 32 MiB array
+    assert L.moe_workspace_bytes(0, 4096, 4096, 1536, 256, 8) > L.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(T=4096, H=4096, I=1536, E=256, n_shared=0, I_shared=0,
+                tile_m=160) == L.MOE_E_WORKSPACE
+    # decode shapes fit (the 64-token W4A8 layer included) and reach the device check
+    assert L.moe_workspace_bytes(1, 64, 2048, 768, 128, 8) <= L.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(act=1, T=64, n_shared=0, I_shared=0) == L.MOE_E_DEVICE
+    assert call() == L.MOE_E_DEVICE
