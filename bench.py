@@ -3,15 +3,22 @@
 
 A step is one pass of the whole layer (route -> permute -> gate/up+SiLU*mul
 -> down+combine) over one batch of synthetic input resident in HBM.
-Default workload: the single-token decode layer (T=1, H=2048, E=128, top-8,
-I=768, int4 G128 experts, one always-on shared expert).  Decode throughput
-is packed-weight GB/s over the experts a step touches (codes + fp16
-scales, each touched expert counted once); prefill (--config 4) is TFLOP/s
-over 6*P*H*I useful flops.
 
-So that repeated steps measure HBM rather than the 256 MB Infinity Cache,
-decode steps rotate over R device copies of the weight bank (same routing,
-distinct addresses) with R * touched bytes >= --rotate-bytes.
+Default run: every benchmark layer, one JSON line.  The headline is the
+prefill chunk (T=4096, H=4096, E=256, top-8, I=1536, 192 int4/G128 + 64
+int2/G64 experts): TFLOP/s over 6*P*H*I useful flops (P = T*k pairs).  The
+three decode layers (T=1 with a shared expert, T=12 Zipf-skewed with a
+shared expert, T=64 W4A8) follow as sub-records: packed-weight GB/s over the
+experts a step touches (codes + fp16 scales, each touched expert counted
+once).  Every record carries the roofline of its dominant kernel (timed live
+with HIP events on the stream it runs on) and the CPU oracle timed on a
+bounded sample.  --config N runs one layer alone.
+
+Decode steps rotate over R device copies of the weight bank (same routing,
+distinct addresses, R * touched bytes >= --rotate-bytes) and every timed step
+continues the cycle where the previous step left it, so each step reads
+weights last touched R steps (>= 1.5 GB) earlier: the 256 MB Infinity Cache
+cannot serve them.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -21,6 +28,7 @@ import argparse
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -29,7 +37,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE W4 FFN layer: packed-weight GB/s (decode) and TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+F16_PEAK_TFLOPS = 2500.0      # dense fp16 / bf16 MFMA
+HEADLINE = 4                  # the prefill chunk
+SUBS = (1, 2, 3)              # decode layers
 
 
 def log(*a):
@@ -66,14 +76,51 @@ def measured_traffic(key):
         return None
 
 
-def cpu_baseline(layer, seconds, unit_amount, unit, sample_note):
-    import numpy as np  # noqa: F401
-    import oracle
+def host_info():
+    """CPU model, affinity and BLAS threads of the host the oracle runs on."""
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    blas, threads = "unknown", 1
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(i.get("num_threads", 1) for i in info)
     except Exception:  # pragma: no cover
-        cores = 1
+        pass
+    return {"cpu_model": model, "cpu_affinity": affinity, "blas": blas,
+            "blas_threads": threads}
+
+
+def timed_loop(fn, n, torch):
+    """Average ms of fn(i), i < n, between HIP events on the current stream
+    (the stream every call here is issued on)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(torch.cuda.current_stream())
+    for i in range(n):
+        fn(i)
+    e1.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def cpu_oracle_decode(layer, seconds, gbytes, hi):
+    """Full oracle layer passes on the host for about `seconds` (at least
+    one), as GB/s of the step's packed bytes."""
+    import oracle
     t0 = time.perf_counter()
     n = 0
     while True:
@@ -83,10 +130,218 @@ def cpu_baseline(layer, seconds, unit_amount, unit, sample_note):
         if el >= seconds:
             break
     per = el / n
-    return {"value": unit_amount / per, "unit": unit, "cores": cores,
+    return {"value": gbytes / per, "unit": "GB/s", "cores": hi["blas_threads"],
             "kind": "oracle",
-            "sample": f"{sample_note}; {n} full oracle layer passes in {el:.1f} s "
-                      f"({per * 1e3:.1f} ms each); cores = BLAS threads"}
+            "sample": f"{layer.cfg.name}: {n} full fp64 oracle layer passes in {el:.1f} s "
+                      f"({per * 1e3:.1f} ms each)",
+            **hi}
+
+
+def cpu_oracle_prefill(layer, n_experts, hi):
+    """The oracle on a bounded sample of the prefill layer: routing and the
+    stable grouping of all 4096 tokens, then gate/up + SiLU*mul and down
+    for every pair routed to the first n_experts experts (int4 and int2 as
+    in the layer); TFLOP/s over those pairs' 6*H*I flops each."""
+    import numpy as np
+    import oracle
+    cfg = layer.cfg
+    t0 = time.perf_counter()
+    ids, w = oracle.route_topk(layer.logits, cfg.k, cfg.renormalize)
+    perm = oracle.permute(ids, cfg.E, 16)
+    off = perm["offsets"]
+    keep = np.arange(cfg.E) < n_experts
+    counts = np.where(keep, np.diff(off), 0)
+    sub = {"offsets": np.concatenate([[0], np.cumsum(counts)]).astype(np.int64),
+           "sorted_pair": perm["sorted_pair"][:int(off[n_experts])]}
+    sub_layer = type(layer)(**{**layer.__dict__,
+                               "cfg": cfg.replace(n_shared=0, I_shared=0), "shared": []})
+    h, _ = oracle.gateup_a16(sub_layer, sub)
+    oracle.down_a16(sub_layer, sub, h)
+    el = time.perf_counter() - t0
+    pairs = int(counts.sum())
+    flops = 6.0 * pairs * cfg.H * cfg.I
+    n2 = int(sum(1 for e in range(n_experts) if layer.experts[e].w13.bits == 2))
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": hi["blas_threads"],
+            "kind": "oracle",
+            "sample": f"{cfg.name}: fp64 oracle routing + grouping of all {cfg.T} tokens, then "
+                      f"gate/up + down of the {pairs} pairs routed to experts 0..{n_experts - 1} "
+                      f"({n2} of them int2) in {el:.1f} s",
+            **hi}
+
+
+def read_ceiling(torch, L, nbytes):
+    """Measured HBM read-stream ceiling: GB/s of one plain streaming read of
+    nbytes (rotating over two buffers so no read is served by the cache)."""
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for b in bufs:
+        b.fill_(1)
+    n_blocks = 256 * 8
+    sink = torch.zeros(n_blocks, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        L.moe_read_stream(b, nbytes, sink, n_blocks)
+    ms = timed_loop(lambda i: L.moe_read_stream(bufs[i % 2], nbytes, sink, n_blocks), 10, torch)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"achieved": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "bytes": nbytes,
+            "kernel": "read_stream_kernel (16-byte loads, 2048 workgroups of 256)"}
+
+
+def run_config(cid, args, torch, L, hi, ceiling):
+    from packed_bit_grouped_amd.layer import DeviceLayer, run_layer
+    from synth import CONFIGS, make_layer
+
+    cfg = CONFIGS[cid]
+    decode = cid != 4
+    flags = {"auto": 0, "gemv": 1, "mfma": 2}[args.path]
+    t0 = time.time()
+    log(f"[bench] generating {cfg.name} ...")
+    layer = make_layer(cfg)
+    log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
+    dl = DeviceLayer.from_synth(layer, "cuda:0")
+    act = cfg.act
+    B = dl.buffers(act)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+
+    # routing is identical on every step: learn the touched experts once
+    dl.run(B, flags)
+    torch.cuda.synchronize()
+    counts = B.counts.cpu().numpy()
+    n_touched = int((counts > 0).sum())
+    bytes_all = touched_bytes(dl, counts)
+    bytes_w13 = touched_bytes(dl, counts, ("w13",))
+    P = T * k
+    flops = 6.0 * P * H * I + 6.0 * cfg.n_shared * T * H * cfg.I_shared
+    flops_gateup = 4.0 * P * H * I + 4.0 * cfg.n_shared * T * H * cfg.I_shared
+
+    # steps per graph: a divisor of --steps (the timed region is exactly K steps)
+    G = next(g for g in (16, 8, 4, 2, 1) if args.steps % g == 0)
+    banks = [dl.bank]
+    if decode:
+        R = max(G, math.ceil(args.rotate_bytes / bytes_all))
+        R = min(-(-R // G) * G, 128 // G * G)
+        free, _ = torch.cuda.mem_get_info()
+        R = max(G, min(R, int(0.5 * free // dl.bank.buf.numel()) // G * G))
+        for _ in range(R - 1):
+            banks.append(dl.bank.rebased(dl.bank.buf.clone()))
+        log(f"[bench] {n_touched} routed experts touched, {bytes_all / 1e6:.3f} MB/step; "
+            f"{R} bank copies ({R * bytes_all / 1e9:.2f} GB per cycle)")
+    else:
+        G = 1
+
+    def step_on(bk):
+        run_layer(bk, dl.x, dl.logits, B, cfg.renormalize, flags)
+
+    # the served form: HIP graphs of G consecutive steps over G distinct bank
+    # copies, replayed in cycle order; warm-up replays come first and the
+    # timed replays continue the cycle
+    n_graphs = len(banks) // G
+    graphs = []
+    for gi in range(n_graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(G):
+                step_on(banks[gi * G + i])
+        graphs.append(g)
+    w_reps = max(1, -(-args.warmup // G))
+    for i in range(w_reps):
+        graphs[i % n_graphs].replay()
+    reps = args.steps // G
+    ms = timed_loop(lambda i: graphs[(w_reps + i) % n_graphs].replay(), reps, torch) / G
+    log(f"[bench] {cfg.name}: graph replay, {reps * G} steps ({G} per graph): "
+        f"{ms * 1e3:.2f} us/step")
+    # the replayed steps against an eager one (same inputs, same bank)
+    last = (w_reps + reps - 1) % n_graphs
+    out_g = B.out.clone()
+    step_on(banks[last * G + G - 1])
+    torch.cuda.synchronize()
+    if not torch.equal(out_g, B.out):
+        log("[bench] graph replay output differs from the eager step")
+        sys.exit(3)
+    # eager issue from Python (secondary: includes host launch cost)
+    ms_eager = timed_loop(lambda i: step_on(banks[i % len(banks)]), args.steps, torch)
+    log(f"[bench] {cfg.name}: eager {ms_eager * 1e3:.2f} us/step")
+
+    # the dominant kernel (gate/up + SiLU*mul) alone: a graph of back-to-back
+    # launches over every bank copy, timed with events on the stream it runs on
+    fused = (decode and act == "a16" and P <= 64 and E <= 512 and B.tile_m <= 16 and H <= 2048)
+
+    def gateup(bk):
+        if fused:
+            L.moe_w4_route_gateup_silu(B.act, dl.logits, dl.x, T, H, I, E, k,
+                                       cfg.renormalize, bk.w13, bk.w13_sh, cfg.n_shared,
+                                       cfg.I_shared, B.tile_m, B.ids, B.w, B.counts,
+                                       B.offsets, B.sorted_pair, B.pair_pos, B.tiles,
+                                       B.n_tiles, B.h, B.ws, B.ws_bytes, flags)
+        else:
+            L.moe_w4_gateup_silu(B.act, dl.x, T, H, I, E, k, bk.w13, bk.w13_sh,
+                                 cfg.n_shared, cfg.I_shared, B.offsets, B.sorted_pair,
+                                 B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes, flags)
+
+    if fused:
+        kname = "dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)"
+    elif decode:
+        kname = ("proj_m16_kernel<0> (gate/up + SiLU*mul)" if act == "a16" else
+                 "proj_m16_kernel<0> (int8 x rows made in the kernel, gate/up + SiLU*mul)")
+    else:
+        kname = "proj_mfma_kernel<0> + convert_x_kernel (gate/up + SiLU*mul)"
+    n_k = len(banks) if decode else 4
+    gk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gk):
+        for i in range(n_k):
+            gateup(banks[i % len(banks)])
+    gk.replay()
+    k_reps = max(1, -(-args.steps // n_k))
+    gu_ms = timed_loop(lambda i: gk.replay(), k_reps, torch) / n_k
+    log(f"[bench] {cfg.name}: gate/up call {gu_ms * 1e3:.2f} us/launch")
+
+    if decode:
+        value = bytes_all / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+        ach = bytes_w13 / (gu_ms * 1e-3) / 1e9
+        key = ("dec_route_gateup_kernel@" if fused else "gateup_call@") + cfg.name
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(key),
+                "kernel": kname, "algorithmic_bytes": bytes_w13,
+                "ms_per_launch": gu_ms,
+                "frac_of_measured_read_ceiling": ach / ceiling["achieved"] if ceiling else None}
+        dtype = "bf16" if act == "a16" else "int8"
+    else:
+        value = flops / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        ach = flops_gateup / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / F16_PEAK_TFLOPS,
+                "traffic": measured_traffic(f"gateup_call@{cfg.name}"),
+                "kernel": kname, "algorithmic_flops": flops_gateup,
+                "ms_per_launch": gu_ms}
+        dtype = "fp16"   # x and the dequantized weights enter the MFMAs as fp16
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] {cfg.name}: timing the CPU oracle")
+        if decode:
+            cpu = cpu_oracle_decode(layer, args.cpu_seconds, bytes_all / 1e9, hi)
+        else:
+            cpu = cpu_oracle_prefill(layer, args.cpu_prefill_experts, hi)
+        log(f"[bench] {cfg.name}: CPU oracle {cpu['value']:.4g} {cpu['unit']}")
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": unit, "ms_per_step": ms,
+        "dtype": dtype,
+        "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "k": k, "I": I,
+                   "n_shared": cfg.n_shared, "act": act, "experts_touched": n_touched,
+                   "bytes_per_step": bytes_all, "flops_per_step": flops,
+                   "bank_copies_rotated": len(banks), "path": args.path,
+                   "timing": (f"HIP graphs of {G} steps over {G} weight copies, replayed in "
+                              f"cycle order after {w_reps} warm-up replays"),
+                   "ms_per_step_eager": ms_eager},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    del graphs, gk, banks, dl, B, layer
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -94,14 +349,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=None,
+                    help="one benchmark layer (0-4); default: the prefill headline "
+                         "plus the three decode layers")
     ap.add_argument("--rotate-bytes", type=float, default=1.5e9)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="CPU oracle time per decode layer")
+    ap.add_argument("--cpu-prefill-experts", type=int, default=12,
+                    help="experts of the prefill layer in the CPU oracle's sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=["auto", "gemv", "mfma"], default="auto")
-    ap.add_argument("--one-launch", action="store_true",
-                    help="run small bf16 decode layers as one launch (moe_w4_layer's "
-                         "opt-in single-launch form)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="after the run, one device copy of MB MiB (a plain copy kernel of "
                          "known size, the scale for hardware byte counters)")
@@ -115,191 +372,31 @@ def main():
             "single-GPU kernel library (expert-parallel sharding is design only)")
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from packed_bit_grouped_amd import _lib as L
-    from packed_bit_grouped_amd.layer import DeviceLayer, run_layer
-    from synth import CONFIGS, make_layer
 
-    cfg = CONFIGS[args.config]
-    flags = {"auto": 0, "gemv": 1, "mfma": 2}[args.path]
-    layer_flags = flags | (L.MOE_LAYER_ONE_LAUNCH if args.one_launch else 0)
     torch.cuda.set_device(0)
-    t0 = time.time()
-    log(f"[bench] generating {cfg.name} ...")
-    layer = make_layer(cfg)
-    log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
-    dl = DeviceLayer.from_synth(layer, "cuda:0")
-    act = cfg.act
-    B = dl.buffers(act)
+    hi = host_info()
+    ceiling = read_ceiling(torch, L, 2 << 30)
+    log(f"[bench] HBM read ceiling: {ceiling['achieved']:.0f} GB/s over "
+        f"{ceiling['bytes'] / 2**30:.0f} GiB")
 
-    # routing is identical on every step: learn the touched experts once
-    dl.run(B, layer_flags)
-    torch.cuda.synchronize()
-    counts = B.counts.cpu().numpy()
-    n_touched = int((counts > 0).sum())
-    decode = args.config != 4
-    bytes_all = touched_bytes(dl, counts)
-    bytes_w13 = touched_bytes(dl, counts, ("w13",))
-    P = cfg.T * cfg.k
-    flops = 6.0 * P * cfg.H * cfg.I + 6.0 * cfg.n_shared * cfg.T * cfg.H * cfg.I_shared
-    flops_gateup = 4.0 * P * cfg.H * cfg.I + 4.0 * cfg.n_shared * cfg.T * cfg.H * cfg.I_shared
-
-    banks = [dl.bank]
-    if decode:
-        R = max(1, math.ceil(args.rotate_bytes / bytes_all))
-        R = min(R, 128)
-        free, _ = torch.cuda.mem_get_info()
-        R = max(1, min(R, int(0.5 * free // dl.bank.buf.numel())))
-        for _ in range(R - 1):
-            banks.append(dl.bank.rebased(dl.bank.buf.clone()))
-        log(f"[bench] {n_touched} routed experts touched, {bytes_all / 1e6:.3f} MB/step; "
-            f"rotating over {R} bank copies ({R * bytes_all / 1e9:.2f} GB touched per cycle)")
-
-    def step(i):
-        run_layer(banks[i % len(banks)], dl.x, dl.logits, B, cfg.renormalize, layer_flags)
-
-    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
-
-    # bf16 decode batches of at most 64 pairs route, sort and run gate/up in
-    # one launch (the library's rule for moe_w4_route_gateup_silu); other
-    # shapes time the gate/up call alone (A8: with its int8 x quantizer)
-    fused = (decode and act == "a16" and cfg.T * cfg.k <= 64 and cfg.E <= 512
-             and B.tile_m <= 16 and cfg.H <= 2048)
-
-    # with --one-launch, small bf16 decode batches run the whole layer as one
-    # launch when the device holds every workgroup of its grid at once (the
-    # library's rule for moe_w4_layer); that launch is then the dominant kernel
-    one = decode and L.moe_w4_layer_one_launch(B.act, T, H, I, E, k, cfg.n_shared,
-                                               cfg.I_shared, B.tile_m, layer_flags) == 1
-
-    def gateup(bk):
-        if one:
-            run_layer(bk, dl.x, dl.logits, B, cfg.renormalize, layer_flags)
-        elif fused:
-            L.moe_w4_route_gateup_silu(B.act, dl.logits, dl.x, T, H, I, E, k,
-                                       cfg.renormalize, bk.w13, bk.w13_sh, cfg.n_shared,
-                                       cfg.I_shared, B.tile_m, B.ids, B.w, B.counts,
-                                       B.offsets, B.sorted_pair, B.pair_pos, B.tiles,
-                                       B.n_tiles, B.h, B.ws, B.ws_bytes, flags)
-        else:
-            L.moe_w4_gateup_silu(B.act, dl.x, T, H, I, E, k, bk.w13, bk.w13_sh,
-                                 cfg.n_shared, cfg.I_shared, B.offsets, B.sorted_pair,
-                                 B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes, flags)
-
-    def timed(fn, n):
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(torch.cuda.current_stream())
-        for i in range(n):
-            fn(i)
-        e1.record(torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    for i in range(args.warmup):
-        step(i)
-    # eager issue from Python (secondary number: includes host launch cost)
-    ms_eager = timed(step, args.steps)
-    log(f"[bench] eager: {ms_eager * 1e3:.2f} us/step")
-
-    # the served form: HIP graphs of G consecutive steps over G distinct
-    # weight-bank copies (as a model's decode graph holds its layers, each
-    # with its own weights), replayed back to back
-    G = next(g for g in (16, 8, 4, 2, 1) if g <= len(banks) and args.steps % g == 0)
-    n_graphs = len(banks) // G
-    graphs = []
-    for gi in range(n_graphs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(G):
-                run_layer(banks[gi * G + i], dl.x, dl.logits, B, cfg.renormalize,
-                          layer_flags)
-        graphs.append(g)
-    reps = args.steps // G
-    for i in range(max(1, args.warmup // G)):
-        graphs[i % n_graphs].replay()
-    ms = timed(lambda i: graphs[i % n_graphs].replay(), reps) / G
-    log(f"[bench] graph replay: {reps * G} steps ({G} per graph): {ms * 1e3:.2f} us/step")
-    # check the replayed steps against an eager one (same inputs, same bank)
-    out_g = B.out.clone()
-    step((reps - 1) % n_graphs * G + G - 1)
-    torch.cuda.synchronize()
-    if not torch.equal(out_g, B.out):
-        log("[bench] graph replay output differs from the eager step")
-        sys.exit(3)
-
-    # the dominant kernel (gate/up + SiLU*mul) alone: a graph of back-to-back
-    # launches over distinct bank copies, timed with events on the stream
-    # the graph runs on
-    n_k = min(len(banks), 32) if decode else 4
-    if one:
-        kname = "dec_layer_kernel (route + sort + gate/up + SiLU*mul + down + combine)"
-    elif fused:
-        kname = "dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)"
-    elif decode:
-        kname = ("proj_m16_kernel<0> (gate/up + SiLU*mul)" if act == "a16" else
-                 "proj_m16_kernel<0> (int8 x rows made in the kernel, gate/up + SiLU*mul)")
-    else:
-        kname = "proj_mfma_kernel<0> + convert_x_kernel (gate/up + SiLU*mul)"
-    gk = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gk):
-        for i in range(n_k):
-            gateup(banks[i % len(banks)])
-    gk.replay()
-    reps = max(1, args.steps // n_k)
-    gu_ms = timed(lambda i: gk.replay(), reps) / n_k
-    log(f"[bench] {'layer' if one else 'gate/up'} kernel: {gu_ms * 1e3:.2f} us/launch")
-
-    if decode:
-        value = bytes_all / (ms * 1e-3) / 1e9
-        unit = "GB/s"
-        alg = bytes_all if one else bytes_w13
-        ach = alg / (gu_ms * 1e-3) / 1e9
-        key = ("dec_layer_kernel@" if one else
-               "dec_route_gateup_kernel@" if fused else "gateup_call@") + cfg.name
-        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBS,
-                "traffic": measured_traffic(key),
-                "kernel": kname,
-                "algorithmic_bytes": alg}
-    else:
-        value = flops / (ms * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        ach = flops_gateup / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
-                "traffic": measured_traffic(f"gateup_call@{cfg.name}"),
-                "kernel": kname, "algorithmic_flops": flops_gateup}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
-        if decode:
-            cpu = cpu_baseline(layer, args.cpu_seconds, bytes_all / 1e9, "GB/s",
-                               f"{cfg.name}, same seeded layer")
-        else:
-            cpu = {"value": None, "unit": "TFLOP/s", "cores": None, "kind": "oracle",
-                   "sample": "prefill oracle not timed by default"}
-
+    cids = [args.config] if args.config is not None else [HEADLINE, *SUBS]
+    recs = [run_config(c, args, torch, L, hi, ceiling) for c in cids]
+    head, subs = recs[0], recs[1:]
     line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if act == "a16" else "int8",
+        "dtype": head["dtype"],
         "data": "synthetic (seeded; int4/int2 experts quantized from N(0, 0.02))",
-        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
-                   "I": cfg.I, "n_shared": cfg.n_shared, "act": act,
-                   "experts_touched": n_touched,
-                   "bytes_per_step": bytes_all, "flops_per_step": flops,
-                   "bank_copies_rotated": len(banks), "path": args.path,
-                   "layer_form": "one launch" if one else "separate calls",
-                   "timing": f"HIP graphs of {G} steps over {G} weight copies, replayed back to back",
-                   "ms_per_step_eager": ms_eager},
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": head["config"], "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "hbm_read_ceiling": ceiling,
     }
+    if subs:
+        line["sub_records"] = subs
     print(json.dumps(line), flush=True)
     if args.copy_probe > 0:
         n = args.copy_probe << 20

@@ -418,6 +418,21 @@ int moe_w4_layer_one_launch(int act, int T, int H, int I, int E, int k,
                             int n_shared, int I_shared, int tile_m, int flags);
 
 /* ---------------------------------------------------------------------
+ * moe_read_stream -- measurement aid: one plain streaming read of `bytes`
+ * bytes of device memory at `src` (16-byte aligned, bytes % 16 == 0) by
+ * n_blocks workgroups of 256 threads, 16-byte loads.  `sink` (device,
+ * n_blocks words) is written only in a case that does not occur, so the
+ * call moves `bytes` from HBM and writes nothing.  The decode layers'
+ * packed-weight bandwidth is reported against this measured ceiling as
+ * well as against the published HBM peak (decode is bound by streaming
+ * the packed expert weights: build log "Two 96 GB Ascend cards run
+ * Qwen3.8 Flash-Next", section "Keep low-bit weights packed, do the work
+ * on the NPU").  Errors: MOE_E_INVAL, MOE_E_DEVICE.
+ * ------------------------------------------------------------------- */
+moe_status moe_read_stream(const void* src, size_t bytes, uint32_t* sink, int n_blocks,
+                           void* stream);
+
+/* ---------------------------------------------------------------------
  * Test hooks of the A8 mode (build log "Two 96 GB Ascend cards run Qwen3.8
  * Flash-Next", section "Keep low-bit weights packed, do the work on the
  * NPU": dedicated W4A8 execution).  They take the path that

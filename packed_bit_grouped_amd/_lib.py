@@ -72,6 +72,7 @@ _SIGS = {
                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                              c_int, c_void_p]),
+    "moe_read_stream": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
     "moe_w4_layer_noalloc": (c_int, [c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                      c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
@@ -269,6 +270,11 @@ def moe_w4_layer(act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared
                  _ptr(counts), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
                  _ptr(tiles), _ptr(n_tiles), _ptr(h), _ptr(out), _ptr(workspace),
                  ws_bytes, flags, _stream(stream), check=check)
+
+
+def moe_read_stream(src, nbytes, sink, n_blocks, stream=None, check=True):
+    return _call("moe_read_stream", _ptr(src), nbytes, _ptr(sink), n_blocks,
+                 _stream(stream), check=check)
 
 
 def moe_w4_layer_noalloc(act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared,
