@@ -36,10 +36,11 @@
  *              (stable: increasing p within an expert)
  *   gate/up  = g = x_t . W13_e[i], u = x_t . W13_e[I+i], h = SiLU(g)*u
  *   down     = y = h . W2_e[n]
- *   combine  = out[t] = sum_j w[t][j] * y(t, ids[t][j]) + sum_s y_s(t)
+ *   combine  = out[t] = sum_j w[t][j] * y(t, ids[t][j]) + sum_s g_s(t) y_s(t)
  *   with W = code * scale (code int4 in [-8,7] or int2 in [-2,1], one
  *   fp16 scale per row per K-group).  Shared experts are always on and
- *   join with weight 1.0.
+ *   join with weight g = 1.0, or with a sigmoid gate g = sigmoid(l) of a
+ *   per-token gate logit l when the caller passes shared-gate logits.
  *
  * Precision: A16 (bf16 activations): fp32 accumulation; h is rounded to
  * bf16 between the projections.  A8: activations are quantized per row to
@@ -323,10 +324,15 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits,
  *              quantized to int8 per row inside this call
  *   w2         device table of E moe_qmat, each [H][I]
  *   w2_shared  device table of n_shared moe_qmat, each [H][I_shared]
+ *   shared_gate fp32 [T][n_shared] gate logits of the shared experts, or
+ *              null: shared expert s joins token t with weight
+ *              sigmoid(shared_gate[t][s]) = 1 / (1 + exp(-l)) (fp32), or
+ *              with weight 1.0 when null
  *   topk_w     fp32 [T][k] from moe_route_topk
  *   pair_pos   from moe_permute
  *   out        bf16 [T][H] (out): out[t] = sum_j topk_w[t][j] * y(pair
- *              t*k+j) + sum_s y(shared s, t), summed in fp32 in that order
+ *              t*k+j) + sum_s g(t, s) * y(shared s, t), summed in fp32 in
+ *              that order (g = the shared gate weight above)
  *              and rounded to bf16; with MOE_OUT_F32 in flags, fp32 [T][H]
  *              holding that sum unrounded
  * Decode batches with bf16 activations (tiles of at most 16 rows, I <= 1024,
@@ -338,7 +344,8 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits,
 moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
                                int E, int k, const moe_qmat* w2,
                                const moe_qmat* w2_shared, int n_shared,
-                               int I_shared, const float* topk_w,
+                               int I_shared, const float* shared_gate,
+                               const float* topk_w,
                                const int32_t* offsets,
                                const int32_t* sorted_pair,
                                const int32_t* pair_pos, const int32_t* tiles,
@@ -371,7 +378,8 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x,
                         int T, int H, int I, int E, int k, int renormalize,
                         const moe_qmat* w13, const moe_qmat* w2,
                         const moe_qmat* w13_shared, const moe_qmat* w2_shared,
-                        int n_shared, int I_shared, int tile_m,
+                        int n_shared, int I_shared, const float* shared_gate,
+                        int tile_m,
                         int32_t* topk_ids, float* topk_w, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_pair,
                         int32_t* pair_pos, int32_t* tiles, int32_t* n_tiles,
@@ -403,7 +411,8 @@ moe_status moe_w4_layer_noalloc(int act, const float* logits, const uint16_t* x,
                                 int renormalize, const moe_qmat* w13,
                                 const moe_qmat* w2, const moe_qmat* w13_shared,
                                 const moe_qmat* w2_shared, int n_shared,
-                                int I_shared, int tile_m, int32_t* topk_ids,
+                                int I_shared, const float* shared_gate,
+                                int tile_m, int32_t* topk_ids,
                                 float* topk_w, int32_t* counts,
                                 int32_t* offsets, int32_t* sorted_pair,
                                 int32_t* pair_pos, int32_t* tiles,
@@ -461,7 +470,7 @@ moe_status moe_dbg_w4a8_gateup_partials(
 moe_status moe_dbg_w4a8_down_partials(
     const void* h, int T, int H, int I, int E, int k, const moe_qmat* w2,
     const moe_qmat* w2_shared, int n_shared, int I_shared,
-    const float* topk_w, const int32_t* offsets, const int32_t* sorted_pair,
+    const float* shared_gate, const float* topk_w, const int32_t* offsets, const int32_t* sorted_pair,
     const int32_t* pair_pos, const int32_t* tiles, const int32_t* n_tiles,
     int tile_m, void* out, void* workspace, size_t ws_bytes, int flags,
     int32_t* partials, int ng_ld, void* stream);

@@ -189,12 +189,16 @@ def layer_brute(layer, act=None):
                 q, s = hq[r]
                 yrow.append(a8_dot(q, s, c2, s2, g2, n))
         y[r] = yrow
+    # shared experts: weight 1, or sigmoid of the token's gate logit
+    sgl = getattr(layer, "shared_gate_logits", None)
+    gate = [[1.0 if sgl is None else 1.0 / (1.0 + math.exp(-float(sgl[t][s])))
+             for s in range(cfg.n_shared)] for t in range(T)]
     out = []
     for t in range(T):
         row = []
         for n in range(H):
             terms = [ws[t][j] * y[pair_pos[t * k + j]][n] for j in range(k)]
-            terms += [y[P + s * T + t][n] for s in range(cfg.n_shared)]
+            terms += [gate[t][s] * y[P + s * T + t][n] for s in range(cfg.n_shared)]
             row.append(math.fsum(terms))
         out.append(row)
     return {"ids": ids, "w": ws, "counts": counts, "offsets": offsets,

@@ -28,7 +28,7 @@ __all__ = [
     "decode_bf16", "decode_fp16", "unpack_codes", "dequantize",
     "router_logits", "route_topk", "permute", "quant_rows_a8", "silu", "round_to_bf16",
     "x_float", "expert_rows", "gateup_a16", "gateup_a8", "down_a16",
-    "down_a8", "a8_group_partials", "combine", "oracle_layer",
+    "down_a8", "a8_group_partials", "shared_weights", "combine", "oracle_layer",
     "oracle_token_outputs", "touched_experts",
 ]
 
@@ -400,21 +400,36 @@ def down_a8(layer, perm, qh, sh, want_partials: bool = False):
     return (y, parts) if want_partials else y
 
 
-def combine(layer, perm, w, y):
-    """out[t] = sum_j w[t][j] * y[row of pair t*k+j] + sum_s y[P + s*T + t].
+def shared_weights(layer) -> np.ndarray:
+    """Weight of shared expert s for token t, float64 [T][n_shared].
 
-    The shared expert joins with weight 1.0 outside the renormalised gate
-    (a reading: nothing fixes a shared-expert gate).  float64, unrounded."""
+    A shared expert is always on and sits outside the renormalised top-k
+    gate.  Without gate logits it joins with weight 1.0 (a reading: nothing
+    fixes a shared-expert gate); with per-token gate logits l (the layer's
+    sigmoid-gated variant) its weight is sigmoid(l) = 1 / (1 + exp(-l))."""
+    cfg = layer.cfg
+    lg = getattr(layer, "shared_gate_logits", None)
+    if lg is None:
+        return np.ones((cfg.T, cfg.n_shared))
+    lg = np.asarray(lg, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-lg))
+
+
+def combine(layer, perm, w, y):
+    """out[t] = sum_j w[t][j] * y[row of pair t*k+j] + sum_s g[t][s] * y[P + s*T + t]
+    with g the shared-expert weights (shared_weights).  float64, unrounded."""
     cfg = layer.cfg
     T, k, E = cfg.T, cfg.k, cfg.E
     P = int(perm["offsets"][E])
     out = np.zeros((T, cfg.H))
     pos = perm["pair_pos"]
+    g = shared_weights(layer)
     for t in range(T):
         for j in range(k):
             out[t] += w[t, j] * y[pos[t * k + j]]
         for s in range(cfg.n_shared):
-            out[t] += y[P + s * T + t]
+            out[t] += g[t, s] * y[P + s * T + t]
     return out
 
 
@@ -466,6 +481,7 @@ def oracle_token_outputs(layer, tokens: Sequence[int], act: Optional[str] = None
     tokens = list(tokens)
     ids_all, w_all = route_topk(layer.logits[tokens], cfg.k, cfg.renormalize)
     x = x_float(layer.x_bf16)
+    gsh = shared_weights(layer)
     cache = {} if deq_cache is None else deq_cache
 
     def deq(key, qm):
@@ -477,7 +493,7 @@ def oracle_token_outputs(layer, tokens: Sequence[int], act: Optional[str] = None
     hs = {}
     for n, t in enumerate(tokens):
         plan = [(int(ids_all[n, j]), None, w_all[n, j]) for j in range(cfg.k)]
-        plan += [(cfg.E + s, s, 1.0) for s in range(cfg.n_shared)]
+        plan += [(cfg.E + s, s, gsh[t, s]) for s in range(cfg.n_shared)]
         for slot, (e, s, wt) in enumerate(plan):
             ex = layer.experts[e] if s is None else layer.shared[s]
             if act == "a16":

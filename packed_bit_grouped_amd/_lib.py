@@ -62,20 +62,21 @@ _SIGS = {
                                          c_void_p, c_size_t, c_int, c_void_p]),
     "moe_w4_down_combine": (c_int, [c_int, c_void_p, c_int, c_int, c_int,
                                     c_int, c_int, c_void_p, c_void_p, c_int,
-                                    c_int, c_void_p, c_void_p, c_void_p,
+                                    c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_int,
                                     c_void_p, c_void_p, c_size_t, c_int,
                                     c_void_p]),
     "moe_w4_layer": (c_int, [c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                              c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
-                             c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                             c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                              c_int, c_void_p]),
     "moe_read_stream": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
     "moe_w4_layer_noalloc": (c_int, [c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                      c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
-                                     c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                                     c_void_p, c_int, c_int, c_void_p, c_int, c_void_p,
+                                     c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                      c_void_p]),
@@ -89,7 +90,7 @@ _SIGS = {
                                              c_void_p, c_int, c_void_p]),
     "moe_dbg_w4a8_down_partials": (c_int, [c_void_p, c_int, c_int, c_int,
                                            c_int, c_int, c_void_p, c_void_p,
-                                           c_int, c_int, c_void_p, c_void_p,
+                                           c_int, c_int, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_int, c_void_p,
                                            c_void_p, c_size_t, c_int, c_void_p,
@@ -252,9 +253,9 @@ def moe_w4_route_gateup_silu(act, logits, x, T, H, I, E, k, renormalize, w13,
 def moe_w4_down_combine(act, h, T, H, I, E, k, w2, w2_shared, n_shared,
                         I_shared, topk_w, offsets, sorted_pair, pair_pos, tiles,
                         n_tiles, tile_m, out, workspace, ws_bytes, flags=0,
-                        stream=None, check=True):
+                        stream=None, check=True, shared_gate=None):
     return _call("moe_w4_down_combine", act, _ptr(h), T, H, I, E, k, _ptr(w2),
-                 _ptr(w2_shared), n_shared, I_shared, _ptr(topk_w),
+                 _ptr(w2_shared), n_shared, I_shared, _ptr(shared_gate), _ptr(topk_w),
                  _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos), _ptr(tiles),
                  _ptr(n_tiles), tile_m, _ptr(out), _ptr(workspace), ws_bytes,
                  flags, _stream(stream), check=check)
@@ -263,10 +264,10 @@ def moe_w4_down_combine(act, h, T, H, I, E, k, w2, w2_shared, n_shared,
 def moe_w4_layer(act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared,
                  w2_shared, n_shared, I_shared, tile_m, topk_ids, topk_w, counts,
                  offsets, sorted_pair, pair_pos, tiles, n_tiles, h, out, workspace,
-                 ws_bytes, flags=0, stream=None, check=True):
+                 ws_bytes, flags=0, stream=None, check=True, shared_gate=None):
     return _call("moe_w4_layer", act, _ptr(logits), _ptr(x), T, H, I, E, k,
                  renormalize, _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared),
-                 n_shared, I_shared, tile_m, _ptr(topk_ids), _ptr(topk_w),
+                 n_shared, I_shared, _ptr(shared_gate), tile_m, _ptr(topk_ids), _ptr(topk_w),
                  _ptr(counts), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
                  _ptr(tiles), _ptr(n_tiles), _ptr(h), _ptr(out), _ptr(workspace),
                  ws_bytes, flags, _stream(stream), check=check)
@@ -280,10 +281,10 @@ def moe_read_stream(src, nbytes, sink, n_blocks, stream=None, check=True):
 def moe_w4_layer_noalloc(act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared,
                          w2_shared, n_shared, I_shared, tile_m, topk_ids, topk_w, counts,
                          offsets, sorted_pair, pair_pos, tiles, n_tiles, h, out, err_out=None,
-                         flags=0, stream=None, check=True):
+                         flags=0, stream=None, check=True, shared_gate=None):
     return _call("moe_w4_layer_noalloc", act, _ptr(logits), _ptr(x), T, H, I, E, k,
                  renormalize, _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared),
-                 n_shared, I_shared, tile_m, _ptr(topk_ids), _ptr(topk_w),
+                 n_shared, I_shared, _ptr(shared_gate), tile_m, _ptr(topk_ids), _ptr(topk_w),
                  _ptr(counts), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
                  _ptr(tiles), _ptr(n_tiles), _ptr(h), _ptr(out), _ptr(err_out),
                  flags, _stream(stream), check=check)
@@ -309,9 +310,11 @@ def moe_dbg_w4a8_gateup_partials(x, T, H, I, E, k, w13, w13_shared, n_shared,
 def moe_dbg_w4a8_down_partials(h, T, H, I, E, k, w2, w2_shared, n_shared,
                                I_shared, topk_w, offsets, sorted_pair, pair_pos,
                                tiles, n_tiles, tile_m, out, workspace, ws_bytes,
-                               partials, ng_ld, flags=0, stream=None, check=True):
+                               partials, ng_ld, flags=0, stream=None, check=True,
+                               shared_gate=None):
     return _call("moe_dbg_w4a8_down_partials", _ptr(h), T, H, I, E, k,
-                 _ptr(w2), _ptr(w2_shared), n_shared, I_shared, _ptr(topk_w),
+                 _ptr(w2), _ptr(w2_shared), n_shared, I_shared, _ptr(shared_gate),
+                 _ptr(topk_w),
                  _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos), _ptr(tiles),
                  _ptr(n_tiles), tile_m, _ptr(out), _ptr(workspace), ws_bytes,
                  flags, _ptr(partials), ng_ld, _stream(stream), check=check)

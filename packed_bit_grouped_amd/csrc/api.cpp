@@ -359,7 +359,8 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
 
 static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
                             int k, const moe_qmat* w2, const moe_qmat* w2_shared,
-                            int n_shared, int I_shared, const float* topk_w,
+                            int n_shared, int I_shared, const float* shared_gate,
+                            const float* topk_w,
                             const int32_t* offsets, const int32_t* sorted_pair,
                             const int32_t* pair_pos, const int32_t* tiles,
                             const int32_t* n_tiles, int tile_m, void* out,
@@ -424,7 +425,7 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
     e = launch_proj_mfma(a, reinterpret_cast<uint16_t*>(ws + L.a16), nullptr, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
-                                   n_shared, out, out_f32, s));
+                                   n_shared, shared_gate, out, out_f32, s));
   }
   if (act == MOE_A8) a.in_f32 = static_cast<const float*>(h);
   else a.in_bf16 = static_cast<const uint16_t*>(h);
@@ -448,7 +449,7 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
     e = launch_proj_m16(a, act, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
-                                   n_shared, out, out_f32, s));
+                                   n_shared, shared_gate, out, out_f32, s));
   }
   a.maxt = gemv_maxt(T, tile_m);
   a.sh_tile = a.maxt;
@@ -458,12 +459,13 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
     a.topk_w = topk_w;
     a.pair_pos = pair_pos;
     a.out_f32 = out_f32;
+    a.sh_gate = n_shared > 0 ? shared_gate : nullptr;
     return from_hip(launch_dec_down_combine(a, out, s));
   }
   e = launch_proj_gemv(a, act, gemv_grid(a), s);
   if (e != hipSuccess) return MOE_E_DEVICE;
   return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
-                                 n_shared, out, out_f32, s));
+                                 n_shared, shared_gate, out, out_f32, s));
 }
 
 moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H, int I,
@@ -552,7 +554,8 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits, const uint16_t
 moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
                                int E, int k, const moe_qmat* w2,
                                const moe_qmat* w2_shared, int n_shared,
-                               int I_shared, const float* topk_w,
+                               int I_shared, const float* shared_gate,
+                               const float* topk_w,
                                const int32_t* offsets,
                                const int32_t* sorted_pair,
                                const int32_t* pair_pos, const int32_t* tiles,
@@ -560,7 +563,7 @@ moe_status moe_w4_down_combine(int act, const void* h, int T, int H, int I,
                                void* out, void* workspace,
                                size_t ws_bytes, int flags, void* stream) {
   return down_impl(act, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared,
-                   topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles,
+                   shared_gate, topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles,
                    tile_m, out, workspace, ws_bytes, flags, nullptr, 0, stream);
 }
 
@@ -581,14 +584,14 @@ moe_status moe_dbg_w4a8_gateup_partials(
 moe_status moe_dbg_w4a8_down_partials(
     const void* h, int T, int H, int I, int E, int k, const moe_qmat* w2,
     const moe_qmat* w2_shared, int n_shared, int I_shared,
-    const float* topk_w, const int32_t* offsets, const int32_t* sorted_pair,
+    const float* shared_gate, const float* topk_w, const int32_t* offsets, const int32_t* sorted_pair,
     const int32_t* pair_pos, const int32_t* tiles, const int32_t* n_tiles,
     int tile_m, void* out, void* workspace, size_t ws_bytes, int flags,
     int32_t* partials, int ng_ld, void* stream) {
   if (!partials) return MOE_E_INVAL;
   if ((flags & MOE_PATH_MASK) == MOE_PATH_MFMA) return MOE_E_UNSUPPORTED;   // A16 only
   return down_impl(MOE_A8, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared,
-                   topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles,
+                   shared_gate, topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles,
                    tile_m, out, workspace, ws_bytes, flags, partials,
                    ng_ld, stream);
 }
@@ -624,7 +627,7 @@ int moe_w4_layer_one_launch(int act, int T, int H, int I, int E, int k, int n_sh
 moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, int H, int I,
                         int E, int k, int renormalize, const moe_qmat* w13, const moe_qmat* w2,
                         const moe_qmat* w13_shared, const moe_qmat* w2_shared, int n_shared,
-                        int I_shared, int tile_m, int32_t* topk_ids, float* topk_w,
+                        int I_shared, const float* shared_gate, int tile_m, int32_t* topk_ids, float* topk_w,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                         int32_t* pair_pos, int32_t* tiles, int32_t* n_tiles, void* h,
                         void* out, void* workspace, size_t ws_bytes, int flags,
@@ -692,6 +695,7 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, 
     ad.topk_w = topk_w;
     ad.pair_pos = pair_pos;
     ad.out_f32 = (flags & MOE_OUT_F32) ? 1 : 0;
+    ad.sh_gate = n_shared > 0 ? shared_gate : nullptr;
     bool launched = false;
     const hipError_t e = launch_dec_layer(
         ag, ad, logits, renormalize, tile_m, topk_ids, topk_w, counts, offsets, sorted_pair,
@@ -705,7 +709,7 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, 
                                 sorted_pair, pair_pos, tiles, n_tiles, h, workspace, ws_bytes,
                                 flags, stream);
   if (st != MOE_OK) return st;
-  return moe_w4_down_combine(act, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared, topk_w,
-                             offsets, sorted_pair, pair_pos, tiles, n_tiles, tile_m, out,
-                             workspace, ws_bytes, flags, stream);
+  return moe_w4_down_combine(act, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared,
+                             shared_gate, topk_w, offsets, sorted_pair, pair_pos, tiles,
+                             n_tiles, tile_m, out, workspace, ws_bytes, flags, stream);
 }

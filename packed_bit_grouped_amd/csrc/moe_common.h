@@ -143,6 +143,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 // int8 row quantizer of the A8 mode: s = fp32(amax) / 127 (IEEE division),
 // q = clamp(rint(v / s), -127, 127); amax == 0 gives s = 0 and q = 0.
 // The projections and the standalone call use these same two functions.
+// Weight of a shared expert for one token from its gate logit l:
+// sigmoid(l) = 1 / (1 + exp(-l)) in fp32 (every combine uses this one).
+__device__ __forceinline__ float shared_gate_weight(float l) {
+  return 1.0f / (1.0f + expf(-l));
+}
+
 __device__ __forceinline__ float a8_scale(float amax) {
   return amax / 127.0f;
 }

@@ -63,6 +63,7 @@ struct ProjArgs {
   const float* topk_w;
   const int32_t* pair_pos;
   int out_f32;                 // the combined output is fp32 (else bf16)
+  const float* sh_gate;        // shared-expert gate logits [T][n_shared], or null (weight 1)
   int32_t* partials;           // A8 test hook (null otherwise)
   int ng_ld;
   int part_rows;               // row stride (in weight rows) of partials
@@ -136,6 +137,7 @@ hipError_t launch_proj_m16(const ProjArgs& a, int act, hipStream_t st);
 // out: bf16 [T][H], or fp32 [T][H] when out_f32
 hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
                           const int32_t* pair_pos, int T, int k, int H, int P,
-                          int n_shared, void* out, int out_f32, hipStream_t st);
+                          int n_shared, const float* sh_gate, void* out, int out_f32,
+                          hipStream_t st);
 
 }  // namespace moe

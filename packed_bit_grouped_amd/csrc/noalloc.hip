@@ -47,7 +47,8 @@ __global__ void err_report_kernel(const int32_t* w, int32_t* out) { *out = *w; }
 extern "C" moe_status moe_w4_layer_noalloc(
     int act, const float* logits, const uint16_t* x, int T, int H, int I, int E, int k,
     int renormalize, const moe_qmat* w13, const moe_qmat* w2, const moe_qmat* w13_shared,
-    const moe_qmat* w2_shared, int n_shared, int I_shared, int tile_m, int32_t* topk_ids,
+    const moe_qmat* w2_shared, int n_shared, int I_shared, const float* shared_gate,
+    int tile_m, int32_t* topk_ids,
     float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
     int32_t* tiles, int32_t* n_tiles, void* h, void* out, int32_t* err_out, int flags,
     void* stream) {
@@ -67,7 +68,7 @@ extern "C" moe_status moe_w4_layer_noalloc(
   }
   const moe_status st = moe_w4_layer(
       act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared, w2_shared, n_shared,
-      I_shared, tile_m, topk_ids, topk_w, counts, offsets, sorted_pair, pair_pos, tiles,
+      I_shared, shared_gate, tile_m, topk_ids, topk_w, counts, offsets, sorted_pair, pair_pos, tiles,
       n_tiles, h, out, ws, kScratchBytes, flags, stream);
   if (st != MOE_OK || !err_out) return st;
   err_report_kernel<<<1, 1, 0, s>>>(err, err_out);

@@ -690,7 +690,11 @@ __device__ __forceinline__ void dn_combine(const ProjArgs& a, const int* ppos, c
       for (int u = 0; u < 8; ++u)
         if (pp[u] >= 0) acc = fmaf(wj[u], yv[u], acc);
     }
-    for (int s = 0; s < a.n_shared; ++s) acc += yb[(size_t)(a.P + s * a.T + t) * kDecDnCols + cc];
+    for (int s = 0; s < a.n_shared; ++s) {
+      // weight 1 (fmaf(1, y, acc) is acc + y) or the token's sigmoid gate
+      const float g = a.sh_gate ? shared_gate_weight(a.sh_gate[t * a.n_shared + s]) : 1.0f;
+      acc = fmaf(g, yb[(size_t)(a.P + s * a.T + t) * kDecDnCols + cc], acc);
+    }
     if (a.out_f32) static_cast<float*>(out)[(size_t)t * H + n0 + cc] = acc;
     else static_cast<uint16_t*>(out)[(size_t)t * H + n0 + cc] = (uint16_t)f32_to_bf16(acc);
   }

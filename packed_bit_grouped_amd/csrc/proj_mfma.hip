@@ -247,9 +247,12 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
     }
   };
   // A staging: 32 * MB rows x 128 bytes per step, LDS laid out [row m][8
-  // 16-byte K chunks] with chunk ci of row m stored at slot ci ^ (m & 7),
-  // so the 8 lanes of an LDS pass hit distinct banks both when a row's
-  // 8 chunks are written and when 8 rows' chunk ci are read.  Thread tid
+  // 16-byte K chunks] with chunk ci of row m stored at slot ci ^ ((m >> 1)
+  // & 7).  A 128-bit LDS access is served 16 lanes (256 bytes, the 64
+  // banks) at a time: the fragment read of 16 consecutive rows' chunk ci
+  // then covers every bank once (even rows take the lower 128 bytes of the
+  // bank space, odd rows the upper, and within a parity the 8 rows have 8
+  // distinct slots); with ci ^ (m & 7), rows m and m + 8 collided.  Thread tid
   // moves chunk tid & 7 of rows (tid >> 3) + 32 i (i < MB): 8 lanes read
   // one whole 128-byte line from memory.
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(c.asrc, c.a_bytes);
@@ -263,7 +266,7 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
     for (int i = 0; i < MB; ++i) ar.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ars, aoff[i], o, 0);
   };
   auto store_a = [&](int buf, const AStep<MB>& ar) {
-    u32x4_v* d = As + buf * kChunks * kRowsMax + m_own * kChunks + (ci_own ^ (m_own & 7));
+    u32x4_v* d = As + buf * kChunks * kRowsMax + m_own * kChunks + (ci_own ^ ((m_own >> 1) & 7));
 #pragma unroll
     for (int i = 0; i < MB; ++i) d[32 * kChunks * i] = ar.a[i];
   };
@@ -290,7 +293,7 @@ __device__ __forceinline__ void mfma_chunk(const ProjArgs& a, const TileCtx& c,
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        af[st][mb] = Ab[32 * kChunks * mb + ((kh * 4 + st) ^ (ln & 7))];
+        af[st][mb] = Ab[32 * kChunks * mb + ((kh * 4 + st) ^ ((ln >> 1) & 7))];
     const uint32_t m16 = live ? 0x10001u : 0u;
     const f16x2_v s0 = as_h2(sc0 * m16);
     const f16x2_v s1 = as_h2(sc1 * m16);

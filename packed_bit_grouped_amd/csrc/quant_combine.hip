@@ -46,7 +46,7 @@ hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y, int ld_y, const float* __restrict__ topk_w,
     const int32_t* __restrict__ pair_pos, int T, int k, int H, int P,
-    int n_shared, void* __restrict__ out, int out_f32) {
+    int n_shared, const float* __restrict__ sh_gate, void* __restrict__ out, int out_f32) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= H) return;
@@ -77,10 +77,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
   for (int s = 0; s < n_shared; ++s) {
     const float4 v =
         *reinterpret_cast<const float4*>(y + (size_t)(P + s * T + t) * ld_y + n);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+    // weight 1 (fmaf(1, v, acc) is acc + v) or the token's sigmoid gate
+    const float g = sh_gate ? shared_gate_weight(sh_gate[t * n_shared + s]) : 1.0f;
+    acc.x = fmaf(g, v.x, acc.x);
+    acc.y = fmaf(g, v.y, acc.y);
+    acc.z = fmaf(g, v.z, acc.z);
+    acc.w = fmaf(g, v.w, acc.w);
   }
   if (out_f32) {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H + n) = acc;
@@ -94,11 +96,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 hipError_t launch_combine(const float* y, int ld_y, const float* topk_w,
                           const int32_t* pair_pos, int T, int k, int H, int P,
-                          int n_shared, void* out, int out_f32, hipStream_t st) {
+                          int n_shared, const float* sh_gate, void* out, int out_f32,
+                          hipStream_t st) {
   if (T == 0) return hipSuccess;
   const dim3 grid((H / 4 + 255) / 256, T);
   combine_kernel<<<grid, 256, 0, st>>>(y, ld_y, topk_w, pair_pos, T, k, H, P,
-                                       n_shared, out, out_f32);
+                                       n_shared, sh_gate, out, out_f32);
   return hipGetLastError();
 }
 

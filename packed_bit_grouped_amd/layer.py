@@ -144,13 +144,15 @@ def fused_routing_ok(T, E, k) -> bool:
 
 def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
               flags: int = 0, stream=None, fused: bool = True,
-              one_call: bool = True) -> None:
+              one_call: bool = True, shared_gate=None) -> None:
     """One layer step: route, permute, gate/up + SiLU*mul, down + combine.
     With ``fused`` and ``one_call`` the whole step is moe_w4_layer (with
     MOE_LAYER_ONE_LAUNCH in ``flags``: one launch for small bf16 decode
     batches); with ``fused`` alone the first three go through
     moe_w4_route_gateup_silu and the rest through moe_w4_down_combine;
-    otherwise every call is issued separately."""
+    otherwise every call is issued separately.  ``shared_gate``: fp32
+    [T][n_shared] gate logits of the shared experts (sigmoid gate), or
+    None (weight 1.0)."""
     T, H, I, E, k = B.T, B.H, B.I, B.E, B.k
     flags |= B.out_flags
     if not (fused and one_call):
@@ -160,7 +162,7 @@ def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
                        bank.w2, bank.w13_sh, bank.w2_sh, B.n_shared, B.I_shared,
                        B.tile_m, B.ids, B.w, B.counts, B.offsets, B.sorted_pair,
                        B.pair_pos, B.tiles, B.n_tiles, B.h, B.out, B.ws,
-                       B.ws_bytes, flags, stream)
+                       B.ws_bytes, flags, stream, shared_gate=shared_gate)
         return
     if fused:
         L.moe_w4_route_gateup_silu(B.act, logits, x, T, H, I, E, k, renormalize,
@@ -184,7 +186,8 @@ def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
     L.moe_w4_down_combine(B.act, B.h, T, H, I, E, k, bank.w2, bank.w2_sh,
                           B.n_shared, B.I_shared, B.w, B.offsets,
                           B.sorted_pair, B.pair_pos, B.tiles, B.n_tiles,
-                          B.tile_m, B.out, B.ws, B.ws_bytes, flags, stream)
+                          B.tile_m, B.out, B.ws, B.ws_bytes, flags, stream,
+                          shared_gate=shared_gate)
 
 
 def bf16_to_float(t):
@@ -200,6 +203,7 @@ class DeviceLayer:
     x: object          # int16 [T][H] (bf16 bits)
     logits: object     # float32 [T][E]
     bank: Bank
+    shared_gate: Optional[object] = None   # float32 [T][n_shared] gate logits, or None
 
     @classmethod
     def from_synth(cls, layer, device="cuda") -> "DeviceLayer":
@@ -208,7 +212,9 @@ class DeviceLayer:
         x = torch.from_numpy(layer.x_bf16.view(np.int16).copy()).to(dev)
         logits = torch.from_numpy(np.ascontiguousarray(layer.logits)).to(dev)
         bank = upload_bank(layer.experts, layer.shared, dev)
-        return cls(layer.cfg, x, logits, bank)
+        sg = getattr(layer, "shared_gate_logits", None)
+        sg = None if sg is None else torch.from_numpy(np.ascontiguousarray(sg)).to(dev)
+        return cls(layer.cfg, x, logits, bank, sg)
 
     def buffers(self, act=None, tile_m=None, out_f32=False) -> LayerBuffers:
         c = self.cfg
@@ -219,4 +225,4 @@ class DeviceLayer:
     def run(self, B: LayerBuffers, flags: int = 0, stream=None, fused: bool = True,
             one_call: bool = True) -> None:
         run_layer(self.bank, self.x, self.logits, B, self.cfg.renormalize,
-                  flags, stream, fused, one_call)
+                  flags, stream, fused, one_call, self.shared_gate)

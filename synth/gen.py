@@ -35,7 +35,7 @@ import multiprocessing as mp
 import numpy as np
 
 # stream ids of SeedSequence([seed, key, stream, expert, matrix])
-_S_X, _S_ROUTER, _S_ZIPF, _S_INT2, _S_EXPERT = 1, 2, 3, 4, 5
+_S_X, _S_ROUTER, _S_ZIPF, _S_INT2, _S_EXPERT, _S_SHGATE = 1, 2, 3, 4, 5, 6
 
 
 @dataclass(frozen=True)
@@ -55,6 +55,7 @@ class LayerConfig:
     n_shared: int = 0        # always-on shared experts (weight 1.0)
     I_shared: int = 0
     zipf_s: float = 0.0      # 0: no router bias; else Zipf(s) log-prior bias
+    shared_gate: bool = False   # shared experts gated by sigmoid(x . w_gate)
     renormalize: int = 1
     x_std: float = 1.0
     w_std: float = 0.02
@@ -178,6 +179,10 @@ class Layer:
     experts: List[Expert]        # E routed experts
     shared: List[Expert]         # n_shared shared experts
     int2_experts: np.ndarray     # int64 sorted ids of the int2 experts
+    # sigmoid-gated shared experts: gate weights fp32 [n_shared][H] and the
+    # gate logits fp32 [T][n_shared] = fp32(x . w in fp64); None otherwise
+    shared_gate_w: Optional[np.ndarray] = None
+    shared_gate_logits: Optional[np.ndarray] = None
 
     def expert_bits(self) -> np.ndarray:
         return np.array([e.w13.bits for e in self.experts], dtype=np.int32)
@@ -292,8 +297,15 @@ def make_layer(cfg: LayerConfig, seed: int = 0, workers: Optional[int] = None,
     for e, ex in zip(wanted, made[:len(wanted)]):
         experts[e] = ex
     shared = made[len(wanted):]
+    sg_w = sg_logits = None
+    if cfg.shared_gate and cfg.n_shared:
+        # one gate vector per shared expert, drawn like the router weights;
+        # its logits are computed once here, as the router logits are
+        sg_w = _rng(seed, cfg.key, _S_SHGATE).standard_normal(
+            (cfg.n_shared, H), dtype=np.float32) * np.float32(cfg.router_std)
+        sg_logits = (x64 @ sg_w.astype(np.float64).T).astype(np.float32)
     layer = Layer(cfg, seed, x_bf16, router_w, bias, logits, experts, shared,
-                  int2)
+                  int2, sg_w, sg_logits)
     if cache_dir and experts_only is None:
         os.makedirs(cache_dir, exist_ok=True)
         _save_layer(layer, path)
@@ -337,6 +349,9 @@ def _save_layer(layer: Layer, path: str) -> None:
             "logits": layer.logits, "int2": layer.int2_experts}
     if layer.bias is not None:
         arrs["bias"] = layer.bias
+    if layer.shared_gate_w is not None:
+        arrs["shared_gate_w"] = layer.shared_gate_w
+        arrs["shared_gate_logits"] = layer.shared_gate_logits
     for tag, lst in (("e", layer.experts), ("s", layer.shared)):
         for i, ex in enumerate(lst):
             for m in ("w13", "w2"):
@@ -360,5 +375,6 @@ def _load_layer(cfg: LayerConfig, seed: int, path: str) -> Layer:
     shared = [Expert(qm("s", i, "w13"), qm("s", i, "w2"))
               for i in range(cfg.n_shared)]
     bias = z["bias"] if "bias" in z.files else None
+    sg = (z["shared_gate_w"], z["shared_gate_logits"]) if "shared_gate_w" in z.files else (None, None)
     return Layer(cfg, seed, z["x_bf16"], z["router_w"], bias, z["logits"],
-                 experts, shared, z["int2"])
+                 experts, shared, z["int2"], *sg)

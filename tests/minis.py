@@ -22,4 +22,11 @@ MINIS = {
     "kE": LayerConfig("tiny_kE", 105, T=3, H=64, E=4, k=4, I=32, group=32),
     "norenorm": LayerConfig("tiny_norenorm", 106, T=4, H=64, E=6, k=2, I=32,
                             group=32, renormalize=0),
+    # sigmoid-gated shared experts
+    "gated_shared": LayerConfig("tiny_gated_shared", 107, T=6, H=128, E=5, k=2, I=64,
+                                group=32, n_int2=1, group_int2=64, n_shared=2,
+                                I_shared=96, shared_gate=True),
+    "gated_shared_a8": LayerConfig("tiny_gated_shared_a8", 108, T=5, H=128, E=4, k=2,
+                                   I=64, group=64, n_shared=1, I_shared=64,
+                                   shared_gate=True, act="a8"),
 }

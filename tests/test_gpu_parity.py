@@ -125,6 +125,48 @@ def test_mfma_path_tile_sizes(tile_m):
     _check_layer(MFMA["mfma_mixed"], tile_m=tile_m, flags=2)
 
 
+GATED = {
+    "gated_mfma": LayerConfig("mfma_gated", 213, T=300, H=512, E=8, k=2, I=256, group=128,
+                              n_int2=2, group_int2=64, n_shared=1, I_shared=384,
+                              shared_gate=True),
+    "gated_c1": LAYERS["decode_w4a16_t1"].replace(name="decode_w4a16_t1_gated",
+                                                  shared_gate=True),
+    "gated_t12": LAYERS["specdecode_w4a16_t12"].replace(name="specdecode_w4a16_t12_gated",
+                                                        shared_gate=True),
+}
+
+
+@pytest.mark.parametrize("name,act,flags,tile_m", [
+    ("gated_shared", "a16", 0, 16), ("gated_shared", "a16", 1, 16),
+    ("gated_shared", "a16", 3, 16), ("gated_shared", "a8", 0, 16),
+    ("gated_shared_a8", "a8", 3, 16), ("gated_shared_a8", "a8", 1, 16),
+    ("gated_mfma", "a16", 2, 160), ("gated_mfma", "a16", 0, 16),
+    ("gated_c1", "a16", 0, 16), ("gated_t12", "a16", 0, 16)])
+def test_sigmoid_gated_shared_experts(name, act, flags, tile_m):
+    """Shared experts gated per token by sigmoid(gate logit), on every
+    combine: the decode kernel's fused combine, the combine kernel after the
+    split-K, 16-row and matrix-core paths."""
+    cfg = MINIS.get(name) or GATED[name]
+    _check_layer(cfg, act=act, tile_m=tile_m, flags=flags)
+
+
+@pytest.mark.parametrize("name", ["gated_c1", "gated_shared"])
+def test_sigmoid_gate_one_launch_matches_two_calls(name):
+    """The one-launch decode layer applies the same gate as the two calls,
+    bit for bit."""
+    from packed_bit_grouped_amd import _lib as L
+    cfg = MINIS.get(name) or GATED[name]
+    dl = _dev(cfg)
+    assert L.moe_w4_layer_one_launch(0, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.n_shared,
+                                     cfg.I_shared, 16, L.MOE_LAYER_ONE_LAUNCH) == 1
+    g1, _ = run_layer_gpu(dl, "a16", 16, flags=L.MOE_LAYER_ONE_LAUNCH)
+    g2, _ = run_layer_gpu(dl, "a16", 16)
+    assert np.array_equal(g1["out"], g2["out"]) and g1["err"] == 0
+    o = oracle.oracle_layer(_layer(cfg))
+    ok, rl2, mabs, rms = float_gate(g1["out"], o["out"])
+    assert rl2 <= 5e-3
+
+
 def test_mfma_path_rejects_a8_and_odd_shapes():
     from packed_bit_grouped_amd import _lib as L
     dl = _dev(MID["mid_mixed"])       # I_shared = 192: not a multiple of 128

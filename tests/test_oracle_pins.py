@@ -394,6 +394,33 @@ def test_shared_expert_joins_with_weight_one():
     assert np.allclose(full, ref, rtol=1e-12, atol=1e-15)
 
 
+def test_shared_gate_is_the_sigmoid_of_the_gate_logit():
+    """Sigmoid-gated shared experts: with every gate logit set to l the
+    layer equals the routed-only layer (built without shared experts) plus
+    sigmoid(l) times the shared experts' ungated contribution; sigmoid(0) =
+    1/2, sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 exactly, so a gate
+    applied to the wrong terms or with the wrong sign fails."""
+    import dataclasses
+    layer = make_layer(MINIS["gated_shared"])
+    cfg = layer.cfg
+    assert layer.shared_gate_logits.shape == (cfg.T, cfg.n_shared)
+    routed = Layer(cfg.replace(n_shared=0, I_shared=0, shared_gate=False), 0, layer.x_bf16,
+                   layer.router_w, layer.bias, layer.logits, layer.experts, [],
+                   layer.int2_experts)
+    r_out = oracle.oracle_layer(routed)["out"]
+    u_out = oracle.oracle_layer(dataclasses.replace(layer, shared_gate_logits=None))["out"]
+    for lv, sig in ((0.0, 0.5), (math.log(3.0), 0.75), (-math.log(3.0), 0.25),
+                    (2.5, 1.0 / (1.0 + math.exp(-2.5)))):
+        gl = np.full((cfg.T, cfg.n_shared), lv)
+        o = oracle.oracle_layer(dataclasses.replace(layer, shared_gate_logits=gl))["out"]
+        assert np.allclose(o, r_out + sig * (u_out - r_out), rtol=1e-12, atol=1e-14), lv
+    # the gate logits are the generator's fp32(x . w_gate), one per token and shared expert
+    x = (layer.x_bf16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want = np.array([[sum(x[t, h] * float(layer.shared_gate_w[s, h]) for h in range(cfg.H))
+                      for s in range(cfg.n_shared)] for t in range(cfg.T)])
+    assert np.allclose(layer.shared_gate_logits, want, rtol=1e-6, atol=1e-7)
+
+
 def test_token_sample_path_matches_full_layer():
     for name in ("mixed_shared", "mixed_shared_a8", "c0"):
         layer = make_layer(MINIS[name])
