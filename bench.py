@@ -198,6 +198,10 @@ def run_config(cid, args, torch, L, hi, ceiling):
     layer = make_layer(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
     dl = DeviceLayer.from_synth(layer, "cuda:0")
+    if args.prepacked and not decode:
+        # codes re-tiled into the matrix-core layout (moe_w4_prepack)
+        dl.bank = dl.bank.prepack()
+        torch.cuda.synchronize()
     act = cfg.act
     B = dl.buffers(act)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
@@ -266,6 +270,7 @@ def run_config(cid, args, torch, L, hi, ceiling):
     fused = (decode and act == "a16" and P <= 64 and E <= 512 and B.tile_m <= 16 and H <= 2048)
 
     def gateup(bk):
+        gflags = flags | (L.MOE_W_PREPACKED if bk.prepacked else 0)
         if fused:
             L.moe_w4_route_gateup_silu(B.act, dl.logits, dl.x, T, H, I, E, k,
                                        cfg.renormalize, bk.w13, bk.w13_sh, cfg.n_shared,
@@ -275,7 +280,7 @@ def run_config(cid, args, torch, L, hi, ceiling):
         else:
             L.moe_w4_gateup_silu(B.act, dl.x, T, H, I, E, k, bk.w13, bk.w13_sh,
                                  cfg.n_shared, cfg.I_shared, B.offsets, B.sorted_pair,
-                                 B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes, flags)
+                                 B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes, gflags)
 
     if fused:
         kname = "dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)"
@@ -283,7 +288,8 @@ def run_config(cid, args, torch, L, hi, ceiling):
         kname = ("proj_m16_kernel<0> (gate/up + SiLU*mul)" if act == "a16" else
                  "proj_m16_kernel<0> (int8 x rows made in the kernel, gate/up + SiLU*mul)")
     else:
-        kname = "proj_mfma_kernel<0> + convert_x_kernel (gate/up + SiLU*mul)"
+        kname = ("proj_mfma8_kernel<0> + convert8_kernel (gate/up + SiLU*mul)"
+                 + (", prepacked weights" if dl.bank.prepacked else ""))
     n_k = len(banks) if decode else 4
     gk = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gk):
@@ -332,6 +338,7 @@ def run_config(cid, args, torch, L, hi, ceiling):
                    "n_shared": cfg.n_shared, "act": act, "experts_touched": n_touched,
                    "bytes_per_step": bytes_all, "flops_per_step": flops,
                    "bank_copies_rotated": len(banks), "path": args.path,
+                   "weights": "prepacked" if dl.bank.prepacked else "canonical",
                    "timing": (f"HIP graphs of {G} steps over {G} weight copies, replayed in "
                               f"cycle order after {w_reps} warm-up replays"),
                    "ms_per_step_eager": ms_eager},
@@ -358,6 +365,8 @@ def main():
     ap.add_argument("--cpu-prefill-experts", type=int, default=12,
                     help="experts of the prefill layer in the CPU oracle's sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prepacked", action="store_true",
+                    help="prefill: run on a bank re-tiled by moe_w4_prepack")
     ap.add_argument("--path", choices=["auto", "gemv", "mfma"], default="auto")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="after the run, one device copy of MB MiB (a plain copy kernel of "

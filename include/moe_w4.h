@@ -240,6 +240,10 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
 #define MOE_LAYER_ONE_LAUNCH 8 /* moe_w4_layer: one launch for the whole    */
                               /* layer where the shape allows it (same      */
                               /* results as the two calls)                  */
+#define MOE_W_PREPACKED 32    /* the weight tables' codes are in the layout */
+                              /* of moe_w4_prepack (scales unchanged); read */
+                              /* by the matrix-core path only: any other    */
+                              /* path returns MOE_E_UNSUPPORTED             */
 #define MOE_OUT_F32 16        /* moe_w4_down_combine / moe_w4_layer: out is */
                               /* fp32 [T][H] (16-byte aligned) holding the  */
                               /* combined sum before any rounding to bf16;  */
@@ -251,6 +255,30 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
  * T*k >= 32*E with A16, else 16.  Both paths accept any tile_m; the MFMA
  * path walks longer tiles in 160-row chunks. */
 int moe_preferred_tile_m(int act, int T, int E, int k);
+
+/* ---------------------------------------------------------------------
+ * moe_w4_prepack -- optional re-tiling of one packed code matrix into the
+ * order the matrix-core path (MOE_PATH_MFMA, prefill shapes) loads it in,
+ * the analogue of the operand layout the build log "Two 96 GB Ascend cards
+ * run Qwen3.8 Flash-Next" adds for its matrix unit (section "Keep low-bit
+ * weights packed, do the work on the NPU").  The canonical layout keeps
+ * working everywhere; a prepacked bank is read only with MOE_W_PREPACKED.
+ *   codes   canonical codes of a [N][K] matrix (moe_qmat layout), device
+ *   bits    4 or 2
+ *   gate_up 1 for a gate/up matrix [2I][H] (rows i and I + i are paired),
+ *           0 for a down matrix [H][I]
+ *   dst     device, N*K*bits/8 bytes (the same size), not overlapping codes
+ * Layout of dst: blocks of 32 rows (gate/up: gate rows 16b..16b+15 then up
+ * rows I+16b..I+16b+15; down: rows 32b..32b+31), per block the K/64 steps,
+ * per step 64 lane slots; slot h*32 + c holds bytes [32 s + 16 h, +16) of
+ * the block's row c for int4, [16 s + 8 h, +8) for int2 with every 4-byte
+ * word's bytes in the order (0, 2, 1, 3).  The fp16 scales are not
+ * changed: a prepacked descriptor keeps the matrix's scale array.
+ * Limits: N % 32 == 0, K % 128 == 0.  Errors: MOE_E_INVAL,
+ * MOE_E_UNSUPPORTED, MOE_E_DEVICE.  Asynchronous on `stream`.
+ * ------------------------------------------------------------------- */
+moe_status moe_w4_prepack(const uint8_t* codes, int bits, int N, int K, int gate_up,
+                          uint8_t* dst, void* stream);
 
 /* ---------------------------------------------------------------------
  * moe_w4_gateup_silu -- grouped gate/up projection of every routed pair

@@ -22,6 +22,7 @@ MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA16 = 0, 1, 2, 3
 MOE_QUANT_SEPARATE = 4
 MOE_LAYER_ONE_LAUNCH = 8
 MOE_OUT_F32 = 16
+MOE_W_PREPACKED = 32
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -73,6 +74,7 @@ _SIGS = {
                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                              c_int, c_void_p]),
     "moe_read_stream": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
+    "moe_w4_prepack": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
     "moe_w4_layer_noalloc": (c_int, [c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                      c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_int, c_int, c_void_p, c_int, c_void_p,
@@ -271,6 +273,11 @@ def moe_w4_layer(act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared
                  _ptr(counts), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
                  _ptr(tiles), _ptr(n_tiles), _ptr(h), _ptr(out), _ptr(workspace),
                  ws_bytes, flags, _stream(stream), check=check)
+
+
+def moe_w4_prepack(codes, bits, N, K, gate_up, dst, stream=None, check=True):
+    return _call("moe_w4_prepack", _ptr(codes), bits, N, K, gate_up, _ptr(dst),
+                 _stream(stream), check=check)
 
 
 def moe_read_stream(src, nbytes, sink, n_blocks, stream=None, check=True):

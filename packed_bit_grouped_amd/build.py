@@ -17,8 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmoe_w4.so")
 SOURCES = ["api.cpp", "route_permute.hip", "quant_combine.hip",
-           "proj_gemv.hip", "proj_decode.hip", "proj_mfma.hip", "proj_m16.hip",
-           "noalloc.hip", "probe.hip"]
+           "proj_gemv.hip", "proj_decode.hip", "proj_m16.hip",
+           "proj_mfma8.hip", "noalloc.hip", "probe.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU forms are kept out of the generated code

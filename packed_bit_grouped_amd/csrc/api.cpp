@@ -69,7 +69,8 @@ moe_status check_layer(int act, int T, int H, int I, int E, int k, int n_shared,
   if (k > E) return MOE_E_INVAL;
   if (n_shared > 0 && I_shared <= 0) return MOE_E_INVAL;
   if (tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
-  if (flags & ~(MOE_PATH_MASK | MOE_QUANT_SEPARATE | MOE_OUT_F32)) return MOE_E_INVAL;
+  if (flags & ~(MOE_PATH_MASK | MOE_QUANT_SEPARATE | MOE_OUT_F32 | MOE_W_PREPACKED))
+    return MOE_E_INVAL;
   if (H % 32 || I % 32 || (n_shared > 0 && I_shared % 32)) return MOE_E_UNSUPPORTED;
   if (E > kPermMaxE) return MOE_E_UNSUPPORTED;
   if ((long long)T * k >= (1LL << 24)) return MOE_E_UNSUPPORTED;
@@ -135,7 +136,7 @@ WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
   L.a16 = off;
   if (act == MOE_A16 && mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) {
     const size_t ld_h = (size_t)(n_shared > 0 && I_shared > I ? I_shared : I);
-    const size_t xs = (size_t)2 * T * H * 2;
+    const size_t xs = (size_t)T * H * 2;
     const size_t hs = (size_t)T * (k + n_shared) * ld_h * 2;
     off += up256(xs > hs ? xs : hs);
   }
@@ -325,12 +326,14 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   a.ng_ld = ng_ld;
   a.part_rows = 2 * ld_h;
 
+  const bool pp = (flags & MOE_W_PREPACKED) != 0;
   if (use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags)) {
     if (!mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) return MOE_E_UNSUPPORTED;
     a.in_bf16 = x;
     uint16_t* x16 = reinterpret_cast<uint16_t*>(ws + L.a16);
-    return from_hip(launch_proj_mfma(a, x16, x16 + (size_t)T * H, s));
+    return from_hip(launch_proj_mfma8(a, x16, pp, s));
   }
+  if (pp) return MOE_E_UNSUPPORTED;   // the prepacked layout is read by the matrix-core path only
   const bool dec = act == MOE_A16 && !partials && dec_gateup_ok(T, H, tile_m);
   const bool on_m16 = path == MOE_PATH_MFMA16 ||
                       (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs));
@@ -419,14 +422,16 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
   a.part_rows = H;
 
   hipError_t e;
+  const bool pp = (flags & MOE_W_PREPACKED) != 0;
   if (use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags)) {
     if (!mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) return MOE_E_UNSUPPORTED;
     a.in_bf16 = static_cast<const uint16_t*>(h);
-    e = launch_proj_mfma(a, reinterpret_cast<uint16_t*>(ws + L.a16), nullptr, s);
+    e = launch_proj_mfma8(a, reinterpret_cast<uint16_t*>(ws + L.a16), pp, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
                                    n_shared, shared_gate, out, out_f32, s));
   }
+  if (pp) return MOE_E_UNSUPPORTED;   // the prepacked layout is read by the matrix-core path only
   if (act == MOE_A8) a.in_f32 = static_cast<const float*>(h);
   else a.in_bf16 = static_cast<const uint16_t*>(h);
   const bool dec = act == MOE_A16 && !partials &&
@@ -493,6 +498,7 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits, const uint16_t
   if (st != MOE_OK) return st;
   if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
   const bool fused = act == MOE_A16 && T > 0 && (flags & MOE_PATH_MASK) != MOE_PATH_MFMA16 &&
+                     !(flags & MOE_W_PREPACKED) &&
                      !use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
                      dec_route_gateup_ok(T, H, E, k, tile_m);
   if (!fused) {
@@ -598,12 +604,27 @@ moe_status moe_dbg_w4a8_down_partials(
 
 }  // extern "C"
 
+extern "C" moe_status moe_w4_prepack(const uint8_t* codes, int bits, int N, int K, int gate_up,
+                                     uint8_t* dst, void* stream) {
+  if (bits != 2 && bits != 4) return MOE_E_UNSUPPORTED;
+  if (N <= 0 || K <= 0 || (gate_up != 0 && gate_up != 1)) return MOE_E_INVAL;
+  if (N % 32 != 0 || K % 128 != 0) return MOE_E_UNSUPPORTED;
+  if ((long long)N * K * bits / 8 >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+  if (!codes || !dst || codes == dst) return MOE_E_INVAL;
+  if (!aligned(codes, 16) || !aligned(dst, 16)) return MOE_E_INVAL;
+  const moe_status d = check_device();
+  if (d != MOE_OK) return d;
+  return from_hip(launch_prepack(codes, bits, N, K, gate_up, dst,
+                                 static_cast<hipStream_t>(stream)));
+}
+
 // Shapes and flags for which moe_w4_layer issues one launch (before the
 // device's residency check).
 static bool layer_one_shape(int act, int T, int H, int I, int E, int k, int n_shared,
                             int I_shared, int tile_m, int flags) {
   const int path = flags & MOE_PATH_MASK;
   return act == MOE_A16 && T > 0 && (path == MOE_PATH_AUTO || path == MOE_PATH_GEMV) &&
+         !(flags & MOE_W_PREPACKED) &&
          !use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
          dec_layer_ok(T, H, I, I_shared, E, k, n_shared, tile_m,
                       moe_permute_max_tiles(T, k, E, tile_m), ld_h_of(I, n_shared, I_shared));

@@ -91,8 +91,14 @@ hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
                            int8_t* q, int ldq, float* s, hipStream_t st);
 hipError_t launch_proj_gemv(const ProjArgs& a, int act, int grid, hipStream_t st);
 int gemv_maxt(int T, int tile_m);
-hipError_t launch_proj_mfma(const ProjArgs& a, uint16_t* a16_4, uint16_t* a16_2,
-                            hipStream_t st);
+// Matrix-core grouped GEMM (two waves per SIMD); a16: workspace for one
+// fp16 copy of the activations; prepacked: the weight tables hold codes in
+// the layout of launch_prepack.
+hipError_t launch_proj_mfma8(const ProjArgs& a, uint16_t* a16, bool prepacked, hipStream_t st);
+// Re-tile one packed matrix [N][K] into the matrix-core fragment layout
+// (N % 32 == 0, K % 64 == 0); gate_up pairs gate rows with up rows.
+hipError_t launch_prepack(const uint8_t* src, int bits, int N, int K, int gate_up, uint8_t* dst,
+                          hipStream_t st);
 bool mfma_available();
 // Decode-shape A16 projections (proj_decode.hip): tiles of at most 16
 // rows, H <= 2048 (gate/up) and I <= 1024 (down), down with the combine

@@ -42,11 +42,26 @@ class Bank:
     nbytes_by_expert: np.ndarray   # packed bytes (codes + scales) per routed expert
     nbytes_shared: int
 
+    prepacked: bool = False  # codes in the matrix-core layout (MOE_W_PREPACKED)
+
     def rebased(self, buf) -> "Bank":
         """Same layout on another buffer (a device copy of ``buf``)."""
         t13, t2, s13, s2 = _tables(self.layout, buf)
         return Bank(buf, t13, t2, s13, s2, self.layout, self.nbytes_by_expert,
-                    self.nbytes_shared)
+                    self.nbytes_shared, self.prepacked)
+
+    def prepack(self) -> "Bank":
+        """A copy of the bank with every code matrix re-tiled by
+        moe_w4_prepack (scales shared in layout, copied with the buffer);
+        calls on it need MOE_W_PREPACKED (run_layer adds it)."""
+        buf = self.buf.clone()
+        base, dst = self.buf.data_ptr(), buf.data_ptr()
+        for tag, oc, os_, (bits, group, N, K) in self.layout:
+            L.moe_w4_prepack(base + oc, bits, N, K, 1 if tag in ("w13", "w13_sh") else 0,
+                             dst + oc)
+        b = self.rebased(buf)
+        b.prepacked = True
+        return b
 
 
 def _qmat_bytes(qm) -> int:
@@ -155,6 +170,8 @@ def run_layer(bank: Bank, x, logits, B: LayerBuffers, renormalize: int = 1,
     None (weight 1.0)."""
     T, H, I, E, k = B.T, B.H, B.I, B.E, B.k
     flags |= B.out_flags
+    if bank.prepacked:
+        flags |= L.MOE_W_PREPACKED
     if not (fused and one_call):
         flags &= ~L.MOE_LAYER_ONE_LAUNCH   # only moe_w4_layer takes it
     if fused and one_call:

@@ -128,7 +128,7 @@ def test_gateup_validation():
     assert _gateup(workspace=None) == L.MOE_E_WORKSPACE
     assert _gateup(workspace=FAKE + 64) == L.MOE_E_WORKSPACE  # 256-byte alignment
     assert _gateup(flags=8) == L.MOE_E_INVAL
-    assert _gateup(flags=32) == L.MOE_E_INVAL
+    assert _gateup(flags=64) == L.MOE_E_INVAL
     assert _gateup(flags=L.MOE_QUANT_SEPARATE | L.MOE_PATH_MFMA16, act=1) == L.MOE_E_DEVICE
     # forced 16-row MFMA tiles: tiles of at most 16 rows, activations in LDS
     assert _gateup(flags=L.MOE_PATH_MFMA16, tile_m=32) == L.MOE_E_UNSUPPORTED
@@ -219,7 +219,7 @@ def test_layer_validation():
     assert call(renormalize=2) == L.MOE_E_INVAL
     assert call(act=2) == L.MOE_E_INVAL
     assert call(k=129) == L.MOE_E_INVAL
-    assert call(flags=32) == L.MOE_E_INVAL
+    assert call(flags=64) == L.MOE_E_INVAL
     assert call(out=None) == L.MOE_E_INVAL
     assert call(w2_shared=None) == L.MOE_E_INVAL
     assert call(workspace=None) == L.MOE_E_WORKSPACE
@@ -286,4 +286,20 @@ def test_noalloc_validation():
     # decode shapes fit (the 64-token W4A8 layer included) and reach the device check
     assert L.moe_workspace_bytes(1, 64, 2048, 768, 128, 8) <= L.MOE_NOALLOC_SCRATCH_BYTES
     assert call(act=1, T=64, n_shared=0, I_shared=0) == L.MOE_E_DEVICE
+    assert call() == L.MOE_E_DEVICE
+
+
+def test_prepack_validation():
+    ok = dict(codes=FAKE, bits=4, N=256, K=512, gate_up=1, dst=FAKE + 4096)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_w4_prepack(*a.values(), stream=0, check=False)
+    assert call(bits=3) == L.MOE_E_UNSUPPORTED
+    assert call(N=48) == L.MOE_E_UNSUPPORTED       # blocks of 32 rows
+    assert call(K=64) == L.MOE_E_UNSUPPORTED       # K % 128
+    assert call(gate_up=2) == L.MOE_E_INVAL
+    assert call(dst=FAKE) == L.MOE_E_INVAL         # in place
+    assert call(dst=None) == L.MOE_E_INVAL
+    assert call(codes=FAKE + 8) == L.MOE_E_INVAL   # 16-byte aligned
     assert call() == L.MOE_E_DEVICE

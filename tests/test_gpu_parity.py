@@ -704,3 +704,47 @@ def test_unusable_descriptor_sets_error_word():
     dl.bank.w13.copy_(torch.from_numpy(raw))
     g, B = run_layer_gpu(dl, "a16", 16)
     assert g["err"] & 1
+
+
+@pytest.mark.parametrize("name,tile_m", [("mfma_mixed", 160), ("mfma_g32_int2", 128),
+                                         ("mfma_g256", 64), ("gated_mfma", 160)])
+def test_prepacked_bank_matches_canonical(name, tile_m):
+    """moe_w4_prepack re-tiles every code matrix into the matrix-core
+    layout; the layer run on the prepacked bank (MOE_W_PREPACKED) gives the
+    same h and output bits as on the canonical bank, which meets the gate
+    against the oracle."""
+    cfg = MFMA.get(name) or GATED[name]
+    dl = _dev(cfg)
+    g0, _ = run_layer_gpu(dl, "a16", tile_m, flags=2)
+    dl.bank = dl.bank.prepack()
+    g1, _ = run_layer_gpu(dl, "a16", tile_m, flags=2)
+    g32, _ = run_layer_gpu(dl, "a16", tile_m, flags=2, out_f32=True)
+    assert g1["err"] == 0
+    assert np.array_equal(g1["h"], g0["h"]) and np.array_equal(g1["out"], g0["out"])
+    o = oracle.oracle_layer(_layer(cfg), tile_m=tile_m)
+    check_out(g1, g32, o["out"], f"prepacked {cfg.name}")
+
+
+def test_prepacked_prefill_layer_matches_canonical():
+    """The prefill layer (4096 tokens, 192 int4 + 64 int2 experts) on a
+    prepacked bank: h and out identical to the canonical bank's, which is
+    compared with the oracle in full by test_prefill_layer_full."""
+    cfg = LAYERS["prefill_mixed_t4096"]
+    dl = _dev(cfg)
+    g0, _ = run_layer_gpu(dl, "a16", 160)
+    dl.bank = dl.bank.prepack()
+    g1, _ = run_layer_gpu(dl, "a16", 160)
+    assert g1["err"] == 0
+    assert np.array_equal(g1["h"], g0["h"]) and np.array_equal(g1["out"], g0["out"])
+
+
+def test_prepacked_bank_needs_the_matrix_core_path():
+    from packed_bit_grouped_amd import _lib as L
+    cfg = MINIS["mixed_shared"]
+    dl = _dev(cfg)
+    B = dl.buffers("a16", 16)
+    st = L.moe_w4_gateup_silu(0, dl.x, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dl.bank.w13,
+                              dl.bank.w13_sh, cfg.n_shared, cfg.I_shared, B.offsets,
+                              B.sorted_pair, B.tiles, B.n_tiles, 16, B.h, B.ws, B.ws_bytes,
+                              L.MOE_W_PREPACKED, check=False)
+    assert st == L.MOE_E_UNSUPPORTED
