@@ -133,12 +133,17 @@ WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
   }
   L.y = off;
   off += up256((size_t)T * (k + n_shared) * H * 4);
+  L.perm = off;
+  off += up256((size_t)permute_multi_blocks((int)((long long)T * k)) * E * 4);
   L.a16 = off;
+  L.h16 = off;
   if (act == MOE_A16 && mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) {
     const size_t ld_h = (size_t)(n_shared > 0 && I_shared > I ? I_shared : I);
     const size_t xs = (size_t)T * H * 2;
     const size_t hs = (size_t)T * (k + n_shared) * ld_h * 2;
     off += up256(xs > hs ? xs : hs);
+    L.h16 = off;
+    off += up256(hs);
   }
   L.total = off;
   return L;
@@ -278,7 +283,8 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
                               const int32_t* sorted_pair, const int32_t* tiles,
                               const int32_t* n_tiles, int tile_m, void* h,
                               void* workspace, size_t ws_bytes, int flags,
-                              int32_t* partials, int ng_ld, void* stream) {
+                              int32_t* partials, int ng_ld, void* stream,
+                              bool stage_h16 = false) {
   moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -331,6 +337,7 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
     if (!mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) return MOE_E_UNSUPPORTED;
     a.in_bf16 = x;
     uint16_t* x16 = reinterpret_cast<uint16_t*>(ws + L.a16);
+    if (stage_h16) a.out16 = reinterpret_cast<uint16_t*>(ws + L.h16);
     return from_hip(launch_proj_mfma8(a, x16, pp, s));
   }
   if (pp) return MOE_E_UNSUPPORTED;   // the prepacked layout is read by the matrix-core path only
@@ -368,7 +375,8 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
                             const int32_t* pair_pos, const int32_t* tiles,
                             const int32_t* n_tiles, int tile_m, void* out,
                             void* workspace, size_t ws_bytes, int flags,
-                            int32_t* partials, int ng_ld, void* stream) {
+                            int32_t* partials, int ng_ld, void* stream,
+                            bool h16_staged = false) {
   moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -426,6 +434,10 @@ static moe_status down_impl(int act, const void* h, int T, int H, int I, int E,
   if (use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags)) {
     if (!mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) return MOE_E_UNSUPPORTED;
     a.in_bf16 = static_cast<const uint16_t*>(h);
+    if (h16_staged) {
+      a.in_bf16 = reinterpret_cast<const uint16_t*>(ws + L.h16);
+      a.in16_ready = 1;
+    }
     e = launch_proj_mfma8(a, reinterpret_cast<uint16_t*>(ws + L.a16), pp, s);
     if (e != hipSuccess) return MOE_E_DEVICE;
     return from_hip(launch_combine(y, H, topk_w, pair_pos, T, k, H, T * k,
@@ -724,6 +736,35 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, 
         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return MOE_E_DEVICE;
     if (launched) return MOE_OK;
+  }
+  if (T > 0 && use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
+      mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) {
+    // matrix-core form: the gate/up epilogue also writes the fp16 copy of h
+    // the down projection reads, so no conversion pass runs between them
+    if (T <= kFusedRouteMaxT && (long long)T * k <= kFusedRouteMaxP && E <= kPermMaxE) {
+      st = moe_route_permute(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w, counts,
+                             offsets, sorted_pair, pair_pos, tiles, n_tiles, stream);
+    } else {
+      st = moe_route_topk(logits, T, E, k, renormalize, topk_ids, topk_w, stream);
+      if (st == MOE_OK && permute_multi_blocks(T * k) > 0) {
+        // the sort over many workgroups, with its counts in the workspace
+        st = from_hip(launch_permute_multi(
+            topk_ids, T * k, E, tile_m, counts, offsets, sorted_pair, pair_pos, tiles, n_tiles,
+            reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.perm),
+            static_cast<hipStream_t>(stream)));
+      } else if (st == MOE_OK) {
+        st = moe_permute(topk_ids, T, k, E, tile_m, counts, offsets, sorted_pair, pair_pos,
+                         tiles, n_tiles, stream);
+      }
+    }
+    if (st != MOE_OK) return st;
+    st = gateup_impl(act, x, T, H, I, E, k, w13, w13_shared, n_shared, I_shared, offsets,
+                     sorted_pair, tiles, n_tiles, tile_m, h, workspace, ws_bytes, flags,
+                     nullptr, 0, stream, true);
+    if (st != MOE_OK) return st;
+    return down_impl(act, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared, shared_gate,
+                     topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles, tile_m, out,
+                     workspace, ws_bytes, flags, nullptr, 0, stream, true);
   }
   st = moe_w4_route_gateup_silu(act, logits, x, T, H, I, E, k, renormalize, w13, w13_shared,
                                 n_shared, I_shared, tile_m, topk_ids, topk_w, counts, offsets,

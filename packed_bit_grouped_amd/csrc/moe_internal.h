@@ -21,7 +21,10 @@ struct WsLayout {
   size_t qh;         // A8: int8 h rows [R][ld_h] (matrix-core decode path)
   size_t sh;         // A8: fp32 [R]
   size_t y;          // fp32 [R][H]
-  size_t a16;        // A16 MFMA path: fp16 activation copies (x twice, or h)
+  size_t a16;        // A16 MFMA path: fp16 copy of x (gate/up) or of h (down)
+  size_t perm;       // moe_w4_layer: per-workgroup counts of the multi-workgroup sort
+  size_t h16;        // A16 MFMA path: fp16 copy of h written by the gate/up epilogue
+                     // (moe_w4_layer: the down call reads it instead of converting h)
   size_t total;
 };
 WsLayout ws_layout(int act, int T, int H, int I, int E, int k, int n_shared,
@@ -62,6 +65,8 @@ struct ProjArgs {
   // sorted row of every pair
   const float* topk_w;
   const int32_t* pair_pos;
+  uint16_t* out16;             // MFMA gate/up: also write h as fp16 in the unpack order, or null
+  int in16_ready;              // MFMA down: in_bf16 already holds that fp16 copy
   int out_f32;                 // the combined output is fp32 (else bf16)
   const float* sh_gate;        // shared-expert gate logits [T][n_shared], or null (weight 1)
   int32_t* partials;           // A8 test hook (null otherwise)
@@ -81,6 +86,15 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int tile_m,
                           int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos,
                           int32_t* tiles, int32_t* n_tiles, hipStream_t st);
+// The same sort over many workgroups for large batches: scratch holds
+// permute_multi_blocks(P) * E ints (zero blocks: P below the threshold,
+// the single-workgroup sort runs).
+constexpr int kPermMultiMinP = 8192;
+int permute_multi_blocks(int P);
+hipError_t launch_permute_multi(const int32_t* ids, int P, int E, int tile_m, int32_t* counts,
+                                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                int32_t* tiles, int32_t* n_tiles, int32_t* scratch,
+                                hipStream_t st);
 hipError_t launch_route_permute(const float* logits, int T, int E, int k,
                                 int renorm, int tile_m, int32_t* ids, float* w,
                                 int32_t* counts, int32_t* offsets,

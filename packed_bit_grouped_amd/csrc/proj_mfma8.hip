@@ -276,8 +276,19 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
         const float up = xch[j * 64 + (lane ^ 16)];
         if (lc < 16 && m < nrows && ln_.wval) {
           const float hv = silu_mul(acc[mb][j], up);
-          static_cast<uint16_t*>(a.out)[(size_t)(orow0 + m) * a.ld_out + ln_.wrow] =
-              (uint16_t)f32_to_bf16(hv);
+          const uint32_t hb = f32_to_bf16(hv);
+          const size_t o = (size_t)(orow0 + m) * a.ld_out;
+          static_cast<uint16_t*>(a.out)[o + ln_.wrow] = (uint16_t)hb;
+          if (a.out16) {
+            // the down projection's fp16 input: the bf16 value (exact in
+            // fp16's normal range) at its place in the unpack order of its
+            // 8-block, (0,4)(1,5)(2,6)(3,7)
+            const int u = ln_.wrow;
+            const int pos = (u & ~7) | ((u & 3) << 1) | ((u >> 2) & 1);
+            const uint32_t f16 = __builtin_bit_cast(
+                uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(hb << 16), 0.0f));
+            a.out16[o + pos] = (uint16_t)(f16 & 0xFFFFu);
+          }
         }
       } else {
         if (m < nrows && ln_.wval)
@@ -475,7 +486,7 @@ hipError_t launch_proj_mfma8(const ProjArgs& a_in, uint16_t* a16, bool prepacked
     const long long units = (long long)a.T * (a.K / 8);
     convert8_kernel<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.in_bf16, a.T, a.K,
                                                                      a.K, a16);
-  } else {
+  } else if (!a.in16_ready) {
     const long long R = (long long)a.P + (long long)a.n_shared * a.T;
     const int Kc = a.K_sh > a.K ? a.K_sh : a.K;
     const long long units = R * (Kc / 8);

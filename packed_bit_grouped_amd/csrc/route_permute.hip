@@ -151,6 +151,127 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int tile_m,
   for (int i = sm.total_valid + tid; i < P; i += 1024) sorted_pair[i] = -1;
 }
 
+// ---------------------------------------------------------------------
+// The same sort over many workgroups, for large batches (the layer call,
+// with its workspace): workgroup b takes pairs [b * kPermChunk, +kPermChunk).
+// (1) each workgroup counts its chunk per expert -> hist[b][e]; (2) one
+// workgroup forms counts, offsets and the tile list and turns hist into the
+// first sorted position of every (workgroup, expert): offsets[e] plus the
+// counts of workgroups 0..b-1; (3) each workgroup places its chunk from
+// those positions with the per-wave counts and ballot ranks of
+// permute_body.  Pairs of an expert stay in increasing p, so the result is
+// the single workgroup's, bit for bit.
+constexpr int kPermChunk = 2048;   // pairs per workgroup (128 per wave)
+
+__global__ __launch_bounds__(1024) void perm_hist_kernel(const int32_t* __restrict__ ids, int P,
+                                                         int E, int32_t* __restrict__ hist) {
+  __shared__ int h[kPermMaxE];
+  for (int i = threadIdx.x; i < E; i += 1024) h[i] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kPermChunk, p1 = min(P, p0 + kPermChunk);
+  for (int p = p0 + threadIdx.x; p < p1; p += 1024) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += 1024) hist[(size_t)blockIdx.x * E + i] = h[i];
+}
+
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int P, int E, int nb, int tile_m,
+                                                         int32_t* __restrict__ hist,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted_pair,
+                                                         int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ n_tiles) {
+  __shared__ int tmp[kPermWaves + 1];
+  __shared__ int total;
+  const int tid = threadIdx.x;
+  int cnt = 0;
+  if (tid < E)
+    for (int b = 0; b < nb; ++b) cnt += hist[(size_t)b * E + tid];
+  const int excl = block_exclusive_scan(cnt, tmp);
+  const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
+  const int texcl = block_exclusive_scan(ntile, tmp);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = excl;
+    int run = excl;
+    for (int b = 0; b < nb; ++b) {
+      const int c = hist[(size_t)b * E + tid];
+      hist[(size_t)b * E + tid] = run;
+      run += c;
+    }
+    for (int i = 0; i < ntile; ++i) {
+      const int r0 = excl + i * tile_m;
+      int4 tl;
+      tl.x = tid;
+      tl.y = r0;
+      tl.z = min(r0 + tile_m, excl + cnt);
+      tl.w = 0;
+      reinterpret_cast<int4*>(tiles)[texcl + i] = tl;
+    }
+    if (tid == E - 1) {
+      offsets[E] = excl + cnt;
+      *n_tiles = texcl + ntile;
+      total = excl + cnt;
+    }
+  }
+  __syncthreads();
+  for (int i = total + tid; i < P; i += 1024) sorted_pair[i] = -1;
+}
+
+__global__ __launch_bounds__(1024) void perm_scatter_kernel(const int32_t* __restrict__ ids,
+                                                            int P, int E,
+                                                            const int32_t* __restrict__ first,
+                                                            int32_t* __restrict__ sorted_pair,
+                                                            int32_t* __restrict__ pair_pos) {
+  __shared__ int wh[kPermWaves * kPermMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kPermWaves * kPermMaxE; i += 1024) wh[i] = 0;
+  __syncthreads();
+  constexpr int seg = kPermChunk / kPermWaves;
+  const int p0 = min(P, (int)blockIdx.x * kPermChunk + wave * seg), p1 = min(P, p0 + seg);
+  for (int p = p0 + lane; p < p1; p += 64) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&wh[wave * kPermMaxE + e], 1);
+  }
+  __syncthreads();
+  if (tid < E) {
+    // wave w of this workgroup starts expert tid after waves 0..w-1
+    int run = first[(size_t)blockIdx.x * E + tid];
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = wh[w * kPermMaxE + tid];
+      wh[w * kPermMaxE + tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    const bool in = p < p1;
+    const int e = in ? ids[p] : -1;
+    const bool valid = in && (unsigned)e < (unsigned)E;
+    unsigned long long m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kPermIdBits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const unsigned long long bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    if (valid) {
+      const int pos = wh[wave * kPermMaxE + e] + __popcll(m & below);
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+      if ((m >> lane) == 1ull) wh[wave * kPermMaxE + e] = pos + 1;
+    } else if (in) {
+      pair_pos[p] = -1;
+    }
+  }
+}
+
 __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t* __restrict__ ids, int P, int E, int tile_m,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -351,6 +472,24 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int tile_m,
                           int32_t* tiles, int32_t* n_tiles, hipStream_t st) {
   permute_kernel<<<1, 1024, 0, st>>>(ids, P, E, tile_m, counts, offsets,
                                      sorted_pair, pair_pos, tiles, n_tiles);
+  return hipGetLastError();
+}
+
+int permute_multi_blocks(int P) {
+  return P >= kPermMultiMinP ? (P + kPermChunk - 1) / kPermChunk : 0;
+}
+
+hipError_t launch_permute_multi(const int32_t* ids, int P, int E, int tile_m, int32_t* counts,
+                                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                int32_t* tiles, int32_t* n_tiles, int32_t* scratch,
+                                hipStream_t st) {
+  const int nb = (P + kPermChunk - 1) / kPermChunk;
+  if (nb == 0) return launch_permute(ids, P, E, tile_m, counts, offsets, sorted_pair, pair_pos,
+                                     tiles, n_tiles, st);
+  perm_hist_kernel<<<nb, 1024, 0, st>>>(ids, P, E, scratch);
+  perm_scan_kernel<<<1, 1024, 0, st>>>(P, E, nb, tile_m, scratch, counts, offsets, sorted_pair,
+                                       tiles, n_tiles);
+  perm_scatter_kernel<<<nb, 1024, 0, st>>>(ids, P, E, scratch, sorted_pair, pair_pos);
   return hipGetLastError();
 }
 

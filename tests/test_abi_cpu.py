@@ -55,13 +55,20 @@ def up256(n):
 
 def test_workspace_sizes():
     # header (error word, then the one-launch layer's 1024 barrier flags) +
-    # fp32 y rows (+ int8 x and fp32 scales for A8) (+ fp16 activation copies
-    # for the A16 matrix core path when H, I, I_shared are multiples of 128),
-    # each region 256-byte aligned
+    # fp32 y rows (+ int8 x and fp32 scales for A8) (+ per-workgroup counts
+    # of the multi-workgroup sort from 8192 pairs) (+ for the A16 matrix
+    # core path when H, I, I_shared are multiples of 128: one fp16 copy of
+    # x or h, and the fp16 h rows the gate/up epilogue writes), each region
+    # 256-byte aligned
     HDR = 256 + 1024 * 4
-    a16 = up256(max(2 * 1 * 2048 * 2, 9 * 768 * 2))
+    a16 = up256(max(1 * 2048 * 2, 9 * 768 * 2)) + up256(9 * 768 * 2)
     assert L.moe_workspace_bytes(0, 1, 2048, 768, 128, 8, 1, 768) == \
         HDR + 9 * 2048 * 4 + a16
+    # the prefill chunk: 32768 pairs over 16 sort workgroups of 2048
+    pre = L.moe_workspace_bytes(0, 4096, 4096, 1536, 256, 8, 0, 0)
+    assert pre == HDR + 32768 * 4096 * 4 + 16 * 256 * 4 + up256(max(4096 * 4096 * 2,
+                                                                    32768 * 1536 * 2)) \
+        + 32768 * 1536 * 2
     # A8: int8 x + scales, then int8 h rows (stride max(I, I_shared)) + scales
     a8 = L.moe_workspace_bytes(1, 64, 2048, 768, 128, 8, 0, 0)
     assert a8 == HDR + 64 * 2048 + 256 + 512 * 768 + 512 * 4 + 512 * 2048 * 4
@@ -71,7 +78,7 @@ def test_workspace_sizes():
     # no matrix-core copies when a dimension is not a multiple of 128
     assert L.moe_workspace_bytes(0, 4, 256, 96, 8, 2, 0, 0) == HDR + up256(8 * 256 * 4)
     # shared expert wider than the routed ones sets the h stride
-    a16 = up256(max(2 * 3 * 512 * 2, 3 * (2 + 1) * 384 * 2))
+    a16 = up256(max(3 * 512 * 2, 3 * (2 + 1) * 384 * 2)) + up256(3 * (2 + 1) * 384 * 2)
     assert L.moe_workspace_bytes(0, 3, 512, 256, 8, 2, 1, 384) == \
         HDR + up256(3 * 3 * 512 * 4) + a16
 

@@ -748,3 +748,30 @@ def test_prepacked_bank_needs_the_matrix_core_path():
                               B.sorted_pair, B.tiles, B.n_tiles, 16, B.h, B.ws, B.ws_bytes,
                               L.MOE_W_PREPACKED, check=False)
     assert st == L.MOE_E_UNSUPPORTED
+
+
+BIG_SORT = LayerConfig("mfma_big_sort", 214, T=1100, H=256, E=40, k=8, I=128, group=64,
+                       n_int2=7, group_int2=32)
+
+
+@pytest.mark.parametrize("name", ["mfma_mixed", "gated_mfma", "big_sort", "prefill"])
+def test_layer_call_matches_separate_calls_on_matrix_cores(name):
+    """moe_w4_layer on the matrix-core path (its gate/up epilogue writes the
+    fp16 h rows the down projection reads; from 8192 pairs the sort runs
+    over many workgroups with its counts in the workspace) gives the same
+    routing tables, h and output bits as the separate calls (one-workgroup
+    sort, fp16 h made by a conversion pass)."""
+    cfg = {"mfma_mixed": MFMA["mfma_mixed"], "gated_mfma": GATED["gated_mfma"],
+           "big_sort": BIG_SORT, "prefill": LAYERS["prefill_mixed_t4096"]}[name]
+    dl = _dev(cfg)
+    g1, _ = run_layer_gpu(dl, "a16", 160)
+    g2, _ = run_layer_gpu(dl, "a16", 160, fused=False)
+    for key in ("ids", "w", "counts", "offsets", "sorted_pair", "pair_pos", "tiles",
+                "n_tiles", "out", "h"):
+        assert np.array_equal(g1[key], g2[key]), key
+    assert g1["err"] == 0
+    if name == "big_sort":
+        o = oracle.oracle_layer(_layer(cfg), tile_m=160)
+        _check_integer_stages(g1, o, cfg)
+        g32, _ = run_layer_gpu(dl, "a16", 160, out_f32=True)
+        check_out(g1, g32, o["out"], "big sort")
