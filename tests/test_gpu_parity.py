@@ -775,3 +775,36 @@ def test_layer_call_matches_separate_calls_on_matrix_cores(name):
         _check_integer_stages(g1, o, cfg)
         g32, _ = run_layer_gpu(dl, "a16", 160, out_f32=True)
         check_out(g1, g32, o["out"], "big sort")
+
+
+@pytest.mark.parametrize("name", ["c1", "c3", "mixed_shared"])
+def test_cached_routing_tables_are_reused(name):
+    """Routing cache: the routing tables a step computed (ids, gate weights,
+    counts, offsets, sorted pairs, pair positions, tile list) are inputs of
+    the projection calls, so later calls over the same tokens reuse them
+    without routing again.  Routed once, then the logits are overwritten;
+    gate/up + down on the cached tables reproduce the routed step bit for
+    bit, twice, and a second bank run on the same tables matches its own
+    routed run."""
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    cfg = {"c1": LAYERS["decode_w4a16_t1"], "c3": LAYERS["decode_w4a8_t64"]}.get(name) or MINIS[name]
+    act = cfg.act
+    dl = _dev(cfg)
+    ref, B = run_layer_gpu(dl, act, 16)
+    dl.logits.fill_(float("nan"))      # the cached tables must not need the logits again
+    c = cfg
+    for rep in range(2):
+        B.h.zero_()
+        B.out.zero_()
+        L.moe_w4_gateup_silu(B.act, dl.x, c.T, c.H, c.I, c.E, c.k, dl.bank.w13, dl.bank.w13_sh,
+                             c.n_shared, c.I_shared, B.offsets, B.sorted_pair, B.tiles,
+                             B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes)
+        L.moe_w4_down_combine(B.act, B.h, c.T, c.H, c.I, c.E, c.k, dl.bank.w2, dl.bank.w2_sh,
+                              c.n_shared, c.I_shared, B.w, B.offsets, B.sorted_pair, B.pair_pos,
+                              B.tiles, B.n_tiles, B.tile_m, B.out, B.ws, B.ws_bytes)
+        torch.cuda.synchronize()
+        got = collect(B)
+        assert np.array_equal(got["out"], ref["out"]), rep
+        for key in ("ids", "sorted_pair", "pair_pos", "tiles"):
+            assert np.array_equal(got[key], ref[key]), key
