@@ -268,13 +268,14 @@ int moe_preferred_tile_m(int act, int T, int E, int k);
  *   gate_up 1 for a gate/up matrix [2I][H] (rows i and I + i are paired),
  *           0 for a down matrix [H][I]
  *   dst     device, N*K*bits/8 bytes (the same size), not overlapping codes
- * Layout of dst: blocks of 32 rows (gate/up: gate rows 16b..16b+15 then up
- * rows I+16b..I+16b+15; down: rows 32b..32b+31), per block the K/64 steps,
- * per step 64 lane slots; slot h*32 + c holds bytes [32 s + 16 h, +16) of
- * the block's row c for int4, [16 s + 8 h, +8) for int2 with every 4-byte
- * word's bytes in the order (0, 2, 1, 3).  The fp16 scales are not
- * changed: a prepacked descriptor keeps the matrix's scale array.
- * Limits: N % 32 == 0, K % 128 == 0.  Errors: MOE_E_INVAL,
+ * Layout of dst: pieces of 64 lane slots; slot h*32 + c of a piece holds
+ * bytes [32 s + 16 h, +16) of one row for int4, [16 s + 8 h, +8) for int2
+ * with every 4-byte word's bytes in the order (0, 2, 1, 3).  Down: piece
+ * (b, s) = rows 32b + c at step s, in order b, s.  Gate/up: pieces (b, s,
+ * p) in order b, s, p, p = 0 the gate rows 32b + c and p = 1 the up rows
+ * I + 32b + c.  The fp16 scales are not changed: a prepacked descriptor
+ * keeps the matrix's scale array.
+ * Limits: N % 32 == 0 (gate/up: N % 64 == 0), K % 128 == 0.  Errors: MOE_E_INVAL,
  * MOE_E_UNSUPPORTED, MOE_E_DEVICE.  Asynchronous on `stream`.
  * ------------------------------------------------------------------- */
 moe_status moe_w4_prepack(const uint8_t* codes, int bits, int N, int K, int gate_up,

@@ -620,7 +620,7 @@ extern "C" moe_status moe_w4_prepack(const uint8_t* codes, int bits, int N, int 
                                      uint8_t* dst, void* stream) {
   if (bits != 2 && bits != 4) return MOE_E_UNSUPPORTED;
   if (N <= 0 || K <= 0 || (gate_up != 0 && gate_up != 1)) return MOE_E_INVAL;
-  if (N % 32 != 0 || K % 128 != 0) return MOE_E_UNSUPPORTED;
+  if (N % (gate_up ? 64 : 32) != 0 || K % 128 != 0) return MOE_E_UNSUPPORTED;
   if ((long long)N * K * bits / 8 >= (1LL << 31)) return MOE_E_UNSUPPORTED;
   if (!codes || !dst || codes == dst) return MOE_E_INVAL;
   if (!aligned(codes, 16) || !aligned(dst, 16)) return MOE_E_INVAL;

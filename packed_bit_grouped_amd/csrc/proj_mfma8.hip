@@ -1,5 +1,5 @@
-// Grouped expert GEMMs for prefill shapes on the CDNA4 matrix cores, two
-// waves per SIMD.
+// Grouped expert GEMMs for prefill shapes on the CDNA4 matrix cores, one
+// wave per SIMD.
 //
 // Build log "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", sections "Keep
 // low-bit weights packed, do the work on the NPU" (grouped expert
@@ -10,30 +10,41 @@
 // dense contraction on v_mfma_f32_32x32x16_f16:
 //
 //  * workgroup = one tile chunk (up to 160 sorted rows of one expert) x 128
-//    gate/up units (256 weight rows) or 256 down rows; 8 waves, two per
-//    SIMD, so one wave's waits (LDS, memory, the step barrier) are covered
-//    by the other's matrix work.  Wave w owns 32 weight rows: for gate/up
-//    the gate rows of 16 units and the up rows of the same units (SiLU*mul
-//    pairs them through LDS in the epilogue), for down 32 output
-//    rows; every wave owns all of the chunk's activation rows (up to 5 x 1
-//    accumulator tiles of 32x32: 80 accumulation registers);
-//  * the K loop walks 64 K per step, four 16-K MFMA sub-steps.  A
-//    (activations, fp16, in the K order of the unpack) is staged through a
-//    double-buffered LDS tile [row][8 x 16-byte chunks], chunk c of row m at
-//    slot c ^ ((m >> 1) & 7): a 128-bit LDS access is served 16 lanes at a
-//    time, and 16 consecutive rows' chunk c then cover the 64 banks once;
-//  * weights go from HBM straight into registers (16 bytes (int4) or 8
-//    bytes (int2) per lane and step, four steps ahead) and are dequantized
-//    there: a code field OR-ed into the mantissa of an fp16 power of two
-//    reads as that power plus the field, a packed subtract gives the exact
-//    code, a packed multiply the fp16 scale (one rounding).  An int2 word's
-//    bytes are reordered (0, 2, 1, 3) first, so int2 codes unpack in the
-//    same K order as int4 and one fp16 copy of x serves both;
+//    gate/up units or 256 down rows; 4 waves, one per SIMD (512 registers:
+//    the accumulators in AGPRs).  Wave w owns 64 weight rows - the gate
+//    rows and the up rows of 32 units (SiLU*mul then pairs registers of the
+//    same lane), or 64 down rows - against all of the chunk's rows: up to
+//    2 x 5 accumulator tiles of 32x32, so every activation fragment read
+//    from LDS feeds two MFMAs;
+//  * the K loop walks 64 K per step, four 16-K MFMA sub-steps; each
+//    sub-step reads the next sub-step's activation fragments and
+//    dequantizes its weights while its own MFMAs run;
+//  * activations (fp16, in the K order of the unpack) go from memory
+//    straight into a ring of six LDS buffers [row][8 x 16-byte chunks] with
+//    buffer loads that write LDS, five steps ahead; chunk c of row m sits in
+//    slot c ^ ((m >> 1) & 7) (a 128-bit LDS access is served 16 lanes at a
+//    time, and 16 consecutive rows' chunk c then cover the 64 banks once);
+//    a load writes its 64 lanes' 16 bytes contiguously, so each lane loads
+//    the global chunk that belongs in its slot;
+//  * weights and their fp16 group scales go from memory into a register
+//    ring eight steps ahead (16 bytes (int4) or 8 bytes (int2) of codes and
+//    one scale per part, lane and step) and are dequantized in registers: a
+//    code field OR-ed into the mantissa of an fp16 power of two reads as
+//    that power plus the field, a packed subtract gives the exact code, a
+//    packed multiply the fp16 scale (one rounding).  An int2 word's bytes
+//    are reordered (0, 2, 1, 3) first, so int2 codes unpack in the same K
+//    order as int4 and one fp16 copy of x serves both;
+//  * one barrier per step, with the wait for the activation loads counted
+//    by hand (every step issues the same loads in the same order);
 //  * canonical layout: lane (row c, half h) of a 32-row block reads bytes
 //    [32 s + 16 h, +16) (int4; int2 [16 s + 8 h, +8)) of its row at step s;
 //    prepacked layout (moe_w4_prepack): those 16 (8) bytes of the 64 lanes
-//    stored contiguously per block and step, so a wave's step is one 1 KB
-//    (512 B) coalesced load, with the int2 byte order applied once;
+//    stored contiguously per block and step (gate/up: the gate block of 32
+//    units, then the up block of the same units), so each of a wave's loads
+//    is one 1 KB (512 B) coalesced piece, with the int2 byte order applied
+//    once;
+//  * the results leave through the wave's part of the idle activation ring
+//    as 16-byte stores;
 //  * workgroups of one tile land on one XCD (blockIdx mod 8 picks the
 //    XCD), so the tile's activation rows are shared in that XCD's L2.
 #include "moe_internal.h"
@@ -48,13 +59,16 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 512;       // 8 waves, two per SIMD
+constexpr int kThreads = 256;       // 4 waves, one per SIMD
 constexpr int kUnits = 128;         // gate/up units per workgroup (shared-expert tile rows too)
 constexpr int kRowsMax = 160;       // activation rows per tile chunk (5 row blocks of 32)
-constexpr int kRing = 4;            // steps in flight
+constexpr int kRing = 8;            // weight steps in flight (registers)
 constexpr int kKS = 64;             // K per step
 constexpr int kChunks = kKS / 8;    // 16-byte fp16 chunks per row and step
 constexpr int kXcd = 8;
+constexpr int kAD = 5;              // activation steps in flight (LDS)
+constexpr int kABufs = 6;           // LDS activation buffers (> kAD)
+constexpr int kABuf = kChunks * kRowsMax;   // 16-byte slots per buffer
 
 __device__ __forceinline__ f16x2_v as_h2(uint32_t v) { return __builtin_bit_cast(f16x2_v, v); }
 
@@ -123,185 +137,316 @@ struct Tile {
   bool is_sh;
 };
 
-// This lane's weight row, its code buffer descriptor and its scales in LDS.
+// This lane's two weight rows (parts p = 0, 1: the gate and up rows of one
+// unit, or two down rows 32 apart), their code and scale offsets.
 struct Lane {
-  __amdgpu_buffer_rsrc_t crs;
-  int coff;                // byte offset of step 0 (+ step * stride)
-  int cstride;             // bytes per step
-  const uint16_t* sc;      // LDS: this lane's row of group scales
-  int wrow;                // weight row (gate/up: unit of the lane's column)
-  bool wval;
+  __amdgpu_buffer_rsrc_t crs, srs;
+  int coff[2];             // code byte offset of step 0 (+ step * cstride)
+  int cstride;             // code bytes per step
+  int soff[2];             // scale byte offset of the row's group 0
+  int wrow[2];             // output column (gate/up: the unit; down: the row)
+  bool wval[2];
   int n_st, gsh;
 };
 
+// SiLU(g) * u with the hardware exp2 and reciprocal (relative error a few
+// fp32 units; the result is rounded to bf16)
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// Eight bf16 values (units 8q..8q+7) as fp16 in the unpack order of an
+// 8-block, (0,4)(1,5)(2,6)(3,7) (exact in fp16's normal range)
+__device__ __forceinline__ u32x4_v bf16x8_to_f16_unpack(u32x4_v v) {
+  const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                         v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+  u32x4_v r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(e[0] << 16),
+                                                               __uint_as_float(e[4] << 16)));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(e[1] << 16),
+                                                               __uint_as_float(e[5] << 16)));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(e[2] << 16),
+                                                               __uint_as_float(e[6] << 16)));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(e[3] << 16),
+                                                               __uint_as_float(e[7] << 16)));
+  return r;
+}
+
+// One step of this lane's weights: codes of both parts and their scales.
 template <int BITS>
 struct BReg {
-  uint32_t c[BITS];        // 16 (int4) or 8 (int2) bytes
+  uint32_t c[2][BITS];     // per part 16 (int4) or 8 (int2) bytes
+  uint32_t s[2];           // fp16 scale bits
 };
 
-template <int MB>
-struct AReg {
-  u32x4_v a[(MB * 32 * kChunks + kThreads - 1) / kThreads];
-};
+// Wait until at most N vector-memory operations of this wave are in flight
+// and every LDS access has completed, then the workgroup barrier.  The
+// scheduling fences keep the compiler from moving any instruction across
+// it, so the count of loads issued after a given one is the program's.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));   // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
-// K loop and epilogue of one chunk of up to 32 * MB rows (tok[] holds
-// their activation rows).  Straight-line loop body, every load
+// K loop and epilogue of one chunk of up to 32 * MBT rows (tok[] holds
+// their activation rows): the wave's 64 weight rows against all of them.
+// Per step every wave issues the same loads in the same order (MBT
+// activation loads into LDS, two code loads, two scale loads), every load
 // unconditional (steps past the end re-read the last step with a zero
-// scale), so the wait counts stay graded.
-template <int MODE, int BITS, int MB, bool PP>
+// scale), so the number of loads issued after any given one is fixed.
+template <int MODE, int BITS, int MBT, bool PP>
 __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const Lane& ln_,
-                                      u32x4_v* As, const int* tok, int mc, int nrows) {
+                                      u32x4_v* As, int* tok, int mc, int nrows) {
   const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lc = lane & 31, kh = lane >> 5;
   const int n_st = ln_.n_st;
-  constexpr int kAN = (MB * 32 * kChunks + kThreads - 1) / kThreads;   // A chunks per thread
-  constexpr int kAChunks = MB * 32 * kChunks;
 
   auto load_b = [&](int st, BReg<BITS>& b) {
     st = min(st, n_st - 1);
-    if constexpr (BITS == 4) {
-      const u32x4_v v =
-          __builtin_amdgcn_raw_buffer_load_b128(ln_.crs, ln_.coff, st * ln_.cstride, 0);
-      b.c[0] = v.x; b.c[1] = v.y; b.c[2] = v.z; b.c[3] = v.w;
-    } else {
-      const u32x2_v v =
-          __builtin_amdgcn_raw_buffer_load_b64(ln_.crs, ln_.coff, st * ln_.cstride, 0);
-      b.c[0] = PP ? v.x : int2_order(v.x);
-      b.c[1] = PP ? v.y : int2_order(v.y);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if constexpr (BITS == 4) {
+        const u32x4_v v =
+            __builtin_amdgcn_raw_buffer_load_b128(ln_.crs, ln_.coff[p], st * ln_.cstride, 0);
+        b.c[p][0] = v.x; b.c[p][1] = v.y; b.c[p][2] = v.z; b.c[p][3] = v.w;
+      } else {
+        const u32x2_v v =
+            __builtin_amdgcn_raw_buffer_load_b64(ln_.crs, ln_.coff[p], st * ln_.cstride, 0);
+        b.c[p][0] = PP ? v.x : int2_order(v.x);
+        b.c[p][1] = PP ? v.y : int2_order(v.y);
+      }
+    }
+    const int gi = (st * kKS + kh * 32) >> ln_.gsh;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      b.s[p] = __builtin_amdgcn_raw_buffer_load_b16(ln_.srs, ln_.soff[p] + gi * 2, 0, 0);
     }
   };
-  // A staging: chunk q = tid + kThreads * i (row q >> 3, chunk q & 7); a
-  // thread past the chunk count re-reads a valid chunk and stores nothing
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(t.asrc, t.a_bytes);
-  int aoff[kAN], adst[kAN];
-#pragma unroll
-  for (int i = 0; i < kAN; ++i) {
-    const int q = tid + kThreads * i;
-    const int qq = q < kAChunks ? q : tid;
-    const int m = qq >> 3, ci = qq & 7;
-    aoff[i] = tok[m] * a.ld_in * 2 + ci * 16;
-    adst[i] = q < kAChunks ? m * kChunks + (ci ^ ((m >> 1) & 7)) : -1;
+  // the weight ring is issued first (it needs only the descriptor), then
+  // the chunk's activation rows are read and published in LDS
+  constexpr int kStepLoads = MBT + 4;
+  // loads issued after A(s + 2), counted without its own step's weight
+  // loads (the compiler may order those before or after it): kAD - 2 steps
+  constexpr int kWaitSteady = (kAD - 2) * kStepLoads;
+  constexpr int kWaitFirst = (kAD - 2) * MBT;   // prologue: A(1) done (weights were issued before)
+  // the chunk's activation rows (a load that needs only the tile), then
+  // the weight ring (it needs the descriptor), then the rows are published
+  int r = 0;
+  if (tid < kRowsMax) {
+    const int mm = tid < nrows ? tid : 0;   // padding rows re-read row 0 (discarded)
+    if (MODE == 0) r = t.is_sh ? mc + mm : a.sorted_pair[mc + mm];
+    else r = t.is_sh ? a.P + t.e * a.T + mc + mm : mc + mm;
   }
-  auto load_a = [&](int st, AReg<MB>& ar) {
+  BReg<BITS> b0, b1, b2, b3, b4, b5, b6, b7;
+  load_b(0, b0); load_b(1, b1); load_b(2, b2); load_b(3, b3);
+  load_b(4, b4); load_b(5, b5); load_b(6, b6); load_b(7, b7);
+  __syncthreads();   // previous chunk's readers of tok are done
+  if (tid < kRowsMax) tok[tid] = (MODE == 0 && !t.is_sh) ? r / a.k : r;
+  __syncthreads();
+  // activations: piece q = (wave * MBT + i) * 64 + lane of a step (row q >>
+  // 3, LDS slot q & 7) holds global chunk (q & 7) ^ ((row >> 1) & 7) of the
+  // row; a load writes its 64 lanes' 16 bytes contiguously from its LDS base
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(t.asrc, t.a_bytes);
+  int aoff[MBT];
+#pragma unroll
+  for (int i = 0; i < MBT; ++i) {
+    const int q = (wave * MBT + i) * 64 + lane;
+    const int m = q >> 3;
+    aoff[i] = tok[m] * a.ld_in * 2 + (((q & 7) ^ ((m >> 1) & 7)) * 16);
+  }
+  auto dma_a = [&](int st, int buf) {
     const int o = min(st, n_st - 1) * (kKS * 2);
 #pragma unroll
-    for (int i = 0; i < kAN; ++i) ar.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ars, aoff[i], o, 0);
-  };
-  auto store_a = [&](int buf, const AReg<MB>& ar) {
-    u32x4_v* d = As + buf * kChunks * kRowsMax;
-#pragma unroll
-    for (int i = 0; i < kAN; ++i)
-      if (adst[i] >= 0) d[adst[i]] = ar.a[i];
+    for (int i = 0; i < MBT; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ars, (__attribute__((address_space(3))) void*)(As + buf * kABuf + (wave * MBT + i) * 64),
+          16, aoff[i], o, 0, 0);
   };
 
-  f32x16_v acc[MB];
+  f32x16_v acc[2][MBT];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[mb][j] = 0.0f;
+    for (int mb = 0; mb < MBT; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[p][mb][j] = 0.0f;
 
-  // fragment read offsets (16-byte units) of this lane's rows 32 mb + lc
+  // fragment of row tile mb, 16-K sub-step ks, from LDS buffer buf: lane
+  // (lc, kh) reads row 32 mb + lc, chunk kh * 4 + ks
   const int rsw = (lc >> 1) & 7;
-  auto compute = [&](int buf, const BReg<BITS>& b, int stg) {
-    const bool live = stg < n_st;
-    const int gi = (min(stg, n_st - 1) * kKS + kh * 32) >> ln_.gsh;
-    const uint32_t m16 = live ? 0x10001u : 0u;
-    const f16x2_v s2 = as_h2((uint32_t)ln_.sc[gi] * m16);
-    const u32x4_v* Ab = As + buf * kChunks * kRowsMax + lc * kChunks;
+  auto read_frags = [&](int buf, int ks, f16x8_v* f) {
+    const u32x4_v* Ab = As + buf * kABuf + lc * kChunks + ((kh * 4 + ks) ^ rsw);
+#pragma unroll
+    for (int mb = 0; mb < MBT; ++mb) f[mb] = __builtin_bit_cast(f16x8_v, Ab[32 * kChunks * mb]);
+  };
+  // steps past the last one (the loop runs whole rings) get a zero scale
+  auto deq = [&](const BReg<BITS>& b, int ks, int stg, f16x8_v* bq) {
+    const uint32_t m16 = stg < n_st ? 0x10001u : 0u;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const f16x2_v s2 = as_h2(b.s[p] * m16);
+      if constexpr (BITS == 4) bq[p] = deq_int4(b.c[p][ks], s2);
+      else if ((ks & 1) == 0) bq[p] = deq_int2<0>(b.c[p][ks >> 1], s2);
+      else bq[p] = deq_int2<1>(b.c[p][ks >> 1], s2);
+    }
+  };
+  f16x8_v fr[2][MBT];
+  f16x8_v bq[2][2];
+  // one 64-K step from LDS buffer buf with the weights of b; sub-step ks
+  // reads the fragments of ks + 1 and dequantizes its weights while its own
+  // MFMAs run; the last sub-step does so for the first sub-step of the next
+  // step (buffer nbuf, weights bn)
+  // Sub-step 1 also issues the activation loads of step dst into LDS
+  // buffer dbuf, sub-step 3 the weight and scale loads of step stg + kRing
+  // into b (its codes are last read by sub-step 2); the loads are spread
+  // between the MFMAs.  Sub-steps end with scheduling fences, so the order
+  // of the loads (activations, then weights and scales) is the same in
+  // every step.
+  auto step = [&](int buf, int nbuf, BReg<BITS>& b, const BReg<BITS>& bn, int stg, int dst,
+                  int dbuf) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      f16x8_v bf;
-      if constexpr (BITS == 4) {
-        bf = deq_int4(b.c[ks], s2);
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks < 3) {
+        read_frags(buf, ks + 1, fr[nxt]);
+        deq(b, ks + 1, stg, bq[nxt]);
       } else {
-        if ((ks & 1) == 0) bf = deq_int2<0>(b.c[ks >> 1], s2);
-        else bf = deq_int2<1>(b.c[ks >> 1], s2);
+        read_frags(nbuf, 0, fr[nxt]);
+        deq(bn, 0, stg + 1, bq[nxt]);
       }
+      if (ks == 1) dma_a(dst, dbuf);
+      if (ks == 3) load_b(stg + kRing, b);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const f16x8_v av =
-            __builtin_bit_cast(f16x8_v, Ab[32 * kChunks * mb + ((kh * 4 + ks) ^ rsw)]);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bf, acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < MBT; ++mb) {
+        acc[0][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[cur][mb], bq[cur][0], acc[0][mb], 0, 0, 0);
+        acc[1][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[cur][mb], bq[cur][1], acc[1][mb], 0, 0, 0);
       }
+      // issue order: the LDS reads, then the MFMAs with the loads (one per
+      // MFMA) and the dequantization between them
+      const int kLd = ks == 1 ? MBT : ks == 3 ? 4 : 0;
+      __builtin_amdgcn_sched_group_barrier(0x100, MBT, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * MBT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < kLd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // weights kRing steps ahead in a register ring; activations two steps
-  // ahead in two register slots (A of step k lives in slot k & 1): step s
-  // computes from LDS buffer s & 1, writes A(s + 1) into the other buffer,
-  // refills that slot with A(s + 3) and the weight slot with step s + 4
-  AReg<MB> ar0, ar1;
-  BReg<BITS> b0, b1, b2, b3;
-  load_a(0, ar0); load_b(0, b0);
-  load_a(1, ar1); load_b(1, b1);
-  load_b(2, b2);
-  load_b(3, b3);
-  store_a(0, ar0);
-  load_a(2, ar0);
-  __syncthreads();
-#define MOE8_STEP(J, AS, BC)                        \
-  compute(J & 1, BC, base + J);                     \
-  store_a((J + 1) & 1, AS);                         \
-  load_a(base + J + 3, AS);                         \
-  load_b(base + J + kRing, BC);                     \
-  __syncthreads();
+  // Activations kAD steps ahead in a ring of kABufs LDS buffers (step s in
+  // buffer s % kABufs); weights and scales kRing steps ahead in registers.
+  // Step s computes, loads A(s + kAD) into the buffer step s - 1 read, and
+  // B(s + kRing) into the register slot it consumed; the barrier that ends
+  // it waits for A(s + 2), whose first fragments step s + 1 reads early.
+  // Loads issued after A(s + 2): 4 of its own step and kAD - 2 full steps.
+#pragma unroll
+  for (int j = 0; j < kAD; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(j, j);
+  }
+  vm_barrier<kWaitFirst>();
+  read_frags(0, 0, fr[0]);
+  deq(b0, 0, 0, bq[0]);
+  int buf = 0;
+#define MOE8_STEP(J, BC, BN)                                  \
+  {                                                           \
+    const int nb = buf == kABufs - 1 ? 0 : buf + 1;           \
+    const int db = buf + kAD >= kABufs ? buf + kAD - kABufs : buf + kAD; \
+    step(buf, nb, BC, BN, base + J, base + J + kAD, db);      \
+    vm_barrier<kWaitSteady>();                                \
+    buf = nb;                                                 \
+  }
   for (int base = 0; base < n_st; base += kRing) {
-    MOE8_STEP(0, ar1, b0)
-    MOE8_STEP(1, ar0, b1)
-    MOE8_STEP(2, ar1, b2)
-    MOE8_STEP(3, ar0, b3)
+    MOE8_STEP(0, b0, b1)
+    MOE8_STEP(1, b1, b2)
+    MOE8_STEP(2, b2, b3)
+    MOE8_STEP(3, b3, b4)
+    MOE8_STEP(4, b4, b5)
+    MOE8_STEP(5, b5, b6)
+    MOE8_STEP(6, b6, b7)
+    MOE8_STEP(7, b7, b0)
   }
 #undef MOE8_STEP
+  // the loads still in flight (past the last step) land before the LDS is
+  // reused
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- epilogue: lane holds column lc (rows 32 mb + 8 (j >> 2) + 4 kh + (j & 3))
+  // ---- epilogue: lane holds column lc of both parts (rows 32 mb + 8 (j >>
+  // 2) + 4 kh + (j & 3)); gate/up: part 0 is the gate, part 1 the up of the
+  // same unit, so SiLU(g) * u needs no exchange.  The wave's results pass
+  // through its own part of the (now idle) activation ring, so the global
+  // stores are 16 bytes per lane.
   const int orow0 = t.is_sh ? a.P + t.e * a.T + mc : mc;
-  // gate/up: the gate of a unit sits in column c < 16, its up in column
-  // c + 16 (lane + 16); the pairs meet through this wave's own 4 KB of the
-  // A tile, free once every wave has passed the K loop's last barrier.
-  // Lane L reads what lane L ^ 16 wrote, which the compiler cannot see as
-  // a dependence: barriers order the writes, the reads and the next writes.
-  float* xch = reinterpret_cast<float*>(As) + (threadIdx.x >> 6) * (16 * 64);
+  __syncthreads();   // every wave is past its last read of the ring
+  if (MODE == 0) {
+    // h tile [rows][32 units] bf16, row stride 80 bytes (rows 4 apart land
+    // on different banks)
+    constexpr int kRowB = 80;
+    unsigned char* stg = reinterpret_cast<unsigned char*>(As) + wave * (kRowsMax * kRowB);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    if (MODE == 0) {
-      if (mb > 0) __syncthreads();   // the previous row block's reads are done
+    for (int mb = 0; mb < MBT; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) xch[j * 64 + lane] = acc[mb][j];
-      __syncthreads();
+      for (int j = 0; j < 16; ++j) {
+        const int m = 32 * mb + (j >> 2) * 8 + kh * 4 + (j & 3);
+        const float hv = silu_mul_fast(acc[0][mb][j], acc[1][mb][j]);
+        *reinterpret_cast<uint16_t*>(stg + m * kRowB + lc * 2) = (uint16_t)f32_to_bf16(hv);
+      }
+    __syncthreads();   // lanes read what other lanes wrote
+    const int q = lane & 3;
+    const int u = ln_.wrow[0] - lc + 8 * q;   // first unit of the lane's 16 bytes
+#pragma unroll
+    for (int i = 0; i < (MBT * 32 + 15) / 16; ++i) {
+      const int m = 16 * i + (lane >> 2);
+      const u32x4_v v = *reinterpret_cast<const u32x4_v*>(stg + m * kRowB + q * 16);
+      if (m < nrows && ln_.wval[0]) {
+        const size_t o = (size_t)(orow0 + m) * a.ld_out + u;
+        *reinterpret_cast<u32x4_v*>(static_cast<uint16_t*>(a.out) + o) = v;
+        if (a.out16) *reinterpret_cast<u32x4_v*>(a.out16 + o) = bf16x8_to_f16_unpack(v);
+      }
     }
+  } else {
+    // y tile of one part [rows][32] fp32, row stride 160 bytes
+    constexpr int kRowB = 160;
+    unsigned char* stg = reinterpret_cast<unsigned char*>(As) + wave * (kRowsMax * kRowB);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int m = 32 * mb + (j >> 2) * 8 + kh * 4 + (j & 3);
-      if (MODE == 0) {
-        const float up = xch[j * 64 + (lane ^ 16)];
-        if (lc < 16 && m < nrows && ln_.wval) {
-          const float hv = silu_mul(acc[mb][j], up);
-          const uint32_t hb = f32_to_bf16(hv);
-          const size_t o = (size_t)(orow0 + m) * a.ld_out;
-          static_cast<uint16_t*>(a.out)[o + ln_.wrow] = (uint16_t)hb;
-          if (a.out16) {
-            // the down projection's fp16 input: the bf16 value (exact in
-            // fp16's normal range) at its place in the unpack order of its
-            // 8-block, (0,4)(1,5)(2,6)(3,7)
-            const int u = ln_.wrow;
-            const int pos = (u & ~7) | ((u & 3) << 1) | ((u >> 2) & 1);
-            const uint32_t f16 = __builtin_bit_cast(
-                uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(hb << 16), 0.0f));
-            a.out16[o + pos] = (uint16_t)(f16 & 0xFFFFu);
-          }
+    for (int p = 0; p < 2; ++p) {
+      if (p > 0) __syncthreads();   // the previous part's reads are done
+#pragma unroll
+      for (int mb = 0; mb < MBT; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int m = 32 * mb + (j >> 2) * 8 + kh * 4 + (j & 3);
+          *reinterpret_cast<float*>(stg + m * kRowB + lc * 4) = acc[p][mb][j];
         }
-      } else {
-        if (m < nrows && ln_.wval)
-          static_cast<float*>(a.out)[(size_t)(orow0 + m) * a.ld_out + ln_.wrow] = acc[mb][j];
+      __syncthreads();   // lanes read what other lanes wrote
+      const int q = lane & 7;
+      const int col = ln_.wrow[p] - lc + 4 * q;
+#pragma unroll
+      for (int i = 0; i < (MBT * 32 + 7) / 8; ++i) {
+        const int m = 8 * i + (lane >> 3);
+        const u32x4_v v = *reinterpret_cast<const u32x4_v*>(stg + m * kRowB + q * 16);
+        if (m < nrows && ln_.wval[p])
+          *reinterpret_cast<u32x4_v*>(static_cast<float*>(a.out) +
+                                      (size_t)(orow0 + m) * a.ld_out + col) = v;
       }
     }
   }
 }
 
 template <int MODE, int BITS, bool PP>
-__device__ __forceinline__ void tile(const ProjArgs& a, const Tile& t, u32x4_v* As, int* tok,
-                                     uint16_t* ssc) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void tile(const ProjArgs& a, const Tile& t, u32x4_v* As, int* tok) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = __builtin_amdgcn_readfirstlane(tid >> 6);   // weight block of the wave
   const int lc = lane & 31, kh = lane >> 5;
   const int K = t.K, U = t.U;
   const int ng = K / t.group;
@@ -310,78 +455,69 @@ __device__ __forceinline__ void tile(const ProjArgs& a, const Tile& t, u32x4_v* 
 
   Lane L;
   L.n_st = K / kKS;
-  int brow, lrow;   // this lane's weight row and its row in the staged scales
+  int brow[2];   // this lane's weight rows
   if (MODE == 0) {
-    const int unit = t.u0 + 16 * wave + (lc & 15);
-    L.wval = unit < U;
-    L.wrow = unit;
-    brow = lc < 16 ? unit : U + unit;
-    lrow = (lc < 16 ? 0 : kUnits) + 16 * wave + (lc & 15);
+    const int unit = t.u0 + 32 * n + lc;
+    L.wval[0] = L.wval[1] = unit < U;
+    L.wrow[0] = L.wrow[1] = unit;
+    brow[0] = unit;
+    brow[1] = U + unit;
   } else {
-    const int r = t.u0 + 32 * wave + lc;
-    L.wval = r < U;
-    L.wrow = r;
-    brow = r;
-    lrow = 32 * wave + lc;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = t.u0 + 64 * n + 32 * p + lc;
+      L.wval[p] = r < U;
+      L.wrow[p] = r;
+      brow[p] = r;
+    }
   }
   L.crs = make_rsrc(t.codes, (uint32_t)((size_t)n_wrows * row_bytes));
+  L.srs = make_rsrc(t.scales, (uint32_t)((size_t)n_wrows * ng * 2));
+#pragma unroll
+  for (int p = 0; p < 2; ++p) L.soff[p] = (L.wval[p] ? brow[p] : 0) * ng * 2;
   constexpr int kLaneBytes = kKS * BITS / 16;   // per lane half and step
   if (PP) {
-    // block of 32 weight rows: gate/up block (u0 + 16 wave) / 16 pairs 16
-    // gate and 16 up rows, down block (u0 + 32 wave) / 32
-    const int blk = MODE == 0 ? t.u0 / 16 + wave : t.u0 / 32 + wave;
-    L.cstride = 64 * kLaneBytes;
-    L.coff = L.wval ? blk * L.n_st * L.cstride + lane * kLaneBytes : 0;
+    // gate/up: [unit block of 32][step][gate, up][64 lane slots]; down:
+    // [row block of 32][step][64 lane slots]
+    if (MODE == 0) {
+      const int blk = t.u0 / 32 + n;
+      L.cstride = 2 * 64 * kLaneBytes;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        L.coff[p] = L.wval[p] ? blk * L.n_st * L.cstride + p * 64 * kLaneBytes + lane * kLaneBytes
+                              : 0;
+    } else {
+      L.cstride = 64 * kLaneBytes;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int blk = (t.u0 + 64 * n) / 32 + p;
+        L.coff[p] = L.wval[p] ? blk * L.n_st * L.cstride + lane * kLaneBytes : 0;
+      }
+    }
   } else {
     L.cstride = kKS * BITS / 8;
-    L.coff = (L.wval ? brow : 0) * row_bytes + kh * kLaneBytes;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) L.coff[p] = (L.wval[p] ? brow[p] : 0) * row_bytes + kh * kLaneBytes;
   }
   L.gsh = 31 - __builtin_clz(t.group);
 
-  // ---- the group scales of the workgroup's weight rows into LDS, [local
-  // row][group]: gate rows u0.. then up rows U+u0.. (gate/up), or down
-  // rows u0..; contiguous runs of the scale matrix copied in 16-byte words
-  // (runs start at multiples of 128 rows, so they are 16-byte aligned).
-  {
-    const __amdgpu_buffer_rsrc_t srs = make_rsrc(t.scales, (uint32_t)(n_wrows * ng * 2));
-    const int run_rows = MODE == 0 ? kUnits : min(2 * kUnits, U - t.u0);
-    const int run_words = run_rows * ng * 2 / 16;
-    const int n_runs = MODE == 0 ? 2 : 1;
-    for (int q = tid; q < n_runs * run_words; q += kThreads) {
-      const int run = q >= run_words, qq = q - run * run_words;
-      const int row0 = run ? U + t.u0 : t.u0;
-      const u32x4_v v =
-          __builtin_amdgcn_raw_buffer_load_b128(srs, row0 * ng * 2 + qq * 16, 0, 0);
-      reinterpret_cast<u32x4_v*>(ssc + (size_t)run * kUnits * ng)[qq] = v;
-    }
-  }
-  L.sc = ssc + lrow * ng;
-
   for (int mc = t.r_begin; mc < t.r_end; mc += kRowsMax) {
     const int nrows = min(kRowsMax, t.r_end - mc);
-    __syncthreads();   // previous chunk's readers of tok / As are done
-    if (tid < kRowsMax) {
-      const int mm = tid < nrows ? tid : 0;   // padding rows re-read row 0 (discarded)
-      int r;
-      if (MODE == 0) r = t.is_sh ? mc + mm : a.sorted_pair[mc + mm] / a.k;
-      else r = t.is_sh ? a.P + t.e * a.T + mc + mm : mc + mm;
-      tok[tid] = r;
-    }
-    __syncthreads();
-    if (nrows > 128) chunk<MODE, BITS, 5, PP>(a, t, L, As, tok, mc, nrows);
-    else if (nrows > 64) chunk<MODE, BITS, 4, PP>(a, t, L, As, tok, mc, nrows);
-    else if (nrows > 32) chunk<MODE, BITS, 2, PP>(a, t, L, As, tok, mc, nrows);
+    const int mbt = (nrows + 31) >> 5;
+    if (mbt == 5) chunk<MODE, BITS, 5, PP>(a, t, L, As, tok, mc, nrows);
+    else if (mbt == 4) chunk<MODE, BITS, 4, PP>(a, t, L, As, tok, mc, nrows);
+    else if (mbt == 3) chunk<MODE, BITS, 3, PP>(a, t, L, As, tok, mc, nrows);
+    else if (mbt == 2) chunk<MODE, BITS, 2, PP>(a, t, L, As, tok, mc, nrows);
     else chunk<MODE, BITS, 1, PP>(a, t, L, As, tok, mc, nrows);
   }
 }
 
 template <int MODE, bool PP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void proj_mfma8_kernel(ProjArgs a, const uint16_t* x16) {
   extern __shared__ __align__(16) unsigned char smem[];
-  u32x4_v* As = reinterpret_cast<u32x4_v*>(smem);                        // [2][kRowsMax][kChunks]
-  int* tok = reinterpret_cast<int*>(smem + 2 * kChunks * kRowsMax * 16);  // [kRowsMax]
-  uint16_t* ssc = reinterpret_cast<uint16_t*>(tok + kRowsMax);             // [256][K / group]
+  u32x4_v* As = reinterpret_cast<u32x4_v*>(smem);                         // [kABufs][kRowsMax][kChunks]
+  int* tok = reinterpret_cast<int*>(smem + kABufs * kABuf * 16);           // [kRowsMax]
   const int tid = threadIdx.x;
 
   // block -> (tile slot, unit block): XCD b mod 8 takes a contiguous range
@@ -433,8 +569,8 @@ void proj_mfma8_kernel(ProjArgs a, const uint16_t* x16) {
   // rows the activation source holds: T token rows, or every h row
   t.a_bytes = (uint32_t)((size_t)(MODE == 0 ? a.T : a.P + a.n_shared * a.T) * a.ld_in * 2);
   t.asrc = MODE == 0 ? x16 : a.in_bf16;
-  if (q.bits == 4) tile<MODE, 4, PP>(a, t, As, tok, ssc);
-  else tile<MODE, 2, PP>(a, t, As, tok, ssc);
+  if (q.bits == 4) tile<MODE, 4, PP>(a, t, As, tok);
+  else tile<MODE, 2, PP>(a, t, As, tok);
 }
 
 // fp16 copy of bf16 rows, every 8-block in the order (0,4)(1,5)(2,6)(3,7)
@@ -496,9 +632,7 @@ hipError_t launch_proj_mfma8(const ProjArgs& a_in, uint16_t* a16, bool prepacked
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int Kmax = a.K_sh > a.K ? a.K_sh : a.K;
-  const size_t lds = (size_t)2 * kChunks * kRowsMax * 16 + kRowsMax * sizeof(int) +
-                     (size_t)2 * kUnits * (Kmax / 32) * 2;
+  const size_t lds = (size_t)kABufs * kABuf * 16 + kRowsMax * sizeof(int);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const dim3 g((unsigned)blocks), blk(kThreads);
   if (a.mode == 0) {
@@ -517,11 +651,12 @@ namespace moe {
 namespace {
 
 // One 16-byte (int4) or 8-byte (int2) unit of the prepacked layout per
-// thread: unit u = (block, step, lane); lane = half * 32 + column; the
-// column's row is 16 gate rows then the same 16 up rows (gate_up) or 32
-// consecutive rows; the unit holds bytes [step * 32 + half * 16, +16) of
-// that row (int2: [step * 16 + half * 8, +8), each 4-byte word's bytes
-// reordered (0, 2, 1, 3)).
+// thread.  gate_up: u = ((block * n_st + step) * 2 + part) * 64 + lane, the
+// row of lane (half * 32 + column) being gate row 32 block + column (part
+// 0) or up row N / 2 + 32 block + column (part 1); down: u = (block * n_st
+// + step) * 64 + lane, row 32 block + column.  The unit holds bytes
+// [step * 32 + half * 16, +16) of that row (int2: [step * 16 + half * 8,
+// +8), each 4-byte word's bytes reordered (0, 2, 1, 3)).
 __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict__ src, int bits,
                                                       int N, int K, int gate_up,
                                                       uint8_t* __restrict__ dst) {
@@ -530,11 +665,13 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
   const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
   if (u >= units) return;
   const int lane = (int)(u & 63);
-  const long long bs = u >> 6;
+  long long bs = u >> 6;
+  const int part = gate_up ? (int)(bs & 1) : 0;
+  if (gate_up) bs >>= 1;
   const int st = (int)(bs % n_st);
   const int blk = (int)(bs / n_st);
   const int c = lane & 31, half = lane >> 5;
-  const int row = gate_up ? (c < 16 ? 16 * blk + c : N / 2 + 16 * blk + c - 16) : 32 * blk + c;
+  const int row = (part ? N / 2 : 0) + 32 * blk + c;
   const size_t row_bytes = (size_t)K * bits / 8;
   if (bits == 4) {
     const uint4 v = *reinterpret_cast<const uint4*>(src + row * row_bytes + st * 32 + half * 16);

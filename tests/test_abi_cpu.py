@@ -304,6 +304,8 @@ def test_prepack_validation():
         return L.moe_w4_prepack(*a.values(), stream=0, check=False)
     assert call(bits=3) == L.MOE_E_UNSUPPORTED
     assert call(N=48) == L.MOE_E_UNSUPPORTED       # blocks of 32 rows
+    assert call(N=96) == L.MOE_E_UNSUPPORTED       # gate/up: blocks of 32 units
+    assert call(N=96, gate_up=0) == L.MOE_E_DEVICE
     assert call(K=64) == L.MOE_E_UNSUPPORTED       # K % 128
     assert call(gate_up=2) == L.MOE_E_INVAL
     assert call(dst=FAKE) == L.MOE_E_INVAL         # in place
