@@ -198,8 +198,9 @@ def run_config(cid, args, torch, L, hi, ceiling):
     layer = make_layer(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
     dl = DeviceLayer.from_synth(layer, "cuda:0")
-    if args.prepacked and not decode:
-        # codes re-tiled into the matrix-core layout (moe_w4_prepack)
+    if not args.canonical_weights and not decode and args.path != "gemv":
+        # the served form of the prefill bank: codes re-tiled once, at load
+        # time, into the matrix-core layout (moe_w4_prepack)
         dl.bank = dl.bank.prepack()
         torch.cuda.synchronize()
     act = cfg.act
@@ -365,8 +366,9 @@ def main():
     ap.add_argument("--cpu-prefill-experts", type=int, default=12,
                     help="experts of the prefill layer in the CPU oracle's sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prepacked", action="store_true",
-                    help="prefill: run on a bank re-tiled by moe_w4_prepack")
+    ap.add_argument("--canonical-weights", action="store_true",
+                    help="prefill: run on the canonical code layout instead of the bank "
+                         "re-tiled by moe_w4_prepack")
     ap.add_argument("--path", choices=["auto", "gemv", "mfma"], default="auto")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="after the run, one device copy of MB MiB (a plain copy kernel of "

@@ -233,10 +233,16 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
   // the weight ring is issued first (it needs only the descriptor), then
   // the chunk's activation rows are read and published in LDS
   constexpr int kStepLoads = MBT + 4;
-  // loads issued after A(s + 2), counted without its own step's weight
-  // loads (the compiler may order those before or after it): kAD - 2 steps
+  // Loads issued after A(s + 2) by the end of step s: from step 3 on, the
+  // weight and scale loads of its own step and three whole steps (at least
+  // (kAD - 2) whole steps, counted without the former); in steps 0 and 1,
+  // whose A(s + 2) the prologue issued (after the weight ring), the
+  // prologue's later activation loads and the steps so far:
+  // (kAD - 2) * MBT + 4 (s + 1).  The prologue's barrier waits for A(1):
+  // A(2) .. A(kAD - 1) come after it.
   constexpr int kWaitSteady = (kAD - 2) * kStepLoads;
-  constexpr int kWaitFirst = (kAD - 2) * MBT;   // prologue: A(1) done (weights were issued before)
+  constexpr int kWaitFirst = (kAD - 2) * MBT;
+  static_assert(kAD == 5, "the early-step counts below assume five steps ahead");
   // the chunk's activation rows (a load that needs only the tile), then
   // the weight ring (it needs the descriptor), then the rows are published
   int r = 0;
@@ -347,8 +353,8 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
   // buffer s % kABufs); weights and scales kRing steps ahead in registers.
   // Step s computes, loads A(s + kAD) into the buffer step s - 1 read, and
   // B(s + kRing) into the register slot it consumed; the barrier that ends
-  // it waits for A(s + 2), whose first fragments step s + 1 reads early.
-  // Loads issued after A(s + 2): 4 of its own step and kAD - 2 full steps.
+  // it waits for A(s + 2), whose first fragments step s + 1 reads early
+  // (the counts above).
 #pragma unroll
   for (int j = 0; j < kAD; ++j) {
     __builtin_amdgcn_sched_barrier(0);
@@ -363,7 +369,10 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     const int nb = buf == kABufs - 1 ? 0 : buf + 1;           \
     const int db = buf + kAD >= kABufs ? buf + kAD - kABufs : buf + kAD; \
     step(buf, nb, BC, BN, base + J, base + J + kAD, db);      \
-    vm_barrier<kWaitSteady>();                                \
+    if (J < 2 && base == 0)                                   \
+      vm_barrier<(kAD - 2) * MBT + 4 * (J + 1)>();            \
+    else                                                      \
+      vm_barrier<kWaitSteady>();                              \
     buf = nb;                                                 \
   }
   for (int base = 0; base < n_st; base += kRing) {

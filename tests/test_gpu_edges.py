@@ -154,14 +154,19 @@ def test_ten_repeats_bitwise_identical(act):
         assert np.array_equal(g[hk], ref[hk]), rep
 
 
-def test_prefill_ten_repeats_bitwise_identical():
+@pytest.mark.parametrize("tile_m", [160, 64])
+def test_prefill_ten_repeats_bitwise_identical(tile_m):
     """The prefill layer (matrix-core path, fixed-order combine) repeated
-    ten times: h and out identical bit for bit (compared on the device)."""
+    ten times: h and out identical bit for bit (compared on the device).
+    Tiles of 64 rows give chunks of one or two 32-row blocks, whose K steps
+    are the shortest: the hand-counted waits for the activation loads of the
+    first steps are exercised hardest there; the separate calls must give
+    the same bits as the layer call."""
     import torch
     from packed_bit_grouped_amd.layer import DeviceLayer
     layer = make_layer(LAYERS["prefill_mixed_t4096"])
     dl = DeviceLayer.from_synth(layer)
-    B = dl.buffers("a16")
+    B = dl.buffers("a16", tile_m)
     dl.run(B)
     torch.cuda.synchronize()
     h0, out0 = B.h.clone(), B.out.clone()
@@ -172,3 +177,7 @@ def test_prefill_ten_repeats_bitwise_identical():
         torch.cuda.synchronize()
         assert torch.equal(B.h, h0) and torch.equal(B.out, out0), rep
     assert B.error_word() == 0
+    B2 = dl.buffers("a16", tile_m)
+    dl.run(B2, fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(B2.h, h0) and torch.equal(B2.out, out0)
