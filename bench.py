@@ -272,6 +272,10 @@ def run_config(cid, args, torch, L, hi, ceiling):
 
     def gateup(bk):
         gflags = flags | (L.MOE_W_PREPACKED if bk.prepacked else 0)
+        if decode and act == "a8":
+            # the step's gate/up reads the int8 x rows its routing launch made
+            # (still in the workspace from the steps above)
+            gflags |= L.MOE_X_QUANTIZED
         if fused:
             L.moe_w4_route_gateup_silu(B.act, dl.logits, dl.x, T, H, I, E, k,
                                        cfg.renormalize, bk.w13, bk.w13_sh, cfg.n_shared,
@@ -287,7 +291,7 @@ def run_config(cid, args, torch, L, hi, ceiling):
         kname = "dec_route_gateup_kernel (route + sort + gate/up + SiLU*mul)"
     elif decode:
         kname = ("proj_m16_kernel<0> (gate/up + SiLU*mul)" if act == "a16" else
-                 "proj_m16_kernel<0> (int8 x rows made in the kernel, gate/up + SiLU*mul)")
+                 "proj_m16_kernel<0> (gate/up + SiLU*mul on the int8 x rows of the routing launch)")
     else:
         kname = ("proj_mfma8_kernel<0> + convert8_kernel (gate/up + SiLU*mul)"
                  + (", prepacked weights" if dl.bank.prepacked else ""))

@@ -237,6 +237,14 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
                               /* launch even where the gate/up kernel would */
                               /* make the int8 rows itself (same codes; a   */
                               /* check and a fallback)                      */
+#define MOE_X_QUANTIZED 64    /* W4A8 moe_w4_gateup_silu: read x's int8    */
+                              /* rows and scales from the workspace, where  */
+                              /* moe_w4_route_gateup_silu / moe_w4_layer    */
+                              /* (T <= 64, H a multiple of 8) left them for */
+                              /* this same x and T, instead of quantizing x */
+                              /* again; the caller guarantees that they are */
+                              /* there.  Ignored by the other calls and for */
+                              /* bf16 activations                            */
 #define MOE_LAYER_ONE_LAUNCH 8 /* moe_w4_layer: one launch for the whole    */
                               /* layer where the shape allows it (same      */
                               /* results as the two calls)                  */
@@ -326,7 +334,12 @@ moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H,
  * T*k <= 64, E <= 512, H <= 2048 and tiles of at most 16 rows (the split-K
  * path) this is ONE launch in which every workgroup routes and sorts the
  * batch itself before its share of the gate/up work; other shapes issue
- * the routing call and the gate/up call.  Errors: those of the two calls.
+ * the routing call and the gate/up call.  For W4A8 with T <= 64 and H a
+ * multiple of 8 (16-byte aligned x) the routing launch also quantizes x
+ * (one extra workgroup per token, the row rule of moe_quant_a8_rows) into
+ * the workspace, and the gate/up call reads those rows (MOE_X_QUANTIZED),
+ * so no quantizing launch or in-kernel quantization follows.  Errors:
+ * those of the two calls.
  * ------------------------------------------------------------------- */
 moe_status moe_w4_route_gateup_silu(int act, const float* logits,
                                     const uint16_t* x, int T, int H, int I,

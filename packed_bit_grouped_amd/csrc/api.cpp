@@ -69,7 +69,8 @@ moe_status check_layer(int act, int T, int H, int I, int E, int k, int n_shared,
   if (k > E) return MOE_E_INVAL;
   if (n_shared > 0 && I_shared <= 0) return MOE_E_INVAL;
   if (tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
-  if (flags & ~(MOE_PATH_MASK | MOE_QUANT_SEPARATE | MOE_OUT_F32 | MOE_W_PREPACKED))
+  if (flags & ~(MOE_PATH_MASK | MOE_QUANT_SEPARATE | MOE_OUT_F32 | MOE_W_PREPACKED |
+                MOE_X_QUANTIZED))
     return MOE_E_INVAL;
   if (H % 32 || I % 32 || (n_shared > 0 && I_shared % 32)) return MOE_E_UNSUPPORTED;
   if (E > kPermMaxE) return MOE_E_UNSUPPORTED;
@@ -244,11 +245,12 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E,
                                  static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_route_permute(const float* logits, int T, int E, int k,
-                             int renormalize, int tile_m, int32_t* topk_ids,
-                             float* topk_w, int32_t* counts, int32_t* offsets,
-                             int32_t* sorted_pair, int32_t* pair_pos,
-                             int32_t* tiles, int32_t* n_tiles, void* stream) {
+static moe_status route_permute_impl(const float* logits, int T, int E, int k,
+                                     int renormalize, int tile_m, int32_t* topk_ids,
+                                     float* topk_w, int32_t* counts, int32_t* offsets,
+                                     int32_t* sorted_pair, int32_t* pair_pos,
+                                     int32_t* tiles, int32_t* n_tiles, void* stream,
+                                     const XQuant* xq) {
   if (T < 0 || E <= 0 || k <= 0 || k > E || tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
   if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
   if (E > kPermMaxE || T > kFusedRouteMaxT || T * k > kFusedRouteMaxP) return MOE_E_UNSUPPORTED;
@@ -261,7 +263,16 @@ moe_status moe_route_permute(const float* logits, int T, int E, int k,
   return from_hip(launch_route_permute(logits, T, E, k, renormalize, tile_m,
                                        topk_ids, topk_w, counts, offsets,
                                        sorted_pair, pair_pos, tiles, n_tiles,
-                                       static_cast<hipStream_t>(stream)));
+                                       static_cast<hipStream_t>(stream), xq));
+}
+
+moe_status moe_route_permute(const float* logits, int T, int E, int k,
+                             int renormalize, int tile_m, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos,
+                             int32_t* tiles, int32_t* n_tiles, void* stream) {
+  return route_permute_impl(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w, counts,
+                            offsets, sorted_pair, pair_pos, tiles, n_tiles, stream, nullptr);
 }
 
 moe_status moe_quant_a8_rows(const void* src, int src_is_f32, int R, int C,
@@ -345,8 +356,12 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   const bool on_m16 = path == MOE_PATH_MFMA16 ||
                       (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs));
   a.in_bf16 = x;
-  if (act == MOE_A8 &&
-      !(on_m16 && !(flags & MOE_QUANT_SEPARATE) && m16_quant_ok(0, T, H, H))) {
+  if (act == MOE_A8 && (flags & MOE_X_QUANTIZED)) {
+    // the int8 rows the routing launch of moe_w4_route_gateup_silu made
+    a.in_q = reinterpret_cast<const int8_t*>(ws + L.qx);
+    a.in_s = reinterpret_cast<const float*>(ws + L.sx);
+  } else if (act == MOE_A8 &&
+             !(on_m16 && !(flags & MOE_QUANT_SEPARATE) && m16_quant_ok(0, T, H, H))) {
     // int8 x rows for the kernels that read them (the 16-row matrix tiles
     // quantize their staged rows themselves when a tile's rows fit)
     int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
@@ -509,6 +524,7 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits, const uint16_t
   moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
   if (st != MOE_OK) return st;
   if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
+  flags &= ~MOE_X_QUANTIZED;   // x is routed here: its int8 rows are made here too
   const bool fused = act == MOE_A16 && T > 0 && (flags & MOE_PATH_MASK) != MOE_PATH_MFMA16 &&
                      !(flags & MOE_W_PREPACKED) &&
                      !use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
@@ -516,8 +532,23 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits, const uint16_t
   if (!fused) {
     // the two calls, each with its own checks
     if (T <= kFusedRouteMaxT && (long long)T * k <= kFusedRouteMaxP && E <= kPermMaxE) {
-      st = moe_route_permute(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w, counts,
-                             offsets, sorted_pair, pair_pos, tiles, n_tiles, stream);
+      // W4A8: the routing launch also makes x's int8 rows (one extra
+      // workgroup per token) and the gate/up call reads them
+      const bool xq_ok = act == MOE_A8 && T > 0 && !(flags & MOE_QUANT_SEPARATE) &&
+                         x && aligned(x, 16) && H % 8 == 0 &&
+                         workspace && aligned(workspace, 256) &&
+                         ws_bytes >= ws_layout(act, T, H, I, E, k, n_shared, I_shared).total;
+      XQuant xq = {nullptr, 0, nullptr, nullptr};
+      if (xq_ok) {
+        const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
+        char* ws = static_cast<char*>(workspace);
+        xq = XQuant{x, H, reinterpret_cast<int8_t*>(ws + L.qx),
+                    reinterpret_cast<float*>(ws + L.sx)};
+        flags |= MOE_X_QUANTIZED;
+      }
+      st = route_permute_impl(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w, counts,
+                              offsets, sorted_pair, pair_pos, tiles, n_tiles, stream,
+                              xq_ok ? &xq : nullptr);
     } else {
       st = moe_route_topk(logits, T, E, k, renormalize, topk_ids, topk_w, stream);
       if (st == MOE_OK)

@@ -95,11 +95,22 @@ hipError_t launch_permute_multi(const int32_t* ids, int P, int E, int tile_m, in
                                 int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                                 int32_t* tiles, int32_t* n_tiles, int32_t* scratch,
                                 hipStream_t st);
+// W4A8: int8 rows of x made by extra workgroups of the routing launch (one
+// row each, the row quantizer's rule), so that the gate/up projection needs
+// no quantizing launch of its own.  x bf16 [T][H], 16-byte aligned, H a
+// multiple of 8; q [T][H]; s [T].
+struct XQuant {
+  const uint16_t* x;
+  int H;
+  int8_t* q;
+  float* s;
+};
 hipError_t launch_route_permute(const float* logits, int T, int E, int k,
                                 int renorm, int tile_m, int32_t* ids, float* w,
                                 int32_t* counts, int32_t* offsets,
                                 int32_t* sorted_pair, int32_t* pair_pos,
-                                int32_t* tiles, int32_t* n_tiles, hipStream_t st);
+                                int32_t* tiles, int32_t* n_tiles, hipStream_t st,
+                                const XQuant* xq = nullptr);
 // Rows [R][C] (row stride ld) to int8 rows of stride ldq and fp32 scales.
 hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
                            int8_t* q, int ldq, float* s, hipStream_t st);

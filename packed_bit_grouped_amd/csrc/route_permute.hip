@@ -11,14 +11,62 @@
 
 namespace moe {
 
+// One row of x to int8 codes and its scale by one workgroup of THREADS
+// threads: the row's absolute maximum (a block reduction: order-free), then
+// the row quantizer's a8_scale / a8_code, so the codes equal that launch's.
+// 16-byte loads of 8 values; the second pass reloads them (cache hits).
+template <int THREADS>
+__device__ void quant_x_row(const XQuant& xq, int t) {
+  __shared__ float red[THREADS / 64];
+  const int tid = threadIdx.x;
+  const uint16_t* row = xq.x + (size_t)t * xq.H;
+  float amax = 0.0f;
+  for (int c = tid * 8; c < xq.H; c += THREADS * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = fmaxf(amax, fabsf(bf16_to_f32(u[j] & 0xFFFFu)));
+      amax = fmaxf(amax, fabsf(bf16_to_f32(u[j] >> 16)));
+    }
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int i = 1; i < THREADS / 64; ++i) amax = fmaxf(amax, red[i]);
+  const float sc = a8_scale(amax);
+  int8_t* qrow = xq.q + (size_t)t * xq.H;
+  for (int c = tid * 8; c < xq.H; c += THREADS * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      lo |= ((uint32_t)a8_code(bf16_to_f32(u[j] & 0xFFFFu), sc) & 0xFFu) << (16 * j);
+      lo |= ((uint32_t)a8_code(bf16_to_f32(u[j] >> 16), sc) & 0xFFu) << (16 * j + 8);
+      hi |= ((uint32_t)a8_code(bf16_to_f32(u[j + 2] & 0xFFFFu), sc) & 0xFFu) << (16 * j);
+      hi |= ((uint32_t)a8_code(bf16_to_f32(u[j + 2] >> 16), sc) & 0xFFu) << (16 * j + 8);
+    }
+    *reinterpret_cast<uint2*>(qrow + c) = make_uint2(lo, hi);
+  }
+  if (tid == 0) xq.s[t] = sc;
+}
+
+// Workgroups [0, nrb) route, 16 tokens each: four per wave (one per row of
+// 16 lanes, or one after another for E > 256); with xq.x set, workgroup
+// nrb + t quantizes row t of x.
 template <int NV>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm,
-    int32_t* __restrict__ ids, float* __restrict__ w) {
-  // 16 tokens per workgroup: four per wave (one per row of 16 lanes, or
-  // one after another for E > 256)
+    int32_t* __restrict__ ids, float* __restrict__ w, int nrb, XQuant xq) {
+  if ((int)blockIdx.x >= nrb) {
+    quant_x_row<256>(xq, blockIdx.x - nrb);
+    return;
+  }
   route_tokens<NV, 1>(logits, T, E, k, renorm, threadIdx.x & 63,
-                      blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4, ids, w, nullptr,
+                      blockIdx.x * 4 + (threadIdx.x >> 6), nrb * 4, ids, w, nullptr,
                       nullptr);
 }
 
@@ -290,7 +338,11 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(
     int tile_m, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, XQuant xq) {
+  if (blockIdx.x > 0) {   // with xq.x set: workgroup 1 + t quantizes row t of x
+    quant_x_row<1024>(xq, blockIdx.x - 1);
+    return;
+  }
   __shared__ PermSmem sm;
   __shared__ int32_t lds_ids[kFusedRouteMaxP];
   static_assert(kFusedRouteMaxT == 4 * kPermWaves, "one token per row of 16 lanes");
@@ -460,9 +512,10 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k,
                              int renorm, int32_t* ids, float* w,
                              hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((T + 15) / 16), block(256);
-  MOE_NV_DISPATCH(NV, route_topk_kernel<NV><<<grid, block, 0, st>>>(
-                          logits, T, E, k, renorm, ids, w));
+  const int nrb = (T + 15) / 16;
+  const XQuant none = {nullptr, 0, nullptr, nullptr};
+  MOE_NV_DISPATCH(NV, route_topk_kernel<NV><<<nrb, 256, 0, st>>>(
+                          logits, T, E, k, renorm, ids, w, nrb, none));
   return hipGetLastError();
 }
 
@@ -498,18 +551,23 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k,
                                 int32_t* counts, int32_t* offsets,
                                 int32_t* sorted_pair, int32_t* pair_pos,
                                 int32_t* tiles, int32_t* n_tiles,
-                                hipStream_t st) {
+                                hipStream_t st, const XQuant* xq) {
+  const XQuant q = xq ? *xq : XQuant{nullptr, 0, nullptr, nullptr};
+  const int nq = xq ? T : 0;   // quantizing workgroups, one per row of x
   // from 16 tokens on the routing is worth more than one compute unit: the
   // multi-workgroup router, then the sort (same functions, same results)
   if (T >= kRouteRowMinT) {
-    const hipError_t e = launch_route_topk(logits, T, E, k, renorm, ids, w, st);
+    const int nrb = (T + 15) / 16;
+    MOE_NV_DISPATCH(NV, route_topk_kernel<NV><<<nrb + nq, 256, 0, st>>>(
+                            logits, T, E, k, renorm, ids, w, nrb, q));
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_permute(ids, T * k, E, tile_m, counts, offsets, sorted_pair, pair_pos, tiles,
                           n_tiles, st);
   }
-  MOE_NV_DISPATCH(NV, route_permute_kernel<NV><<<1, 1024, 0, st>>>(
+  MOE_NV_DISPATCH(NV, route_permute_kernel<NV><<<1 + nq, 1024, 0, st>>>(
                           logits, T, E, k, renorm, tile_m, ids, w, counts,
-                          offsets, sorted_pair, pair_pos, tiles, n_tiles));
+                          offsets, sorted_pair, pair_pos, tiles, n_tiles, q));
   return hipGetLastError();
 }
 

@@ -135,7 +135,8 @@ def test_gateup_validation():
     assert _gateup(workspace=None) == L.MOE_E_WORKSPACE
     assert _gateup(workspace=FAKE + 64) == L.MOE_E_WORKSPACE  # 256-byte alignment
     assert _gateup(flags=8) == L.MOE_E_INVAL
-    assert _gateup(flags=64) == L.MOE_E_INVAL
+    assert _gateup(flags=128) == L.MOE_E_INVAL
+    assert _gateup(flags=L.MOE_X_QUANTIZED, act=1) == L.MOE_E_DEVICE
     assert _gateup(flags=L.MOE_QUANT_SEPARATE | L.MOE_PATH_MFMA16, act=1) == L.MOE_E_DEVICE
     # forced 16-row MFMA tiles: tiles of at most 16 rows, activations in LDS
     assert _gateup(flags=L.MOE_PATH_MFMA16, tile_m=32) == L.MOE_E_UNSUPPORTED
@@ -226,7 +227,7 @@ def test_layer_validation():
     assert call(renormalize=2) == L.MOE_E_INVAL
     assert call(act=2) == L.MOE_E_INVAL
     assert call(k=129) == L.MOE_E_INVAL
-    assert call(flags=64) == L.MOE_E_INVAL
+    assert call(flags=128) == L.MOE_E_INVAL
     assert call(out=None) == L.MOE_E_INVAL
     assert call(w2_shared=None) == L.MOE_E_INVAL
     assert call(workspace=None) == L.MOE_E_WORKSPACE

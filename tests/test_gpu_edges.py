@@ -127,18 +127,43 @@ def test_edge_activation_rows(name, act, flags):
 
 
 @pytest.mark.parametrize("name", ["mixed_shared", "c3_t16"])
-def test_in_kernel_int8_rows_match_row_quantizer_on_edge_rows(name):
-    """W4A8 on the 16-row matrix tiles makes its int8 x rows in the kernel;
-    on the edge rows (zero row, subnormal row scale, zero elements) they
-    equal the row quantizer's bit for bit, so h and out do too."""
+def test_int8_rows_of_every_maker_match_row_quantizer_on_edge_rows(name):
+    """W4A8 x rows are made three ways: by the routing launch of the layer
+    call (extra workgroups), by the 16-row gate/up kernel itself (separate
+    calls), and by the row quantizer launch (MOE_QUANT_SEPARATE).  On the
+    edge rows (zero row, subnormal row scale, zero elements) all three give
+    the same codes and scales, so h and out agree bit for bit."""
     from packed_bit_grouped_amd.layer import DeviceLayer
     layer = _edge_rows(_base(name))
     dl = DeviceLayer.from_synth(layer)
     g1, _ = run_layer_gpu(dl, "a8", 16, 3)
     g2, _ = run_layer_gpu(dl, "a8", 16, 3 | 4)
-    assert np.array_equal(g1["h32"], g2["h32"])
-    assert np.array_equal(g1["out"], g2["out"])
-    assert g1["err"] == 0 and g2["err"] == 0
+    g3, _ = run_layer_gpu(dl, "a8", 16, 3, fused=False)
+    for g in (g2, g3):
+        assert np.array_equal(g1["h32"], g["h32"])
+        assert np.array_equal(g1["out"], g["out"])
+    assert g1["err"] == 0 and g2["err"] == 0 and g3["err"] == 0
+
+
+@pytest.mark.parametrize("name", ["mixed_shared_a8", "c3_t16"])
+def test_gateup_reads_int8_rows_left_by_the_layer_call(name):
+    """MOE_X_QUANTIZED: after a W4A8 layer call the workspace holds x's int8
+    rows; a gate/up call that reads them writes the same h as the layer."""
+    from packed_bit_grouped_amd import _lib as L
+    from packed_bit_grouped_amd.layer import DeviceLayer
+    torch = pytest.importorskip("torch")
+    layer = _base(name)
+    cfg = layer.cfg
+    dl = DeviceLayer.from_synth(layer)
+    g1, B = run_layer_gpu(dl, "a8", 16, 0)
+    B.h.zero_()
+    L.moe_w4_gateup_silu(B.act, dl.x, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dl.bank.w13,
+                         dl.bank.w13_sh, cfg.n_shared, cfg.I_shared, B.offsets,
+                         B.sorted_pair, B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes,
+                         L.MOE_X_QUANTIZED)
+    torch.cuda.synchronize()
+    h = B.h.cpu().numpy()[:B.R].astype(np.float32)
+    assert np.array_equal(h, g1["h32"])
 
 
 @pytest.mark.parametrize("act", ["a16", "a8"])
