@@ -202,13 +202,13 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int tile_m,
 // ---------------------------------------------------------------------
 // The same sort over many workgroups, for large batches (the layer call,
 // with its workspace): workgroup b takes pairs [b * kPermChunk, +kPermChunk).
-// (1) each workgroup counts its chunk per expert -> hist[b][e]; (2) one
-// workgroup forms counts, offsets and the tile list and turns hist into the
-// first sorted position of every (workgroup, expert): offsets[e] plus the
-// counts of workgroups 0..b-1; (3) each workgroup places its chunk from
-// those positions with the per-wave counts and ballot ranks of
-// permute_body.  Pairs of an expert stay in increasing p, so the result is
-// the single workgroup's, bit for bit.
+// Two launches: (1) each workgroup counts its chunk per expert ->
+// hist[b][e]; (2) each workgroup forms the offsets from all the counts
+// (workgroup 0 also writes counts, offsets and the tile list), its first
+// sorted position of every expert: offsets[e] plus the counts of
+// workgroups 0..b-1, and places its chunk from there with the per-wave
+// counts and ballot ranks of permute_body.  Pairs of an expert stay in
+// increasing p, so the result is the single workgroup's, bit for bit.
 constexpr int kPermChunk = 2048;   // pairs per workgroup (128 per wave)
 
 __global__ __launch_bounds__(1024) void perm_hist_kernel(const int32_t* __restrict__ ids, int P,
@@ -225,69 +225,76 @@ __global__ __launch_bounds__(1024) void perm_hist_kernel(const int32_t* __restri
   for (int i = threadIdx.x; i < E; i += 1024) hist[(size_t)blockIdx.x * E + i] = h[i];
 }
 
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int P, int E, int nb, int tile_m,
-                                                         int32_t* __restrict__ hist,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ sorted_pair,
-                                                         int32_t* __restrict__ tiles,
-                                                         int32_t* __restrict__ n_tiles) {
+// (2) + (3) in one launch: every workgroup sums the chunks' counts into the
+// expert totals (all of hist: nb * E ints from the cache), scans them into
+// the offsets, adds the counts of chunks 0..b-1 for its own first positions
+// and places its chunk; workgroup 0 also writes counts, offsets, the tile
+// list, n_tiles and the -1 tail of sorted_pair.
+__global__ __launch_bounds__(1024) void perm_place_kernel(const int32_t* __restrict__ ids, int P,
+                                                          int E, int nb, int tile_m,
+                                                          const int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_pair,
+                                                          int32_t* __restrict__ pair_pos,
+                                                          int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ n_tiles) {
+  __shared__ int wh[kPermWaves * kPermMaxE];
   __shared__ int tmp[kPermWaves + 1];
   __shared__ int total;
-  const int tid = threadIdx.x;
-  int cnt = 0;
-  if (tid < E)
-    for (int b = 0; b < nb; ++b) cnt += hist[(size_t)b * E + tid];
-  const int excl = block_exclusive_scan(cnt, tmp);
-  const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
-  const int texcl = block_exclusive_scan(ntile, tmp);
-  if (tid < E) {
-    counts[tid] = cnt;
-    offsets[tid] = excl;
-    int run = excl;
-    for (int b = 0; b < nb; ++b) {
-      const int c = hist[(size_t)b * E + tid];
-      hist[(size_t)b * E + tid] = run;
-      run += c;
-    }
-    for (int i = 0; i < ntile; ++i) {
-      const int r0 = excl + i * tile_m;
-      int4 tl;
-      tl.x = tid;
-      tl.y = r0;
-      tl.z = min(r0 + tile_m, excl + cnt);
-      tl.w = 0;
-      reinterpret_cast<int4*>(tiles)[texcl + i] = tl;
-    }
-    if (tid == E - 1) {
-      offsets[E] = excl + cnt;
-      *n_tiles = texcl + ntile;
-      total = excl + cnt;
-    }
-  }
-  __syncthreads();
-  for (int i = total + tid; i < P; i += 1024) sorted_pair[i] = -1;
-}
-
-__global__ __launch_bounds__(1024) void perm_scatter_kernel(const int32_t* __restrict__ ids,
-                                                            int P, int E,
-                                                            const int32_t* __restrict__ first,
-                                                            int32_t* __restrict__ sorted_pair,
-                                                            int32_t* __restrict__ pair_pos) {
-  __shared__ int wh[kPermWaves * kPermMaxE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  // the chunk's counts per wave and expert (exact integer atomics)
   for (int i = tid; i < kPermWaves * kPermMaxE; i += 1024) wh[i] = 0;
   __syncthreads();
   constexpr int seg = kPermChunk / kPermWaves;
-  const int p0 = min(P, (int)blockIdx.x * kPermChunk + wave * seg), p1 = min(P, p0 + seg);
+  const int p0 = min(P, b * kPermChunk + wave * seg), p1 = min(P, p0 + seg);
   for (int p = p0 + lane; p < p1; p += 64) {
     const int e = ids[p];
     if ((unsigned)e < (unsigned)E) atomicAdd(&wh[wave * kPermMaxE + e], 1);
   }
-  __syncthreads();
+  // expert totals and the counts of the chunks before this one, eight
+  // chunks' loads in flight at a time
+  int cnt = 0, before = 0;
   if (tid < E) {
-    // wave w of this workgroup starts expert tid after waves 0..w-1
-    int run = first[(size_t)blockIdx.x * E + tid];
+    for (int c0 = 0; c0 < nb; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nb ? hist[(size_t)(c0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        cnt += v[u];
+        before += c0 + u < b ? v[u] : 0;
+      }
+    }
+  }
+  const int excl = block_exclusive_scan(cnt, tmp);
+  if (b == 0) {   // uniform in the workgroup: the scan's barriers are reached by all
+    const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
+    const int texcl = block_exclusive_scan(ntile, tmp);
+    if (tid < E) {
+      counts[tid] = cnt;
+      offsets[tid] = excl;
+      for (int i = 0; i < ntile; ++i) {
+        const int r0 = excl + i * tile_m;
+        int4 tl;
+        tl.x = tid;
+        tl.y = r0;
+        tl.z = min(r0 + tile_m, excl + cnt);
+        tl.w = 0;
+        reinterpret_cast<int4*>(tiles)[texcl + i] = tl;
+      }
+      if (tid == E - 1) {
+        offsets[E] = excl + cnt;
+        *n_tiles = texcl + ntile;
+      }
+    }
+  }
+  if (tid == E - 1) total = excl + cnt;
+  __syncthreads();   // the wave counts are complete
+  if (tid < E) {
+    // wave w of this chunk starts expert tid after waves 0..w-1
+    int run = excl + before;
 #pragma unroll
     for (int w = 0; w < kPermWaves; ++w) {
       const int c = wh[w * kPermMaxE + tid];
@@ -304,10 +311,10 @@ __global__ __launch_bounds__(1024) void perm_scatter_kernel(const int32_t* __res
     const bool valid = in && (unsigned)e < (unsigned)E;
     unsigned long long m = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < kPermIdBits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const unsigned long long bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
+    for (int bb = 0; bb < kPermIdBits; ++bb) {
+      const bool bit = valid && ((e >> bb) & 1);
+      const unsigned long long bm = __ballot(bit);
+      m &= bit ? bm : ~bm;
     }
     if (valid) {
       const int pos = wh[wave * kPermMaxE + e] + __popcll(m & below);
@@ -318,6 +325,8 @@ __global__ __launch_bounds__(1024) void perm_scatter_kernel(const int32_t* __res
       pair_pos[p] = -1;
     }
   }
+  if (b == 0)
+    for (int i = total + tid; i < P; i += 1024) sorted_pair[i] = -1;
 }
 
 __global__ __launch_bounds__(1024) void permute_kernel(
@@ -540,9 +549,8 @@ hipError_t launch_permute_multi(const int32_t* ids, int P, int E, int tile_m, in
   if (nb == 0) return launch_permute(ids, P, E, tile_m, counts, offsets, sorted_pair, pair_pos,
                                      tiles, n_tiles, st);
   perm_hist_kernel<<<nb, 1024, 0, st>>>(ids, P, E, scratch);
-  perm_scan_kernel<<<1, 1024, 0, st>>>(P, E, nb, tile_m, scratch, counts, offsets, sorted_pair,
-                                       tiles, n_tiles);
-  perm_scatter_kernel<<<nb, 1024, 0, st>>>(ids, P, E, scratch, sorted_pair, pair_pos);
+  perm_place_kernel<<<nb, 1024, 0, st>>>(ids, P, E, nb, tile_m, scratch, counts, offsets,
+                                         sorted_pair, pair_pos, tiles, n_tiles);
   return hipGetLastError();
 }
 

@@ -46,6 +46,9 @@ MFMA = {
                                  I=128, group=64, n_int2=3, group_int2=32),
     "mfma_g256": LayerConfig("mfma_g256", 212, T=130, H=1024, E=8, k=3, I=512,
                              group=256, n_int2=2, group_int2=128),
+    # 8800 pairs: the sort over five workgroups of 2048 pairs, the last partial
+    "mfma_multisort": LayerConfig("mfma_multisort", 214, T=1100, H=256, E=48, k=8, I=128,
+                                  group=128, n_int2=8, group_int2=64),
 }
 
 _cache = {}
