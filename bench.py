@@ -272,10 +272,11 @@ def run_config(cid, args, torch, L, hi, ceiling):
 
     def gateup(bk):
         gflags = flags | (L.MOE_W_PREPACKED if bk.prepacked else 0)
-        if decode and act == "a8":
-            # the step's gate/up reads the int8 x rows its routing launch made
-            # (still in the workspace from the steps above)
-            gflags |= L.MOE_X_QUANTIZED
+        if (decode and act == "a8") or not decode:
+            # the step's gate/up reads the copy of x its routing launch made
+            # (int8 rows / the fp16 copy; still in the workspace from the
+            # steps above)
+            gflags |= L.MOE_X_PREPARED
         if fused:
             L.moe_w4_route_gateup_silu(B.act, dl.logits, dl.x, T, H, I, E, k,
                                        cfg.renormalize, bk.w13, bk.w13_sh, cfg.n_shared,
@@ -293,7 +294,7 @@ def run_config(cid, args, torch, L, hi, ceiling):
         kname = ("proj_m16_kernel<0> (gate/up + SiLU*mul)" if act == "a16" else
                  "proj_m16_kernel<0> (gate/up + SiLU*mul on the int8 x rows of the routing launch)")
     else:
-        kname = ("proj_mfma8_kernel<0> + convert8_kernel (gate/up + SiLU*mul)"
+        kname = ("proj_mfma8_kernel<0> (gate/up + SiLU*mul on the fp16 x copy of the routing launch)"
                  + (", prepacked weights" if dl.bank.prepacked else ""))
     n_k = len(banks) if decode else 4
     gk = torch.cuda.CUDAGraph()

@@ -237,14 +237,16 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
                               /* launch even where the gate/up kernel would */
                               /* make the int8 rows itself (same codes; a   */
                               /* check and a fallback)                      */
-#define MOE_X_QUANTIZED 64    /* W4A8 moe_w4_gateup_silu: read x's int8    */
-                              /* rows and scales from the workspace, where  */
-                              /* moe_w4_route_gateup_silu / moe_w4_layer    */
-                              /* (T <= 64, H a multiple of 8) left them for */
-                              /* this same x and T, instead of quantizing x */
-                              /* again; the caller guarantees that they are */
-                              /* there.  Ignored by the other calls and for */
-                              /* bf16 activations                            */
+#define MOE_X_PREPARED 64     /* moe_w4_gateup_silu: read the prepared copy */
+                              /* of x from the workspace instead of making  */
+                              /* it: W4A8 int8 rows and scales, or the fp16 */
+                              /* copy the matrix-core path stages (bf16,    */
+                              /* prefill shapes).  The routing launch of    */
+                              /* moe_w4_route_gateup_silu (W4A8, T <= 64,   */
+                              /* H a multiple of 8) and of moe_w4_layer     */
+                              /* (also the matrix-core path) leaves it for  */
+                              /* that x and T; the caller guarantees it is  */
+                              /* there.  Ignored where no copy is read      */
 #define MOE_LAYER_ONE_LAUNCH 8 /* moe_w4_layer: one launch for the whole    */
                               /* layer where the shape allows it (same      */
                               /* results as the two calls)                  */
@@ -337,8 +339,9 @@ moe_status moe_w4_gateup_silu(int act, const uint16_t* x, int T, int H,
  * the routing call and the gate/up call.  For W4A8 with T <= 64 and H a
  * multiple of 8 (16-byte aligned x) the routing launch also quantizes x
  * (one extra workgroup per token, the row rule of moe_quant_a8_rows) into
- * the workspace, and the gate/up call reads those rows (MOE_X_QUANTIZED),
- * so no quantizing launch or in-kernel quantization follows.  Errors:
+ * the workspace, and the gate/up call reads those rows (MOE_X_PREPARED),
+ * so no quantizing launch or in-kernel quantization follows.  (moe_w4_layer
+ * does the same with the fp16 copy of x on the matrix-core path.)  Errors:
  * those of the two calls.
  * ------------------------------------------------------------------- */
 moe_status moe_w4_route_gateup_silu(int act, const float* logits,

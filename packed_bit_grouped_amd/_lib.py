@@ -20,7 +20,7 @@ MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_DEVICE, MOE_E_WORKSPACE = 0, -1, -
 MOE_A16, MOE_A8 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA, MOE_PATH_MFMA16 = 0, 1, 2, 3
 MOE_QUANT_SEPARATE = 4
-MOE_X_QUANTIZED = 64
+MOE_X_PREPARED = 64
 MOE_LAYER_ONE_LAUNCH = 8
 MOE_OUT_F32 = 16
 MOE_W_PREPACKED = 32

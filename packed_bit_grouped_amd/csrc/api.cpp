@@ -70,7 +70,7 @@ moe_status check_layer(int act, int T, int H, int I, int E, int k, int n_shared,
   if (n_shared > 0 && I_shared <= 0) return MOE_E_INVAL;
   if (tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
   if (flags & ~(MOE_PATH_MASK | MOE_QUANT_SEPARATE | MOE_OUT_F32 | MOE_W_PREPACKED |
-                MOE_X_QUANTIZED))
+                MOE_X_PREPARED))
     return MOE_E_INVAL;
   if (H % 32 || I % 32 || (n_shared > 0 && I_shared % 32)) return MOE_E_UNSUPPORTED;
   if (E > kPermMaxE) return MOE_E_UNSUPPORTED;
@@ -184,9 +184,9 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
   return ws_layout(act, T, H, I, E, k, n_shared, I_shared).total;
 }
 
-moe_status moe_route_topk(const float* logits, int T, int E, int k,
-                          int renormalize, int32_t* topk_ids, float* topk_w,
-                          void* stream) {
+static moe_status route_topk_impl(const float* logits, int T, int E, int k,
+                                  int renormalize, int32_t* topk_ids, float* topk_w,
+                                  void* stream, const XPrep* xp) {
   if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_E_INVAL;
   if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
   if (E > kRouteMaxE) return MOE_E_UNSUPPORTED;
@@ -195,7 +195,13 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k,
   const moe_status d = check_device();
   if (d != MOE_OK) return d;
   return from_hip(launch_route_topk(logits, T, E, k, renormalize, topk_ids,
-                                    topk_w, static_cast<hipStream_t>(stream)));
+                                    topk_w, static_cast<hipStream_t>(stream), xp));
+}
+
+moe_status moe_route_topk(const float* logits, int T, int E, int k,
+                          int renormalize, int32_t* topk_ids, float* topk_w,
+                          void* stream) {
+  return route_topk_impl(logits, T, E, k, renormalize, topk_ids, topk_w, stream, nullptr);
 }
 
 size_t moe_router_workspace_bytes(int T, int H, int E) {
@@ -250,7 +256,7 @@ static moe_status route_permute_impl(const float* logits, int T, int E, int k,
                                      float* topk_w, int32_t* counts, int32_t* offsets,
                                      int32_t* sorted_pair, int32_t* pair_pos,
                                      int32_t* tiles, int32_t* n_tiles, void* stream,
-                                     const XQuant* xq) {
+                                     const XPrep* xq) {
   if (T < 0 || E <= 0 || k <= 0 || k > E || tile_m <= 0 || tile_m > 4096) return MOE_E_INVAL;
   if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
   if (E > kPermMaxE || T > kFusedRouteMaxT || T * k > kFusedRouteMaxP) return MOE_E_UNSUPPORTED;
@@ -348,6 +354,8 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
     if (!mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) return MOE_E_UNSUPPORTED;
     a.in_bf16 = x;
     uint16_t* x16 = reinterpret_cast<uint16_t*>(ws + L.a16);
+    // the routing launch of moe_w4_layer made the fp16 copy of x already
+    if (flags & MOE_X_PREPARED) a.in16_ready = 1;
     if (stage_h16) a.out16 = reinterpret_cast<uint16_t*>(ws + L.h16);
     return from_hip(launch_proj_mfma8(a, x16, pp, s));
   }
@@ -356,7 +364,7 @@ static moe_status gateup_impl(int act, const uint16_t* x, int T, int H, int I,
   const bool on_m16 = path == MOE_PATH_MFMA16 ||
                       (path == MOE_PATH_AUTO && m16 && !(dec && (long long)T * k <= kDecPairs));
   a.in_bf16 = x;
-  if (act == MOE_A8 && (flags & MOE_X_QUANTIZED)) {
+  if (act == MOE_A8 && (flags & MOE_X_PREPARED)) {
     // the int8 rows the routing launch of moe_w4_route_gateup_silu made
     a.in_q = reinterpret_cast<const int8_t*>(ws + L.qx);
     a.in_s = reinterpret_cast<const float*>(ws + L.sx);
@@ -524,7 +532,7 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits, const uint16_t
   moe_status st = check_layer(act, T, H, I, E, k, n_shared, I_shared, tile_m, flags);
   if (st != MOE_OK) return st;
   if (renormalize != 0 && renormalize != 1) return MOE_E_INVAL;
-  flags &= ~MOE_X_QUANTIZED;   // x is routed here: its int8 rows are made here too
+  flags &= ~MOE_X_PREPARED;   // x is routed here: its int8 rows are made here too
   const bool fused = act == MOE_A16 && T > 0 && (flags & MOE_PATH_MASK) != MOE_PATH_MFMA16 &&
                      !(flags & MOE_W_PREPACKED) &&
                      !use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
@@ -538,13 +546,13 @@ moe_status moe_w4_route_gateup_silu(int act, const float* logits, const uint16_t
                          x && aligned(x, 16) && H % 8 == 0 &&
                          workspace && aligned(workspace, 256) &&
                          ws_bytes >= ws_layout(act, T, H, I, E, k, n_shared, I_shared).total;
-      XQuant xq = {nullptr, 0, nullptr, nullptr};
+      XPrep xq = {nullptr, 0, nullptr, nullptr, nullptr};
       if (xq_ok) {
         const WsLayout L = ws_layout(act, T, H, I, E, k, n_shared, I_shared);
         char* ws = static_cast<char*>(workspace);
-        xq = XQuant{x, H, reinterpret_cast<int8_t*>(ws + L.qx),
-                    reinterpret_cast<float*>(ws + L.sx)};
-        flags |= MOE_X_QUANTIZED;
+        xq = XPrep{x, H, reinterpret_cast<int8_t*>(ws + L.qx),
+                   reinterpret_cast<float*>(ws + L.sx), nullptr};
+        flags |= MOE_X_PREPARED;
       }
       st = route_permute_impl(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w, counts,
                               offsets, sorted_pair, pair_pos, tiles, n_tiles, stream,
@@ -770,13 +778,16 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, 
   }
   if (T > 0 && use_mfma(act, T, H, I, E, k, n_shared, I_shared, flags) &&
       mfma_shape_ok(act, T, H, I, k, n_shared, I_shared)) {
-    // matrix-core form: the gate/up epilogue also writes the fp16 copy of h
-    // the down projection reads, so no conversion pass runs between them
+    // matrix-core form: the routing launch also makes the fp16 copy of x the
+    // gate/up stages (extra workgroups), and the gate/up epilogue writes the
+    // fp16 copy of h the down projection reads, so no conversion pass runs
+    const XPrep xp = {x, H, nullptr, nullptr,
+                      reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + L.a16)};
     if (T <= kFusedRouteMaxT && (long long)T * k <= kFusedRouteMaxP && E <= kPermMaxE) {
-      st = moe_route_permute(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w, counts,
-                             offsets, sorted_pair, pair_pos, tiles, n_tiles, stream);
+      st = route_permute_impl(logits, T, E, k, renormalize, tile_m, topk_ids, topk_w, counts,
+                              offsets, sorted_pair, pair_pos, tiles, n_tiles, stream, &xp);
     } else {
-      st = moe_route_topk(logits, T, E, k, renormalize, topk_ids, topk_w, stream);
+      st = route_topk_impl(logits, T, E, k, renormalize, topk_ids, topk_w, stream, &xp);
       if (st == MOE_OK && permute_multi_blocks(T * k) > 0) {
         // the sort over many workgroups, with its counts in the workspace
         st = from_hip(launch_permute_multi(
@@ -790,8 +801,8 @@ moe_status moe_w4_layer(int act, const float* logits, const uint16_t* x, int T, 
     }
     if (st != MOE_OK) return st;
     st = gateup_impl(act, x, T, H, I, E, k, w13, w13_shared, n_shared, I_shared, offsets,
-                     sorted_pair, tiles, n_tiles, tile_m, h, workspace, ws_bytes, flags,
-                     nullptr, 0, stream, true);
+                     sorted_pair, tiles, n_tiles, tile_m, h, workspace, ws_bytes,
+                     flags | MOE_X_PREPARED, nullptr, 0, stream, true);
     if (st != MOE_OK) return st;
     return down_impl(act, h, T, H, I, E, k, w2, w2_shared, n_shared, I_shared, shared_gate,
                      topk_w, offsets, sorted_pair, pair_pos, tiles, n_tiles, tile_m, out,

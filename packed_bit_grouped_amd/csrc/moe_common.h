@@ -240,4 +240,20 @@ __device__ __forceinline__ bool qmat_usable(const moe_qmat& q, int N, int K) {
   return true;
 }
 
+// fp16 copy of 8 bf16 values in the order (0,4)(1,5)(2,6)(3,7): the order
+// in which the matrix-core path unpacks 8 int4 codes (and int2 codes after
+// their byte reorder), so one copy of x serves both formats.  Exact for
+// values within fp16 range (bf16 has fewer mantissa bits).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t lo_bf16, uint32_t hi_bf16) {
+  const float x0 = __uint_as_float(lo_bf16 << 16);
+  const float x1 = __uint_as_float(hi_bf16 << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+}
+__device__ __forceinline__ uint4 convert8(uint4 v) {
+  const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                         v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+  return make_uint4(bf16x2_to_f16x2(e[0], e[4]), bf16x2_to_f16x2(e[1], e[5]),
+                    bf16x2_to_f16x2(e[2], e[6]), bf16x2_to_f16x2(e[3], e[7]));
+}
+
 }  // namespace moe

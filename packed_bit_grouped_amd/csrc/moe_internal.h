@@ -66,7 +66,8 @@ struct ProjArgs {
   const float* topk_w;
   const int32_t* pair_pos;
   uint16_t* out16;             // MFMA gate/up: also write h as fp16 in the unpack order, or null
-  int in16_ready;              // MFMA down: in_bf16 already holds that fp16 copy
+  int in16_ready;              // MFMA down: in_bf16 already holds that fp16 copy;
+                               // MFMA gate/up: the fp16 copy of x is made
   int out_f32;                 // the combined output is fp32 (else bf16)
   const float* sh_gate;        // shared-expert gate logits [T][n_shared], or null (weight 1)
   int32_t* partials;           // A8 test hook (null otherwise)
@@ -74,8 +75,7 @@ struct ProjArgs {
   int part_rows;               // row stride (in weight rows) of partials
 };
 
-hipError_t launch_route_topk(const float* logits, int T, int E, int k,
-                             int renorm, int32_t* ids, float* w, hipStream_t st);
+
 // Router logits = x . W (+ prior), fp32 in a fixed order; part: the
 // workspace of router_workspace_bytes (null when that is 0).
 size_t router_workspace_bytes(int T, int H, int E);
@@ -95,22 +95,29 @@ hipError_t launch_permute_multi(const int32_t* ids, int P, int E, int tile_m, in
                                 int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                                 int32_t* tiles, int32_t* n_tiles, int32_t* scratch,
                                 hipStream_t st);
-// W4A8: int8 rows of x made by extra workgroups of the routing launch (one
-// row each, the row quantizer's rule), so that the gate/up projection needs
-// no quantizing launch of its own.  x bf16 [T][H], 16-byte aligned, H a
-// multiple of 8; q [T][H]; s [T].
-struct XQuant {
+// Copies of x made by extra workgroups of the routing launch, so that the
+// gate/up projection needs no preparing launch of its own: W4A8 int8 rows
+// and scales (q, s: one workgroup per row, the row quantizer's rule), or
+// the matrix-core path's fp16 copy in the unpack order (x16).  x bf16
+// [T][H], 16-byte aligned, H a multiple of 8.
+struct XPrep {
   const uint16_t* x;
   int H;
-  int8_t* q;
-  float* s;
+  int8_t* q;        // [T][H], or null
+  float* s;         // [T]
+  uint16_t* x16;    // [T][H] fp16, or null
 };
+// workgroups of 256 threads that make the fp16 copy of T rows of H
+int xprep_convert_blocks(int T, int H);
 hipError_t launch_route_permute(const float* logits, int T, int E, int k,
                                 int renorm, int tile_m, int32_t* ids, float* w,
                                 int32_t* counts, int32_t* offsets,
                                 int32_t* sorted_pair, int32_t* pair_pos,
                                 int32_t* tiles, int32_t* n_tiles, hipStream_t st,
-                                const XQuant* xq = nullptr);
+                                const XPrep* xq = nullptr);
+hipError_t launch_route_topk(const float* logits, int T, int E, int k,
+                             int renorm, int32_t* ids, float* w, hipStream_t st,
+                             const XPrep* xp = nullptr);
 // Rows [R][C] (row stride ld) to int8 rows of stride ldq and fp32 scales.
 hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
                            int8_t* q, int ldq, float* s, hipStream_t st);

@@ -582,20 +582,6 @@ void proj_mfma8_kernel(ProjArgs a, const uint16_t* x16) {
   else tile<MODE, 2, PP>(a, t, As, tok);
 }
 
-// fp16 copy of bf16 rows, every 8-block in the order (0,4)(1,5)(2,6)(3,7)
-// (the unpack order of int4, and of int2 after its byte reorder).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t lo_bf16, uint32_t hi_bf16) {
-  const float x0 = __uint_as_float(lo_bf16 << 16);
-  const float x1 = __uint_as_float(hi_bf16 << 16);
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-}
-__device__ __forceinline__ uint4 convert8(uint4 v) {
-  const uint32_t e[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                         v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-  return make_uint4(bf16x2_to_f16x2(e[0], e[4]), bf16x2_to_f16x2(e[1], e[5]),
-                    bf16x2_to_f16x2(e[2], e[6]), bf16x2_to_f16x2(e[3], e[7]));
-}
-
 // rows [R][ld] bf16 -> fp16 in the unpack order: the first K columns of
 // every row (K % 8 == 0), one 8-block per thread.
 __global__ __launch_bounds__(256) void convert8_kernel(const uint16_t* __restrict__ src,
@@ -626,8 +612,9 @@ hipError_t launch_proj_mfma8(const ProjArgs& a_in, uint16_t* a16, bool prepacked
   const long long blocks = groups * kXcd * a.n_rb;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  // one fp16 copy of the activations in the unpack's K order
-  if (a.mode == 0) {
+  // one fp16 copy of the activations in the unpack's K order (gate/up:
+  // unless the routing launch made it, a.in16_ready)
+  if (a.mode == 0 && !a.in16_ready) {
     const long long units = (long long)a.T * (a.K / 8);
     convert8_kernel<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(a.in_bf16, a.T, a.K,
                                                                      a.K, a16);

@@ -16,7 +16,7 @@ namespace moe {
 // the row quantizer's a8_scale / a8_code, so the codes equal that launch's.
 // 16-byte loads of 8 values; the second pass reloads them (cache hits).
 template <int THREADS>
-__device__ void quant_x_row(const XQuant& xq, int t) {
+__device__ void quant_x_row(const XPrep& xq, int t) {
   __shared__ float red[THREADS / 64];
   const int tid = threadIdx.x;
   const uint16_t* row = xq.x + (size_t)t * xq.H;
@@ -54,15 +54,51 @@ __device__ void quant_x_row(const XQuant& xq, int t) {
   if (tid == 0) xq.s[t] = sc;
 }
 
+// The fp16 copy of x in the unpack order (what the matrix-core gate/up
+// stages), by workgroup b of nb workgroups of THREADS threads, the same
+// conversion as that path's own.  A thread takes 8-value blocks u, u + S,
+// ... (S = nb * THREADS) eight at a time: the eight loads are issued
+// before the first store, so the copy streams instead of waiting one
+// memory latency per block.
+template <int THREADS>
+__device__ void convert_x_rows(const XPrep& xp, int T, int b, int nb) {
+  const long long units = (long long)T * (xp.H / 8);   // x rows are contiguous
+  const long long S = (long long)nb * THREADS;
+  const uint4* src = reinterpret_cast<const uint4*>(xp.x);
+  uint4* dst = reinterpret_cast<uint4*>(xp.x16);
+  for (long long u0 = (long long)b * THREADS + threadIdx.x; u0 < units; u0 += 8 * S) {
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (u0 + i * S < units) v[i] = src[u0 + i * S];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (u0 + i * S < units) dst[u0 + i * S] = convert8(v[i]);
+  }
+}
+
+// The preparing workgroups of a routing launch: b of nb.
+template <int THREADS>
+__device__ void prep_x(const XPrep& xp, int T, int b, int nb) {
+  if (xp.q) quant_x_row<THREADS>(xp, b);
+  else convert_x_rows<THREADS>(xp, T, b, nb);
+}
+
+int xprep_convert_blocks(int T, int H) {
+  const long long units = (long long)T * (H / 8);
+  const long long nb = (units + 256 * 8 - 1) / (256 * 8);   // about 8 blocks per thread
+  return (int)(nb < 1 ? 1 : nb > 1024 ? 1024 : nb);
+}
+
 // Workgroups [0, nrb) route, 16 tokens each: four per wave (one per row of
-// 16 lanes, or one after another for E > 256); with xq.x set, workgroup
-// nrb + t quantizes row t of x.
+// 16 lanes, or one after another for E > 256); the workgroups after them
+// prepare x (xp: int8 rows, one workgroup per row, or the fp16 copy).
 template <int NV>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm,
-    int32_t* __restrict__ ids, float* __restrict__ w, int nrb, XQuant xq) {
+    int32_t* __restrict__ ids, float* __restrict__ w, int nrb, XPrep xp) {
   if ((int)blockIdx.x >= nrb) {
-    quant_x_row<256>(xq, blockIdx.x - nrb);
+    prep_x<256>(xp, T, blockIdx.x - nrb, gridDim.x - nrb);
     return;
   }
   route_tokens<NV, 1>(logits, T, E, k, renorm, threadIdx.x & 63,
@@ -347,9 +383,9 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(
     int tile_m, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, XQuant xq) {
-  if (blockIdx.x > 0) {   // with xq.x set: workgroup 1 + t quantizes row t of x
-    quant_x_row<1024>(xq, blockIdx.x - 1);
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, XPrep xp) {
+  if (blockIdx.x > 0) {   // the workgroups after the first prepare x
+    prep_x<1024>(xp, T, blockIdx.x - 1, gridDim.x - 1);
     return;
   }
   __shared__ PermSmem sm;
@@ -519,12 +555,13 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const float* W,
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k,
                              int renorm, int32_t* ids, float* w,
-                             hipStream_t st) {
+                             hipStream_t st, const XPrep* xp) {
   if (T == 0) return hipSuccess;
   const int nrb = (T + 15) / 16;
-  const XQuant none = {nullptr, 0, nullptr, nullptr};
-  MOE_NV_DISPATCH(NV, route_topk_kernel<NV><<<nrb, 256, 0, st>>>(
-                          logits, T, E, k, renorm, ids, w, nrb, none));
+  const XPrep p = xp ? *xp : XPrep{nullptr, 0, nullptr, nullptr, nullptr};
+  const int np = !xp ? 0 : p.q ? T : xprep_convert_blocks(T, p.H);
+  MOE_NV_DISPATCH(NV, route_topk_kernel<NV><<<nrb + np, 256, 0, st>>>(
+                          logits, T, E, k, renorm, ids, w, nrb, p));
   return hipGetLastError();
 }
 
@@ -559,20 +596,19 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k,
                                 int32_t* counts, int32_t* offsets,
                                 int32_t* sorted_pair, int32_t* pair_pos,
                                 int32_t* tiles, int32_t* n_tiles,
-                                hipStream_t st, const XQuant* xq) {
-  const XQuant q = xq ? *xq : XQuant{nullptr, 0, nullptr, nullptr};
-  const int nq = xq ? T : 0;   // quantizing workgroups, one per row of x
+                                hipStream_t st, const XPrep* xq) {
   // from 16 tokens on the routing is worth more than one compute unit: the
   // multi-workgroup router, then the sort (same functions, same results)
   if (T >= kRouteRowMinT) {
-    const int nrb = (T + 15) / 16;
-    MOE_NV_DISPATCH(NV, route_topk_kernel<NV><<<nrb + nq, 256, 0, st>>>(
-                            logits, T, E, k, renorm, ids, w, nrb, q));
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_route_topk(logits, T, E, k, renorm, ids, w, st, xq);
     if (e != hipSuccess) return e;
     return launch_permute(ids, T * k, E, tile_m, counts, offsets, sorted_pair, pair_pos, tiles,
                           n_tiles, st);
   }
+  const XPrep q = xq ? *xq : XPrep{nullptr, 0, nullptr, nullptr, nullptr};
+  // preparing workgroups of 1024 threads: one per row (int8), or the
+  // fp16 copy at about 8 blocks per thread
+  const int nq = !xq ? 0 : q.q ? T : (xprep_convert_blocks(T, q.H) + 3) / 4;
   MOE_NV_DISPATCH(NV, route_permute_kernel<NV><<<1 + nq, 1024, 0, st>>>(
                           logits, T, E, k, renorm, tile_m, ids, w, counts,
                           offsets, sorted_pair, pair_pos, tiles, n_tiles, q));

@@ -136,7 +136,7 @@ def test_gateup_validation():
     assert _gateup(workspace=FAKE + 64) == L.MOE_E_WORKSPACE  # 256-byte alignment
     assert _gateup(flags=8) == L.MOE_E_INVAL
     assert _gateup(flags=128) == L.MOE_E_INVAL
-    assert _gateup(flags=L.MOE_X_QUANTIZED, act=1) == L.MOE_E_DEVICE
+    assert _gateup(flags=L.MOE_X_PREPARED, act=1) == L.MOE_E_DEVICE
     assert _gateup(flags=L.MOE_QUANT_SEPARATE | L.MOE_PATH_MFMA16, act=1) == L.MOE_E_DEVICE
     # forced 16-row MFMA tiles: tiles of at most 16 rows, activations in LDS
     assert _gateup(flags=L.MOE_PATH_MFMA16, tile_m=32) == L.MOE_E_UNSUPPORTED

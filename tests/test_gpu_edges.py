@@ -147,7 +147,7 @@ def test_int8_rows_of_every_maker_match_row_quantizer_on_edge_rows(name):
 
 @pytest.mark.parametrize("name", ["mixed_shared_a8", "c3_t16"])
 def test_gateup_reads_int8_rows_left_by_the_layer_call(name):
-    """MOE_X_QUANTIZED: after a W4A8 layer call the workspace holds x's int8
+    """MOE_X_PREPARED: after a W4A8 layer call the workspace holds x's int8
     rows; a gate/up call that reads them writes the same h as the layer."""
     from packed_bit_grouped_amd import _lib as L
     from packed_bit_grouped_amd.layer import DeviceLayer
@@ -160,7 +160,7 @@ def test_gateup_reads_int8_rows_left_by_the_layer_call(name):
     L.moe_w4_gateup_silu(B.act, dl.x, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dl.bank.w13,
                          dl.bank.w13_sh, cfg.n_shared, cfg.I_shared, B.offsets,
                          B.sorted_pair, B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes,
-                         L.MOE_X_QUANTIZED)
+                         L.MOE_X_PREPARED)
     torch.cuda.synchronize()
     h = B.h.cpu().numpy()[:B.R].astype(np.float32)
     assert np.array_equal(h, g1["h32"])

@@ -759,11 +759,12 @@ BIG_SORT = LayerConfig("mfma_big_sort", 214, T=1100, H=256, E=40, k=8, I=128, gr
 
 @pytest.mark.parametrize("name", ["mfma_mixed", "gated_mfma", "big_sort", "prefill"])
 def test_layer_call_matches_separate_calls_on_matrix_cores(name):
-    """moe_w4_layer on the matrix-core path (its gate/up epilogue writes the
-    fp16 h rows the down projection reads; from 8192 pairs the sort runs
-    over many workgroups with its counts in the workspace) gives the same
-    routing tables, h and output bits as the separate calls (one-workgroup
-    sort, fp16 h made by a conversion pass)."""
+    """moe_w4_layer on the matrix-core path (its routing launch makes the fp16
+    copy of x, its gate/up epilogue writes the fp16 h rows the down
+    projection reads; from 8192 pairs the sort runs over many workgroups
+    with its counts in the workspace) gives the same routing tables, h and
+    output bits as the separate calls (one-workgroup sort, fp16 x and h made
+    by conversion passes)."""
     cfg = {"mfma_mixed": MFMA["mfma_mixed"], "gated_mfma": GATED["gated_mfma"],
            "big_sort": BIG_SORT, "prefill": LAYERS["prefill_mixed_t4096"]}[name]
     dl = _dev(cfg)
@@ -778,6 +779,26 @@ def test_layer_call_matches_separate_calls_on_matrix_cores(name):
         _check_integer_stages(g1, o, cfg)
         g32, _ = run_layer_gpu(dl, "a16", 160, out_f32=True)
         check_out(g1, g32, o["out"], "big sort")
+
+
+def test_gateup_reads_fp16_copy_left_by_the_layer_call():
+    """MOE_X_PREPARED on the matrix-core path: the routing launch of the
+    layer call leaves the fp16 copy of x in the workspace; a gate/up call
+    that reads it (no conversion of its own) writes the layer's h bits."""
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    cfg = MFMA["mfma_mixed"]
+    dl = _dev(cfg)
+    g1, B = run_layer_gpu(dl, "a16", 160)
+    B.h.zero_()
+    L.moe_w4_gateup_silu(B.act, dl.x, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dl.bank.w13,
+                         dl.bank.w13_sh, cfg.n_shared, cfg.I_shared, B.offsets,
+                         B.sorted_pair, B.tiles, B.n_tiles, B.tile_m, B.h, B.ws, B.ws_bytes,
+                         L.MOE_X_PREPARED)
+    torch.cuda.synchronize()
+    g2 = collect(B)
+    assert np.array_equal(g1["h"], g2["h"])
+    assert g2["err"] == 0
 
 
 @pytest.mark.parametrize("name", ["c1", "c3", "mixed_shared"])
