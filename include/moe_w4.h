@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOE_W4_ABI_VERSION 2
+#define MOE_W4_ABI_VERSION 3
 
 /* Version of the compiled library.  The Python binding refuses to load a
  * library whose version differs from the header it was written for. */
@@ -251,9 +251,10 @@ size_t moe_workspace_bytes(int act, int T, int H, int I, int E, int k,
                               /* layer where the shape allows it (same      */
                               /* results as the two calls)                  */
 #define MOE_W_PREPACKED 32    /* the weight tables' codes are in the layout */
-                              /* of moe_w4_prepack (scales unchanged); read */
-                              /* by the matrix-core path only: any other    */
-                              /* path returns MOE_E_UNSUPPORTED             */
+                              /* of moe_w4_prepack and their scales in that */
+                              /* of moe_w4_prepack_scales; read by the      */
+                              /* matrix-core path only: any other path      */
+                              /* returns MOE_E_UNSUPPORTED                  */
 #define MOE_OUT_F32 16        /* moe_w4_down_combine / moe_w4_layer: out is */
                               /* fp32 [T][H] (16-byte aligned) holding the  */
                               /* combined sum before any rounding to bf16;  */
@@ -283,13 +284,32 @@ int moe_preferred_tile_m(int act, int T, int E, int k);
  * with every 4-byte word's bytes in the order (0, 2, 1, 3).  Down: piece
  * (b, s) = rows 32b + c at step s, in order b, s.  Gate/up: pieces (b, s,
  * p) in order b, s, p, p = 0 the gate rows 32b + c and p = 1 the up rows
- * I + 32b + c.  The fp16 scales are not changed: a prepacked descriptor
- * keeps the matrix's scale array.
+ * I + 32b + c.  The scales are re-tiled by moe_w4_prepack_scales.
  * Limits: N % 32 == 0 (gate/up: N % 64 == 0), K % 128 == 0.  Errors: MOE_E_INVAL,
  * MOE_E_UNSUPPORTED, MOE_E_DEVICE.  Asynchronous on `stream`.
  * ------------------------------------------------------------------- */
 moe_status moe_w4_prepack(const uint8_t* codes, int bits, int N, int K, int gate_up,
                           uint8_t* dst, void* stream);
+
+/* ---------------------------------------------------------------------
+ * moe_w4_prepack_scales -- the fp16 group scales of one matrix re-tiled for
+ * the matrix-core path next to moe_w4_prepack's codes (same build log and
+ * section): a wave then reads the scales of its 32 row pairs for one group
+ * as one 128-byte run instead of 64 rows' scattered 2-byte values.
+ *   scales  canonical scales [N][K/group] (moe_qmat layout), device
+ *   group   32, 64, 128 or 256 (K % group == 0)
+ *   gate_up 1 for a gate/up matrix [2I][H], 0 for a down matrix [H][I]
+ *   dst     device, N*(K/group)*2 bytes (the same size), 4-byte aligned,
+ *           not overlapping scales
+ * Layout of dst: 4-byte words ((b * ng + g) * 32 + c), ng = K/group, each
+ * the scale of group g of row r0 (low half) and of row r1 (high half):
+ * gate/up r0 = 32b + c (gate), r1 = N/2 + 32b + c (up); down r0 = 64b + c,
+ * r1 = 64b + 32 + c.
+ * Limits: N % 64 == 0.  Errors: MOE_E_INVAL, MOE_E_UNSUPPORTED,
+ * MOE_E_DEVICE.  Asynchronous on `stream`.
+ * ------------------------------------------------------------------- */
+moe_status moe_w4_prepack_scales(const uint16_t* scales, int N, int K, int group, int gate_up,
+                                 uint16_t* dst, void* stream);
 
 /* ---------------------------------------------------------------------
  * moe_w4_gateup_silu -- grouped gate/up projection of every routed pair

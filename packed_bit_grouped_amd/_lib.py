@@ -14,7 +14,7 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_DEVICE, MOE_E_WORKSPACE = 0, -1, -2, -3, -4
 MOE_A16, MOE_A8 = 0, 1
@@ -76,6 +76,8 @@ _SIGS = {
                              c_int, c_void_p]),
     "moe_read_stream": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
     "moe_w4_prepack": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
+    "moe_w4_prepack_scales": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p,
+                                      c_void_p]),
     "moe_w4_layer_noalloc": (c_int, [c_int, c_void_p, c_void_p, c_int, c_int, c_int,
                                      c_int, c_int, c_int, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_int, c_int, c_void_p, c_int, c_void_p,
@@ -278,6 +280,11 @@ def moe_w4_layer(act, logits, x, T, H, I, E, k, renormalize, w13, w2, w13_shared
 
 def moe_w4_prepack(codes, bits, N, K, gate_up, dst, stream=None, check=True):
     return _call("moe_w4_prepack", _ptr(codes), bits, N, K, gate_up, _ptr(dst),
+                 _stream(stream), check=check)
+
+
+def moe_w4_prepack_scales(scales, N, K, group, gate_up, dst, stream=None, check=True):
+    return _call("moe_w4_prepack_scales", _ptr(scales), N, K, group, gate_up, _ptr(dst),
                  _stream(stream), check=check)
 
 

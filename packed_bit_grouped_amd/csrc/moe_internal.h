@@ -131,6 +131,9 @@ hipError_t launch_proj_mfma8(const ProjArgs& a, uint16_t* a16, bool prepacked, h
 // (N % 32 == 0, K % 64 == 0); gate_up pairs gate rows with up rows.
 hipError_t launch_prepack(const uint8_t* src, int bits, int N, int K, int gate_up, uint8_t* dst,
                           hipStream_t st);
+// Scales in the prepacked layout (moe_w4_prepack_scales), ng groups per row.
+hipError_t launch_prepack_scales(const uint16_t* src, int N, int ng, int gate_up, uint16_t* dst,
+                                 hipStream_t st);
 bool mfma_available();
 // Decode-shape A16 projections (proj_decode.hip): tiles of at most 16
 // rows, H <= 2048 (gate/up) and I <= 1024 (down), down with the combine

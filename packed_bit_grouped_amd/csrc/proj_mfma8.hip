@@ -143,7 +143,8 @@ struct Lane {
   __amdgpu_buffer_rsrc_t crs, srs;
   int coff[2];             // code byte offset of step 0 (+ step * cstride)
   int cstride;             // code bytes per step
-  int soff[2];             // scale byte offset of the row's group 0
+  int soff[2];             // scale byte offset of the row's group 0 (prepacked:
+                           // soff[0], both parts' scales in one word)
   int wrow[2];             // output column (gate/up: the unit; down: the row)
   bool wval[2];
   int n_st, gsh;
@@ -177,7 +178,8 @@ __device__ __forceinline__ u32x4_v bf16x8_to_f16_unpack(u32x4_v v) {
 template <int BITS>
 struct BReg {
   uint32_t c[2][BITS];     // per part 16 (int4) or 8 (int2) bytes
-  uint32_t s[2];           // fp16 scale bits
+  uint32_t s[2];           // fp16 scale bits (prepacked: s[0] holds part 0 in
+                           // its low half and part 1 in its high half)
 };
 
 // Wait until at most N vector-memory operations of this wave are in flight
@@ -225,20 +227,27 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
       }
     }
     const int gi = (st * kKS + kh * 32) >> ln_.gsh;
+    if constexpr (PP) {
+      // both parts' scales of the lane's row pair: one word of 128 bytes
+      // per (block, group), so the wave's load covers two cache lines
+      b.s[0] = __builtin_amdgcn_raw_buffer_load_b32(ln_.srs, ln_.soff[0] + gi * 128, 0, 0);
+      b.s[1] = 0u;
+    } else {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      b.s[p] = __builtin_amdgcn_raw_buffer_load_b16(ln_.srs, ln_.soff[p] + gi * 2, 0, 0);
+      for (int p = 0; p < 2; ++p)
+        b.s[p] = __builtin_amdgcn_raw_buffer_load_b16(ln_.srs, ln_.soff[p] + gi * 2, 0, 0);
     }
   };
   // the weight ring is issued first (it needs only the descriptor), then
   // the chunk's activation rows are read and published in LDS
-  constexpr int kStepLoads = MBT + 4;
+  constexpr int kBLoads = PP ? 3 : 4;   // code and scale loads per step
+  constexpr int kStepLoads = MBT + kBLoads;
   // Loads issued after A(s + 2) by the end of step s: from step 3 on, the
   // weight and scale loads of its own step and three whole steps (at least
   // (kAD - 2) whole steps, counted without the former); in steps 0 and 1,
   // whose A(s + 2) the prologue issued (after the weight ring), the
   // prologue's later activation loads and the steps so far:
-  // (kAD - 2) * MBT + 4 (s + 1).  The prologue's barrier waits for A(1):
+  // (kAD - 2) * MBT + kBLoads (s + 1).  The prologue's barrier waits for A(1):
   // A(2) .. A(kAD - 1) come after it.
   constexpr int kWaitSteady = (kAD - 2) * kStepLoads;
   constexpr int kWaitFirst = (kAD - 2) * MBT;
@@ -298,7 +307,8 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     const uint32_t m16 = stg < n_st ? 0x10001u : 0u;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const f16x2_v s2 = as_h2(b.s[p] * m16);
+      const uint32_t sv = PP ? (p ? b.s[0] >> 16 : b.s[0] & 0xFFFFu) : b.s[p];
+      const f16x2_v s2 = as_h2(sv * m16);
       if constexpr (BITS == 4) bq[p] = deq_int4(b.c[p][ks], s2);
       else if ((ks & 1) == 0) bq[p] = deq_int2<0>(b.c[p][ks >> 1], s2);
       else bq[p] = deq_int2<1>(b.c[p][ks >> 1], s2);
@@ -337,7 +347,7 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
       }
       // issue order: the LDS reads, then the MFMAs with the loads (one per
       // MFMA) and the dequantization between them
-      const int kLd = ks == 1 ? MBT : ks == 3 ? 4 : 0;
+      const int kLd = ks == 1 ? MBT : ks == 3 ? kBLoads : 0;
       __builtin_amdgcn_sched_group_barrier(0x100, MBT, 0);
 #pragma unroll
       for (int i = 0; i < 2 * MBT; ++i) {
@@ -370,7 +380,7 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     const int db = buf + kAD >= kABufs ? buf + kAD - kABufs : buf + kAD; \
     step(buf, nb, BC, BN, base + J, base + J + kAD, db);      \
     if (J < 2 && base == 0)                                   \
-      vm_barrier<(kAD - 2) * MBT + 4 * (J + 1)>();            \
+      vm_barrier<(kAD - 2) * MBT + kBLoads * (J + 1)>();      \
     else                                                      \
       vm_barrier<kWaitSteady>();                              \
     buf = nb;                                                 \
@@ -484,6 +494,13 @@ __device__ __forceinline__ void tile(const ProjArgs& a, const Tile& t, u32x4_v* 
   L.srs = make_rsrc(t.scales, (uint32_t)((size_t)n_wrows * ng * 2));
 #pragma unroll
   for (int p = 0; p < 2; ++p) L.soff[p] = (L.wval[p] ? brow[p] : 0) * ng * 2;
+  if (PP) {
+    // prepacked scales: [block][group][32 rows][2 parts] fp16, a block being
+    // a gate/up unit block of 32 (gate, up) or a down pair of 32-row blocks
+    const int sblk = MODE == 0 ? t.u0 / 32 + n : (t.u0 + 64 * n) / 64;
+    L.soff[0] = L.wval[0] ? sblk * ng * 128 + lc * 4 : 0;
+    L.soff[1] = 0;
+  }
   constexpr int kLaneBytes = kKS * BITS / 16;   // per lane half and step
   if (PP) {
     // gate/up: [unit block of 32][step][gate, up][64 lane slots]; down:
@@ -678,7 +695,34 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
   }
 }
 
+// One 4-byte word of the prepacked scales per thread: word u = (b * ng + g)
+// * 32 + c holds group g of rows r0 (low half) and r1 (high half), gate/up
+// r0 = 32b + c, r1 = N/2 + 32b + c; down r0 = 64b + c, r1 = 64b + 32 + c.
+__global__ __launch_bounds__(256) void prepack_scales_kernel(const uint16_t* __restrict__ src,
+                                                             int N, int ng, int gate_up,
+                                                             uint32_t* __restrict__ dst) {
+  const long long words = (long long)(N / 2) * ng;
+  const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (u >= words) return;
+  const int c = (int)(u & 31);
+  const long long bg = u >> 5;
+  const int g = (int)(bg % ng);
+  const int b = (int)(bg / ng);
+  const int r0 = gate_up ? 32 * b + c : 64 * b + c;
+  const int r1 = gate_up ? N / 2 + 32 * b + c : 64 * b + 32 + c;
+  dst[u] = (uint32_t)src[(size_t)r0 * ng + g] | ((uint32_t)src[(size_t)r1 * ng + g] << 16);
+}
+
 }  // namespace
+
+hipError_t launch_prepack_scales(const uint16_t* src, int N, int ng, int gate_up, uint16_t* dst,
+                                 hipStream_t st) {
+  const long long words = (long long)(N / 2) * ng;
+  if (words <= 0) return hipSuccess;
+  prepack_scales_kernel<<<(unsigned)((words + 255) / 256), 256, 0, st>>>(
+      src, N, ng, gate_up, reinterpret_cast<uint32_t*>(dst));
+  return hipGetLastError();
+}
 
 hipError_t launch_prepack(const uint8_t* src, int bits, int N, int K, int gate_up, uint8_t* dst,
                           hipStream_t st) {

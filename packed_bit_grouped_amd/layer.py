@@ -52,13 +52,14 @@ class Bank:
 
     def prepack(self) -> "Bank":
         """A copy of the bank with every code matrix re-tiled by
-        moe_w4_prepack (scales shared in layout, copied with the buffer);
-        calls on it need MOE_W_PREPACKED (run_layer adds it)."""
+        moe_w4_prepack and its scales by moe_w4_prepack_scales; calls on it
+        need MOE_W_PREPACKED (run_layer adds it)."""
         buf = self.buf.clone()
         base, dst = self.buf.data_ptr(), buf.data_ptr()
         for tag, oc, os_, (bits, group, N, K) in self.layout:
-            L.moe_w4_prepack(base + oc, bits, N, K, 1 if tag in ("w13", "w13_sh") else 0,
-                             dst + oc)
+            gu = 1 if tag in ("w13", "w13_sh") else 0
+            L.moe_w4_prepack(base + oc, bits, N, K, gu, dst + oc)
+            L.moe_w4_prepack_scales(base + os_, N, K, group, gu, dst + os_)
         b = self.rebased(buf)
         b.prepacked = True
         return b

@@ -313,3 +313,22 @@ def test_prepack_validation():
     assert call(dst=None) == L.MOE_E_INVAL
     assert call(codes=FAKE + 8) == L.MOE_E_INVAL   # 16-byte aligned
     assert call() == L.MOE_E_DEVICE
+
+
+def test_prepack_scales_validation():
+    ok = dict(scales=FAKE, N=256, K=512, group=128, gate_up=1, dst=FAKE + 4096)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.moe_w4_prepack_scales(*a.values(), stream=0, check=False)
+    assert call(group=16) == L.MOE_E_UNSUPPORTED
+    assert call(K=448) == L.MOE_E_UNSUPPORTED      # K % group
+    assert call(N=96) == L.MOE_E_UNSUPPORTED       # pairs of 32-row blocks
+    assert call(N=96, gate_up=0) == L.MOE_E_UNSUPPORTED
+    assert call(gate_up=2) == L.MOE_E_INVAL
+    assert call(N=0) == L.MOE_E_INVAL
+    assert call(dst=FAKE) == L.MOE_E_INVAL         # in place
+    assert call(dst=None) == L.MOE_E_INVAL
+    assert call(scales=FAKE + 2) == L.MOE_E_INVAL  # 4-byte aligned
+    assert call() == L.MOE_E_DEVICE
+    assert call(gate_up=0, group=32) == L.MOE_E_DEVICE
