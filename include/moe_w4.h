@@ -299,14 +299,16 @@ moe_status moe_w4_prepack(const uint8_t* codes, int bits, int N, int K, int gate
  *   scales  canonical scales [N][K/group] (moe_qmat layout), device
  *   group   32, 64, 128 or 256 (K % group == 0)
  *   gate_up 1 for a gate/up matrix [2I][H], 0 for a down matrix [H][I]
- *   dst     device, N*(K/group)*2 bytes (the same size), 4-byte aligned,
+ *   dst     device, N*(K/group)*2 bytes (the same size), 16-byte aligned,
  *           not overlapping scales
  * Layout of dst: 4-byte words ((b * ng + g) * 32 + c), ng = K/group, each
  * the scale of group g of row r0 (low half) and of row r1 (high half):
  * gate/up r0 = 32b + c (gate), r1 = N/2 + 32b + c (up); down r0 = 64b + c,
  * r1 = 64b + 32 + c.
- * Limits: N % 64 == 0.  Errors: MOE_E_INVAL, MOE_E_UNSUPPORTED,
- * MOE_E_DEVICE.  Asynchronous on `stream`.
+ * The matrix-core kernel copies a wave's block of words into LDS once per
+ * tile, so a prepacked matrix has at most 64 groups per row.
+ * Limits: N % 64 == 0, K / group <= 64.  Errors: MOE_E_INVAL,
+ * MOE_E_UNSUPPORTED, MOE_E_DEVICE.  Asynchronous on `stream`.
  * ------------------------------------------------------------------- */
 moe_status moe_w4_prepack_scales(const uint16_t* scales, int N, int K, int group, int gate_up,
                                  uint16_t* dst, void* stream);

@@ -673,10 +673,10 @@ extern "C" moe_status moe_w4_prepack_scales(const uint16_t* scales, int N, int K
                                             int gate_up, uint16_t* dst, void* stream) {
   if (N <= 0 || K <= 0 || (gate_up != 0 && gate_up != 1)) return MOE_E_INVAL;
   if (group != 32 && group != 64 && group != 128 && group != 256) return MOE_E_UNSUPPORTED;
-  if (K % group != 0 || N % 64 != 0) return MOE_E_UNSUPPORTED;
+  if (K % group != 0 || N % 64 != 0 || K / group > 64) return MOE_E_UNSUPPORTED;
   if ((long long)N * (K / group) * 2 >= (1LL << 31)) return MOE_E_UNSUPPORTED;
   if (!scales || !dst || scales == dst) return MOE_E_INVAL;
-  if (!aligned(scales, 4) || !aligned(dst, 4)) return MOE_E_INVAL;
+  if (!aligned(scales, 4) || !aligned(dst, 16)) return MOE_E_INVAL;
   const moe_status d = check_device();
   if (d != MOE_OK) return d;
   return from_hip(launch_prepack_scales(scales, N, K / group, gate_up, dst,

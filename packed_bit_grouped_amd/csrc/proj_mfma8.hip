@@ -62,6 +62,7 @@ typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;       // 4 waves, one per SIMD
 constexpr int kUnits = 128;         // gate/up units per workgroup (shared-expert tile rows too)
 constexpr int kRowsMax = 160;       // activation rows per tile chunk (5 row blocks of 32)
+constexpr int kSclGroupsMax = 64;   // prepacked scales: groups per row staged in LDS
 constexpr int kRing = 8;            // weight steps in flight (registers)
 constexpr int kKS = 64;             // K per step
 constexpr int kChunks = kKS / 8;    // 16-byte fp16 chunks per row and step
@@ -146,6 +147,7 @@ struct Lane {
   int soff[2];             // scale byte offset of the row's group 0 (prepacked:
                            // soff[0], both parts' scales in one word)
   int wrow[2];             // output column (gate/up: the unit; down: the row)
+  const uint32_t* ss;      // prepacked: this wave's staged scale words + lane column
   bool wval[2];
   int n_st, gsh;
 };
@@ -211,7 +213,7 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
   const int lc = lane & 31, kh = lane >> 5;
   const int n_st = ln_.n_st;
 
-  auto load_b = [&](int st, BReg<BITS>& b) {
+  auto load_c = [&](int st, BReg<BITS>& b) {
     st = min(st, n_st - 1);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -226,11 +228,14 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
         b.c[p][1] = PP ? v.y : int2_order(v.y);
       }
     }
+  };
+  auto load_s = [&](int st, BReg<BITS>& b) {
+    st = min(st, n_st - 1);
     const int gi = (st * kKS + kh * 32) >> ln_.gsh;
     if constexpr (PP) {
-      // both parts' scales of the lane's row pair: one word of 128 bytes
-      // per (block, group), so the wave's load covers two cache lines
-      b.s[0] = __builtin_amdgcn_raw_buffer_load_b32(ln_.srs, ln_.soff[0] + gi * 128, 0, 0);
+      // both parts' scales of the lane's row pair, from the wave's copy of
+      // its block's scale words in LDS (32 words per group)
+      b.s[0] = ln_.ss[gi * 32];
       b.s[1] = 0u;
     } else {
 #pragma unroll
@@ -238,9 +243,13 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
         b.s[p] = __builtin_amdgcn_raw_buffer_load_b16(ln_.srs, ln_.soff[p] + gi * 2, 0, 0);
     }
   };
+  auto load_b = [&](int st, BReg<BITS>& b) {
+    load_c(st, b);
+    load_s(st, b);
+  };
   // the weight ring is issued first (it needs only the descriptor), then
   // the chunk's activation rows are read and published in LDS
-  constexpr int kBLoads = PP ? 3 : 4;   // code and scale loads per step
+  constexpr int kBLoads = PP ? 2 : 4;   // code and scale loads per step
   constexpr int kStepLoads = MBT + kBLoads;
   // Loads issued after A(s + 2) by the end of step s: from step 3 on, the
   // weight and scale loads of its own step and three whole steps (at least
@@ -261,8 +270,15 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     else r = t.is_sh ? a.P + t.e * a.T + mc + mm : mc + mm;
   }
   BReg<BITS> b0, b1, b2, b3, b4, b5, b6, b7;
-  load_b(0, b0); load_b(1, b1); load_b(2, b2); load_b(3, b3);
-  load_b(4, b4); load_b(5, b5); load_b(6, b6); load_b(7, b7);
+  if (PP) {
+    // codes only: the scale words of these steps are read from LDS after
+    // the prologue barrier, once their copy (issued before) has landed
+    load_c(0, b0); load_c(1, b1); load_c(2, b2); load_c(3, b3);
+    load_c(4, b4); load_c(5, b5); load_c(6, b6); load_c(7, b7);
+  } else {
+    load_b(0, b0); load_b(1, b1); load_b(2, b2); load_b(3, b3);
+    load_b(4, b4); load_b(5, b5); load_b(6, b6); load_b(7, b7);
+  }
   __syncthreads();   // previous chunk's readers of tok are done
   if (tid < kRowsMax) tok[tid] = (MODE == 0 && !t.is_sh) ? r / a.k : r;
   __syncthreads();
@@ -328,9 +344,15 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
   // every step.
   auto step = [&](int buf, int nbuf, BReg<BITS>& b, const BReg<BITS>& bn, int stg, int dst,
                   int dbuf) {
+    // prepacked: the scale word of step stg + kRing is read from LDS in
+    // sub-step 0 (b's own scale is still in use until sub-step 2) and moved
+    // into b with its codes in sub-step 3, so the read has landed long
+    // before the step's barrier waits for the LDS
+    BReg<BITS> sn;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int cur = ks & 1, nxt = cur ^ 1;
+      if (PP && ks == 0) load_s(stg + kRing, sn);
       if (ks < 3) {
         read_frags(buf, ks + 1, fr[nxt]);
         deq(b, ks + 1, stg, bq[nxt]);
@@ -339,7 +361,14 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
         deq(bn, 0, stg + 1, bq[nxt]);
       }
       if (ks == 1) dma_a(dst, dbuf);
-      if (ks == 3) load_b(stg + kRing, b);
+      if (ks == 3) {
+        if (PP) {
+          load_c(stg + kRing, b);
+          b.s[0] = sn.s[0];
+        } else {
+          load_b(stg + kRing, b);
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < MBT; ++mb) {
         acc[0][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[cur][mb], bq[cur][0], acc[0][mb], 0, 0, 0);
@@ -348,7 +377,8 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
       // issue order: the LDS reads, then the MFMAs with the loads (one per
       // MFMA) and the dequantization between them
       const int kLd = ks == 1 ? MBT : ks == 3 ? kBLoads : 0;
-      __builtin_amdgcn_sched_group_barrier(0x100, MBT, 0);
+      if (PP && ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, MBT + 1, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, MBT, 0);
 #pragma unroll
       for (int i = 0; i < 2 * MBT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -371,6 +401,10 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     dma_a(j, j);
   }
   vm_barrier<kWaitFirst>();
+  if (PP) {
+    load_s(0, b0); load_s(1, b1); load_s(2, b2); load_s(3, b3);
+    load_s(4, b4); load_s(5, b5); load_s(6, b6); load_s(7, b7);
+  }
   read_frags(0, 0, fr[0]);
   deq(b0, 0, 0, bq[0]);
   int buf = 0;
@@ -494,13 +528,9 @@ __device__ __forceinline__ void tile(const ProjArgs& a, const Tile& t, u32x4_v* 
   L.srs = make_rsrc(t.scales, (uint32_t)((size_t)n_wrows * ng * 2));
 #pragma unroll
   for (int p = 0; p < 2; ++p) L.soff[p] = (L.wval[p] ? brow[p] : 0) * ng * 2;
-  if (PP) {
-    // prepacked scales: [block][group][32 rows][2 parts] fp16, a block being
-    // a gate/up unit block of 32 (gate, up) or a down pair of 32-row blocks
-    const int sblk = MODE == 0 ? t.u0 / 32 + n : (t.u0 + 64 * n) / 64;
-    L.soff[0] = L.wval[0] ? sblk * ng * 128 + lc * 4 : 0;
-    L.soff[1] = 0;
-  }
+  // prepacked scales: [block][group][32 rows][2 parts] fp16, a block being
+  // a gate/up unit block of 32 (gate, up) or a down pair of 32-row blocks;
+  // staged in LDS below (soff unused)
   constexpr int kLaneBytes = kKS * BITS / 16;   // per lane half and step
   if (PP) {
     // gate/up: [unit block of 32][step][gate, up][64 lane slots]; down:
@@ -526,6 +556,21 @@ __device__ __forceinline__ void tile(const ProjArgs& a, const Tile& t, u32x4_v* 
     for (int p = 0; p < 2; ++p) L.coff[p] = (L.wval[p] ? brow[p] : 0) * row_bytes + kh * kLaneBytes;
   }
   L.gsh = 31 - __builtin_clz(t.group);
+  if (PP) {
+    // the wave's block of prepacked scale words ([group][32 rows][2 parts],
+    // ng * 128 bytes) into its LDS region once per tile, 1 KB per load;
+    // issued before every load of the chunks, so the first chunk's prologue
+    // barrier (it waits for an activation load issued later) covers them
+    uint32_t* sw = reinterpret_cast<uint32_t*>(As + kABufs * kABuf) + kRowsMax +
+                   n * (kSclGroupsMax * 32);
+    const int sblk = MODE == 0 ? t.u0 / 32 + n : (t.u0 + 64 * n) / 64;
+    const int nld = (ng * 128 + 1023) / 1024;
+    for (int i = 0; i < nld; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          L.srs, (__attribute__((address_space(3))) void*)(sw + 256 * i), 16,
+          lane * 16, sblk * ng * 128 + i * 1024, 0, 0);
+    L.ss = sw + lc;
+  }
 
   for (int mc = t.r_begin; mc < t.r_end; mc += kRowsMax) {
     const int nrows = min(kRowsMax, t.r_end - mc);
@@ -585,7 +630,9 @@ void proj_mfma8_kernel(ProjArgs a, const uint16_t* x16) {
   t.u0 = nb * (MODE == 0 ? kUnits : 2 * kUnits);
   if (t.u0 >= t.U) return;
   const moe_qmat q = t.is_sh ? a.w_sh[t.e] : a.w[t.e];
-  if (!qmat_usable(q, MODE == 0 ? 2 * t.U : t.U, t.K) || t.K % (2 * kKS) != 0) {
+  if (!qmat_usable(q, MODE == 0 ? 2 * t.U : t.U, t.K) || t.K % (2 * kKS) != 0 ||
+      (PP && (t.K / q.group > kSclGroupsMax ||
+              (reinterpret_cast<uintptr_t>(q.scales) & 15) != 0))) {
     if (tid == 0) atomicOr(a.err, 1);
     return;
   }
@@ -645,7 +692,9 @@ hipError_t launch_proj_mfma8(const ProjArgs& a_in, uint16_t* a16, bool prepacked
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)kABufs * kABuf * 16 + kRowsMax * sizeof(int);
+  // prepacked banks: the four waves' scale words after the row numbers
+  const size_t lds = (size_t)kABufs * kABuf * 16 + kRowsMax * sizeof(int) +
+                     (prepacked ? (size_t)4 * kSclGroupsMax * 32 * 4 : 0);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const dim3 g((unsigned)blocks), blk(kThreads);
   if (a.mode == 0) {

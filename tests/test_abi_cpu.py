@@ -330,5 +330,7 @@ def test_prepack_scales_validation():
     assert call(dst=FAKE) == L.MOE_E_INVAL         # in place
     assert call(dst=None) == L.MOE_E_INVAL
     assert call(scales=FAKE + 2) == L.MOE_E_INVAL  # 4-byte aligned
+    assert call(dst=FAKE + 4104) == L.MOE_E_INVAL  # 16-byte aligned
+    assert call(K=8192, group=64) == L.MOE_E_UNSUPPORTED   # more than 64 groups
     assert call() == L.MOE_E_DEVICE
     assert call(gate_up=0, group=32) == L.MOE_E_DEVICE
