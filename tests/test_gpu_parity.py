@@ -741,6 +741,67 @@ def test_prepacked_prefill_layer_matches_canonical():
     assert np.array_equal(g1["h"], g0["h"]) and np.array_equal(g1["out"], g0["out"])
 
 
+def _prepack_codes_ref(codes, bits, N, K, gate_up):
+    """The documented moe_w4_prepack layout, written out from its definition:
+    pieces of 64 lane slots, slot h*32 + c holding bytes [32 s + 16 h, +16)
+    (int4) or [16 s + 8 h, +8) (int2, each 4-byte word's bytes reordered
+    0, 2, 1, 3) of one row; down pieces (b, s) = rows 32b + c; gate/up pieces
+    (b, s, p): p = 0 gate rows 32b + c, p = 1 up rows N/2 + 32b + c."""
+    rb = K * bits // 8
+    w = 16 if bits == 4 else 8
+    rows = codes.reshape(N, rb)
+    n_st = K // 64
+    out = []
+    nblk = (N // 2 if gate_up else N) // 32
+    for blk in range(nblk):
+        for st in range(n_st):
+            for p in (range(2) if gate_up else range(1)):
+                for h in range(2):
+                    for c in range(32):
+                        r = (N // 2 if (gate_up and p) else 0) + 32 * blk + c
+                        piece = rows[r, st * 2 * w + h * w: st * 2 * w + h * w + w]
+                        if bits == 2:
+                            piece = piece.reshape(-1, 4)[:, [0, 2, 1, 3]].ravel()
+                        out.append(piece)
+    return np.concatenate(out)
+
+
+def _prepack_scales_ref(scales, N, ng, gate_up):
+    """The documented moe_w4_prepack_scales layout: word (b*ng + g)*32 + c =
+    scale of group g of row r0 (low half) and row r1 (high half)."""
+    s = scales.reshape(N, ng)
+    out = np.zeros((N // 64, ng, 32, 2), np.uint16)
+    for b in range(N // 64):
+        for c in range(32):
+            r0, r1 = (32 * b + c, N // 2 + 32 * b + c) if gate_up else (64 * b + c,
+                                                                        64 * b + 32 + c)
+            out[b, :, c, 0] = s[r0]
+            out[b, :, c, 1] = s[r1]
+    return out.ravel()
+
+
+@pytest.mark.parametrize("bits,group,gate_up", [(4, 128, 1), (4, 32, 0), (2, 64, 1),
+                                                (2, 256, 0)])
+def test_prepack_layouts_match_their_definitions(bits, group, gate_up):
+    """moe_w4_prepack and moe_w4_prepack_scales on random bytes against the
+    layouts the header defines, re-tiled here on the host."""
+    torch = torch_mod()
+    from packed_bit_grouped_amd import _lib as L
+    rng = np.random.default_rng(bits * 1000 + group + gate_up)
+    N, K = 192, 512
+    ng = K // group
+    codes = rng.integers(0, 256, size=N * K * bits // 8, dtype=np.uint8)
+    scales = rng.integers(0, 1 << 16, size=N * ng, dtype=np.uint16)
+    dc, ds = torch.from_numpy(codes).cuda(), torch.from_numpy(scales.view(np.int16)).cuda()
+    oc, os_ = torch.zeros_like(dc), torch.zeros_like(ds)
+    L.moe_w4_prepack(dc, bits, N, K, gate_up, oc)
+    L.moe_w4_prepack_scales(ds, N, K, group, gate_up, os_)
+    torch.cuda.synchronize()
+    assert np.array_equal(oc.cpu().numpy(), _prepack_codes_ref(codes, bits, N, K, gate_up))
+    assert np.array_equal(os_.cpu().numpy().view(np.uint16),
+                          _prepack_scales_ref(scales, N, ng, gate_up))
+
+
 def test_prepacked_bank_needs_the_matrix_core_path():
     from packed_bit_grouped_amd import _lib as L
     cfg = MINIS["mixed_shared"]
