@@ -130,10 +130,16 @@ __device__ __forceinline__ void route_group_vals(const float (&v)[NVV], int E, i
 }
 
 // Batches of at least this many tokens route one token per row of 16 lanes
-// (when E <= 256): four tokens per wave at once, for throughput; smaller
-// batches one token per wave, for latency.  Every routing kernel applies
-// the same rule, so their results agree bit for bit.
-constexpr int kRouteRowMinT = 16;
+// (when E <= 256): four tokens per wave at once; smaller batches one token
+// per wave.  A workgroup's waves share its CU's four SIMDs, so from five
+// tokens on (more token waves than SIMDs) the row form finishes first: at
+// 12 tokens in one workgroup the last of twelve token waves ended ~9.3 k
+// cycles after the start, three waves per SIMD of ~3 k each.  Every routing
+// kernel applies the same rule, so their results agree bit for bit.
+constexpr int kRouteRowMinT = 5;
+// From this many tokens the routing of moe_route_permute / the layer call
+// runs over several workgroups (16 tokens each), then the sort.
+constexpr int kRouteMultiMinT = 16;
 
 // Route tokens [0, T) with the waves w0, w0 + ws, ... of the caller (w0 =
 // this wave's index among the ws routing waves).  Each wave handles up to

@@ -375,8 +375,105 @@ __global__ __launch_bounds__(1024) void permute_kernel(
                n_tiles, sm);
 }
 
+// Stable counting sort of P <= 128 pairs by one wave (valid ids below
+// 2^kPermIdBits; lane l holds pairs l and l + 64): one radix pass over the
+// id bits with ballots gives, for each of a lane's pairs and each of the
+// two pair slots, the lanes whose id is smaller (lt) and equal (eq); a
+// pair's position is the number of pairs sorted before it (smaller id, or
+// equal id and smaller index), its rank in its expert the equal-id pairs
+// before it, a tile starts where that rank is a multiple of tile_m, and
+// the tile's index is the number of starts sorted before it.  Straight-line
+// mask arithmetic, the same outputs as permute_body (counts and offsets
+// per expert come from count_experts).
+template <int NV>
+__device__ void wave_sort128(const int32_t* ids, int P, int E, int tile_m,
+                             int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+                             int32_t* __restrict__ pair_pos, int32_t* __restrict__ tiles,
+                             int32_t* __restrict__ n_tiles) {
+  const int lane = threadIdx.x & 63;
+  const bool in0 = lane < P, in1 = lane + 64 < P;
+  const int e0 = in0 ? ids[lane] : 0, e1 = in1 ? ids[lane + 64] : 0;
+  const uint64_t v0 = __ballot(in0), v1 = __ballot(in1);
+  // [my pair][slot]
+  uint64_t eq00 = v0, eq01 = v1, eq10 = v0, eq11 = v1;
+  uint64_t lt00 = 0, lt01 = 0, lt10 = 0, lt11 = 0;
+  // ids below E <= 64 NV: the bits of 64 NV - 1
+  constexpr int kBits = NV <= 1 ? 6 : NV <= 2 ? 7 : NV <= 4 ? 8 : kPermIdBits;
+  static_assert(kBits <= kPermIdBits, "ids below 2^kPermIdBits");
+#pragma unroll
+  for (int b = kBits - 1; b >= 0; --b) {
+    const bool b0 = (e0 >> b) & 1, b1 = (e1 >> b) & 1;
+    const uint64_t o0 = __ballot(in0 && b0), o1 = __ballot(in1 && b1);
+    lt00 = b0 ? (lt00 | (eq00 & ~o0)) : lt00;
+    lt01 = b0 ? (lt01 | (eq01 & ~o1)) : lt01;
+    eq00 = b0 ? (eq00 & o0) : (eq00 & ~o0);
+    eq01 = b0 ? (eq01 & o1) : (eq01 & ~o1);
+    lt10 = b1 ? (lt10 | (eq10 & ~o0)) : lt10;
+    lt11 = b1 ? (lt11 | (eq11 & ~o1)) : lt11;
+    eq10 = b1 ? (eq10 & o0) : (eq10 & ~o0);
+    eq11 = b1 ? (eq11 & o1) : (eq11 & ~o1);
+  }
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;   // lanes < lane
+  // pair lane: same-id pairs before it are slot-0 lanes below; pair lane +
+  // 64: every same-id slot-0 pair and the slot-1 lanes below
+  const uint64_t ahead00 = lt00 | (eq00 & below), ahead01 = lt01;
+  const uint64_t ahead10 = lt10 | eq10, ahead11 = lt11 | (eq11 & below);
+  const int nlt0 = __popcll(lt00) + __popcll(lt01);
+  const int nlt1 = __popcll(lt10) + __popcll(lt11);
+  const int bef0 = __popcll(eq00 & below);
+  const int bef1 = __popcll(eq10) + __popcll(eq11 & below);
+  const int end0 = nlt0 + __popcll(eq00) + __popcll(eq01);
+  const int end1 = nlt1 + __popcll(eq10) + __popcll(eq11);
+  const int pos0 = nlt0 + bef0, pos1 = nlt1 + bef1;
+  const bool st0 = in0 && bef0 % tile_m == 0, st1 = in1 && bef1 % tile_m == 0;
+  const uint64_t s0 = __ballot(st0), s1 = __ballot(st1);
+  const int tix0 = __popcll(s0 & ahead00) + __popcll(s1 & ahead01);
+  const int tix1 = __popcll(s0 & ahead10) + __popcll(s1 & ahead11);
+  if (in0) {
+    sorted_pair[pos0] = lane;
+    pair_pos[lane] = pos0;
+  }
+  if (in1) {
+    sorted_pair[pos1] = lane + 64;
+    pair_pos[lane + 64] = pos1;
+  }
+  if (st0) reinterpret_cast<int4*>(tiles)[tix0] = make_int4(e0, pos0, min(pos0 + tile_m, end0), 0);
+  if (st1) reinterpret_cast<int4*>(tiles)[tix1] = make_int4(e1, pos1, min(pos1 + tile_m, end1), 0);
+  if (lane == 0) {
+    *n_tiles = __popcll(s0) + __popcll(s1);
+    offsets[E] = P;
+  }
+}
+
+// Per-expert pair counts and offsets (pairs of a smaller expert) of the
+// experts e = first, first + stride, ... by one thread each, reading the
+// P ids from LDS (every thread reads the same ids at a time: broadcasts),
+// eight 16-byte reads in flight per turn.  ids: 16-byte aligned, padded
+// with an id no expert has up to a multiple of 32.
+__device__ void count_experts(const int32_t* ids, int P, int E, int first, int stride,
+                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  const int4* v = reinterpret_cast<const int4*>(ids);
+  for (int ex = first; ex < E; ex += stride) {
+    int c = 0, o = 0;
+    for (int q = 0; q < P; q += 32) {
+      int4 r[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r[u] = v[q / 4 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        c += (r[u].x == ex) + (r[u].y == ex) + (r[u].z == ex) + (r[u].w == ex);
+        o += (r[u].x < ex) + (r[u].y < ex) + (r[u].z < ex) + (r[u].w < ex);
+      }
+    }
+    counts[ex] = c;
+    offsets[ex] = o;
+  }
+}
+
 // Route and permute in one launch for small batches: the 16 waves route
-// the tokens (ids kept in LDS as well), then the same workgroup sorts.
+// the tokens (ids kept in LDS as well), then the same workgroup sorts: up
+// to 128 pairs wave 0 alone (the other waves count the experts), more with
+// the block-wide sort.
 template <int NV>
 __global__ __launch_bounds__(1024) void route_permute_kernel(
     const float* __restrict__ logits, int T, int E, int k, int renorm,
@@ -389,12 +486,23 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(
     return;
   }
   __shared__ PermSmem sm;
-  __shared__ int32_t lds_ids[kFusedRouteMaxP];
+  __shared__ __align__(16) int32_t lds_ids[kFusedRouteMaxP];
   static_assert(kFusedRouteMaxT == 4 * kPermWaves, "one token per row of 16 lanes");
   route_tokens<NV, 1>(logits, T, E, k, renorm, threadIdx.x & 63, threadIdx.x >> 6, kPermWaves,
                       ids, w, lds_ids, nullptr);
   __syncthreads();
-  permute_body(lds_ids, T * k, E, tile_m, counts, offsets, sorted_pair, pair_pos,
+  const int P = T * k;
+  if (P <= 128) {
+    // ids past P read by the counting threads: an id no expert has
+    if (threadIdx.x >= P && threadIdx.x < 128) lds_ids[threadIdx.x] = 0x7fffffff;
+    __syncthreads();
+    if (threadIdx.x < 64)
+      wave_sort128<NV>(lds_ids, P, E, tile_m, offsets, sorted_pair, pair_pos, tiles, n_tiles);
+    else
+      count_experts(lds_ids, P, E, threadIdx.x - 64, 1024 - 64, counts, offsets);
+    return;
+  }
+  permute_body(lds_ids, P, E, tile_m, counts, offsets, sorted_pair, pair_pos,
                tiles, n_tiles, sm);
 }
 
@@ -599,7 +707,7 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k,
                                 hipStream_t st, const XPrep* xq) {
   // from 16 tokens on the routing is worth more than one compute unit: the
   // multi-workgroup router, then the sort (same functions, same results)
-  if (T >= kRouteRowMinT) {
+  if (T >= kRouteMultiMinT) {
     const hipError_t e = launch_route_topk(logits, T, E, k, renorm, ids, w, st, xq);
     if (e != hipSuccess) return e;
     return launch_permute(ids, T * k, E, tile_m, counts, offsets, sorted_pair, pair_pos, tiles,

@@ -287,7 +287,11 @@ def test_fused_route_permute_matches_separate_calls():
     rng = np.random.default_rng(5)
     for T, E, k, tile_m, renorm in [(1, 128, 8, 16, 1), (12, 128, 8, 16, 1),
                                     (64, 128, 8, 16, 1), (64, 512, 64, 3, 1),
-                                    (7, 288, 8, 1, 0), (33, 8, 8, 4096, 1)]:
+                                    (7, 288, 8, 1, 0), (33, 8, 8, 4096, 1),
+                                    # one-wave sort: up to 128 pairs, pairs in both
+                                    # lane slots, ragged tiles, E up to 512
+                                    (15, 64, 8, 5, 1), (9, 40, 14, 2, 0), (13, 512, 9, 7, 1),
+                                    (11, 16, 11, 3, 1), (8, 128, 16, 1, 1), (3, 6, 5, 4096, 0)]:
         lg = rng.standard_normal((T, E)).astype(np.float32)
         lg[:, 3::5] = lg[:, 1:2]
         d = torch.from_numpy(lg).cuda()
