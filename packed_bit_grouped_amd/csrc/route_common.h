@@ -67,18 +67,21 @@ __device__ __forceinline__ void route_group_vals(const float (&v)[NVV], int E, i
 #pragma unroll
   for (int j = 0; j < NVV; ++j) { sel_v[j] = 0.0f; sel_id[j] = 0; }
   for (int rr = 0; rr < k; ++rr) {
-    uint32_t hi = 0, lo = 0;
+    // the lane's best free candidate: a pairwise tree over its NVV keys
+    // (keys are unique, so the maximum is the same in any order; the tree
+    // is log2(NVV) dependent steps instead of NVV)
+    uint64_t cand[NVV];
 #pragma unroll
     for (int j = 0; j < NVV; ++j) {
       const bool free_j = !((taken >> j) & 1u);
-      const uint32_t chi = free_j ? key_hi[j] : 0u;
-      const uint32_t clo = free_j ? ~(uint32_t)(r + LANES * j) : 0u;
-      const uint64_t a = ((uint64_t)hi << 32) | lo, b = ((uint64_t)chi << 32) | clo;
-      if (b > a) {
-        hi = chi;
-        lo = clo;
-      }
+      cand[j] = free_j ? (((uint64_t)key_hi[j] << 32) | ~(uint32_t)(r + LANES * j)) : 0ull;
     }
+#pragma unroll
+    for (int wdt = 1; wdt < NVV; wdt *= 2)
+#pragma unroll
+      for (int j = 0; j + wdt < NVV; j += 2 * wdt)
+        cand[j] = cand[j + wdt] > cand[j] ? cand[j + wdt] : cand[j];
+    uint32_t hi = (uint32_t)(cand[0] >> 32), lo = (uint32_t)cand[0];
     key_max_step<kDppXor1>(hi, lo);
     key_max_step<kDppXor2>(hi, lo);
     key_max_step<kDppRowHalfMirror>(hi, lo);
