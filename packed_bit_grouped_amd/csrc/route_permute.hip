@@ -123,31 +123,53 @@ constexpr int kPermWaves = 16;
 
 struct PermSmem {
   int hist[kPermWaves * kPermMaxE];
-  int tmp[kPermWaves + 1];
+  int tmp[2 * (kPermWaves + 1)];
   int total_valid;
 };
 
-__device__ int block_exclusive_scan(int v, int* tmp /* kPermWaves + 1 */) {
+// Exclusive scans of two values over the workgroup's 16 waves at once:
+// shuffle scans inside each wave, then the 16 wave totals scanned by 16
+// lanes of wave 0 (integer sums: exact in any order).  tmp: 2 * (kPermWaves
+// + 1) ints; every thread of the workgroup calls it.
+__device__ int2 block_exclusive_scan2(int a, int b, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
+  int ia = a, ib = b;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < kPermWaves; ++i) {
-      const int c = tmp[i];
-      tmp[i] = run;
-      run += c;
+    const int oa = __shfl_up(ia, off), ob = __shfl_up(ib, off);
+    if (lane >= off) {
+      ia += oa;
+      ib += ob;
     }
-    tmp[kPermWaves] = run;
+  }
+  if (lane == 63) {
+    tmp[wave] = ia;
+    tmp[kPermWaves + 1 + wave] = ib;
   }
   __syncthreads();
-  const int r = tmp[wave] + incl - v;
+  if (wave == 0) {
+    const int ta = lane < kPermWaves ? tmp[lane] : 0;
+    const int tb = lane < kPermWaves ? tmp[kPermWaves + 1 + lane] : 0;
+    int sa = ta, sb = tb;
+#pragma unroll
+    for (int off = 1; off < kPermWaves; off <<= 1) {
+      const int oa = __shfl_up(sa, off), ob = __shfl_up(sb, off);
+      if (lane >= off) {
+        sa += oa;
+        sb += ob;
+      }
+    }
+    if (lane < kPermWaves) {
+      tmp[lane] = sa - ta;
+      tmp[kPermWaves + 1 + lane] = sb - tb;
+    }
+    if (lane == kPermWaves - 1) {
+      tmp[kPermWaves] = sa;
+      tmp[2 * kPermWaves + 1] = sb;
+    }
+  }
+  __syncthreads();
+  const int2 r = make_int2(tmp[wave] + ia - a, tmp[kPermWaves + 1 + wave] + ib - b);
   __syncthreads();
   return r;
 }
@@ -180,9 +202,9 @@ __device__ void permute_body(const int32_t* ids, int P, int E, int tile_m,
 #pragma unroll
     for (int w = 0; w < kPermWaves; ++w) cnt += wc[w];
   }
-  const int excl = block_exclusive_scan(cnt, sm.tmp);
   const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
-  const int texcl = block_exclusive_scan(ntile, sm.tmp);
+  const int2 sc = block_exclusive_scan2(cnt, ntile, sm.tmp);
+  const int excl = sc.x, texcl = sc.y;
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = excl;
@@ -276,7 +298,7 @@ __global__ __launch_bounds__(1024) void perm_place_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ tiles,
                                                           int32_t* __restrict__ n_tiles) {
   __shared__ int wh[kPermWaves * kPermMaxE];
-  __shared__ int tmp[kPermWaves + 1];
+  __shared__ int tmp[2 * (kPermWaves + 1)];
   __shared__ int total;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
@@ -304,10 +326,11 @@ __global__ __launch_bounds__(1024) void perm_place_kernel(const int32_t* __restr
       }
     }
   }
-  const int excl = block_exclusive_scan(cnt, tmp);
-  if (b == 0) {   // uniform in the workgroup: the scan's barriers are reached by all
-    const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
-    const int texcl = block_exclusive_scan(ntile, tmp);
+  const int ntile = tid < E ? (cnt + tile_m - 1) / tile_m : 0;
+  const int2 sc = block_exclusive_scan2(cnt, ntile, tmp);
+  const int excl = sc.x;
+  if (b == 0) {
+    const int texcl = sc.y;
     if (tid < E) {
       counts[tid] = cnt;
       offsets[tid] = excl;
