@@ -56,6 +56,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_v;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_v;
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
 
@@ -199,13 +200,23 @@ __device__ __forceinline__ void vm_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// K loop and epilogue of one chunk of up to 32 * MBT rows (tok[] holds
-// their activation rows): the wave's 64 weight rows against all of them.
-// Per step every wave issues the same loads in the same order (MBT
-// activation loads into LDS, two code loads, two scale loads), every load
-// unconditional (steps past the end re-read the last step with a zero
-// scale), so the number of loads issued after any given one is fixed.
-template <int MODE, int BITS, int MBT, bool PP>
+// K loop and epilogue of one chunk of up to 32 * MBT + 16 * HT rows (tok[]
+// holds their activation rows): the wave's 64 weight rows against all of
+// them.  Per step every wave issues the same loads in the same order
+// (MBT + HT activation loads into LDS, two code loads, two scale loads),
+// every load unconditional (steps past the end re-read the last step with a
+// zero scale), so the number of loads issued after any given one is fixed.
+//
+// HT = 1 adds a half block of 16 rows on v_mfma_f32_16x16x32_f16 (a chunk
+// of 32 MBT + 1 .. 32 MBT + 16 rows then pays for 16 padding rows at most,
+// not 31).  Its MFMA contracts two consecutive 16-K sub-steps at once: the
+// weight fragments of both (32x32 layout: lane (c, h) holds row c, chunk
+// 4 h + ks) pass through one permlane16 swap per register, which leaves
+// rows 0..15 of the 32-row tile in one register and rows 16..31 in the
+// other, lane (c, g) = (lane & 15, lane >> 4) holding chunk 4 (g >> 1) + ks
+// - 1 + (g & 1) of its row (ks odd); the half block's activation fragment
+// takes the same chunks of its rows, so both operands agree on K.
+template <int MODE, int BITS, int MBT, int HT, bool PP>
 __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const Lane& ln_,
                                       u32x4_v* As, int* tok, int mc, int nrows) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -250,16 +261,17 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
   // the weight ring is issued first (it needs only the descriptor), then
   // the chunk's activation rows are read and published in LDS
   constexpr int kBLoads = PP ? 2 : 4;   // code and scale loads per step
-  constexpr int kStepLoads = MBT + kBLoads;
+  constexpr int MBA = MBT + HT;         // 32-row pieces staged in LDS per step
+  constexpr int kStepLoads = MBA + kBLoads;
   // Loads issued after A(s + 2) by the end of step s: from step 3 on, the
   // weight and scale loads of its own step and three whole steps (at least
   // (kAD - 2) whole steps, counted without the former); in steps 0 and 1,
   // whose A(s + 2) the prologue issued (after the weight ring), the
   // prologue's later activation loads and the steps so far:
-  // (kAD - 2) * MBT + kBLoads (s + 1).  The prologue's barrier waits for A(1):
+  // (kAD - 2) * MBA + kBLoads (s + 1).  The prologue's barrier waits for A(1):
   // A(2) .. A(kAD - 1) come after it.
   constexpr int kWaitSteady = (kAD - 2) * kStepLoads;
-  constexpr int kWaitFirst = (kAD - 2) * MBT;
+  constexpr int kWaitFirst = (kAD - 2) * MBA;
   static_assert(kAD == 5, "the early-step counts below assume five steps ahead");
   // the chunk's activation rows (a load that needs only the tile), then
   // the weight ring (it needs the descriptor), then the rows are published
@@ -282,24 +294,29 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
   __syncthreads();   // previous chunk's readers of tok are done
   if (tid < kRowsMax) tok[tid] = (MODE == 0 && !t.is_sh) ? r / a.k : r;
   __syncthreads();
-  // activations: piece q = (wave * MBT + i) * 64 + lane of a step (row q >>
+  // activations: piece q = (wave * MBA + i) * 64 + lane of a step (row q >>
   // 3, LDS slot q & 7) holds global chunk (q & 7) ^ ((row >> 1) & 7) of the
   // row; a load writes its 64 lanes' 16 bytes contiguously from its LDS base
+  // (a half block stages a whole 32-row piece: rows past the chunk re-read
+  // row 0, and every wave keeps one load count)
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(t.asrc, t.a_bytes);
-  int aoff[MBT];
+  int aoff[MBA];
 #pragma unroll
-  for (int i = 0; i < MBT; ++i) {
-    const int q = (wave * MBT + i) * 64 + lane;
+  for (int i = 0; i < MBA; ++i) {
+    const int q = (wave * MBA + i) * 64 + lane;
     const int m = q >> 3;
     aoff[i] = tok[m] * a.ld_in * 2 + (((q & 7) ^ ((m >> 1) & 7)) * 16);
   }
-  auto dma_a = [&](int st, int buf) {
+  // pieces i with i % 3 == part of step st (part < 0: all of them)
+  auto dma_a = [&](int st, int buf, int part) {
     const int o = min(st, n_st - 1) * (kKS * 2);
 #pragma unroll
-    for (int i = 0; i < MBT; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ars, (__attribute__((address_space(3))) void*)(As + buf * kABuf + (wave * MBT + i) * 64),
-          16, aoff[i], o, 0, 0);
+    for (int i = 0; i < MBA; ++i)
+      if (part < 0 || i % 3 == part)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ars,
+            (__attribute__((address_space(3))) void*)(As + buf * kABuf + (wave * MBA + i) * 64),
+            16, aoff[i], o, 0, 0);
   };
 
   f32x16_v acc[2][MBT];
@@ -309,6 +326,12 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     for (int mb = 0; mb < MBT; ++mb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[p][mb][j] = 0.0f;
+  // half block: [part][rows 0..15 / 16..31 of the part's 32-row tile]
+  f32x4_v acch[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) acch[p][q] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
 
   // fragment of row tile mb, 16-K sub-step ks, from LDS buffer buf: lane
   // (lc, kh) reads row 32 mb + lc, chunk kh * 4 + ks
@@ -317,6 +340,29 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     const u32x4_v* Ab = As + buf * kABuf + lc * kChunks + ((kh * 4 + ks) ^ rsw);
 #pragma unroll
     for (int mb = 0; mb < MBT; ++mb) f[mb] = __builtin_bit_cast(f16x8_v, Ab[32 * kChunks * mb]);
+  };
+  // half-block fragment for sub-steps ks, ks + 1 (ks even): lane (c, g)
+  // reads row 32 MBT + c, chunk 4 (g >> 1) + ks + (g & 1)
+  const int hc = lane & 15, hg = lane >> 4;
+  const int hoff = (32 * MBT + hc) * kChunks;
+  const int hsw = (hc >> 1) & 7;
+  auto read_half = [&](int buf, int ks) {
+    return __builtin_bit_cast(
+        f16x8_v, As[buf * kABuf + hoff + ((4 * (hg >> 1) + ks + (hg & 1)) ^ hsw)]);
+  };
+  // 16x16x32 weight operands of one part from its 32x32 fragments of
+  // sub-steps ks - 1 (x) and ks (y): rows 0..15 (t0) and 16..31 (t1)
+  auto swap16 = [&](const f16x8_v& x, const f16x8_v& y, f16x8_v& t0, f16x8_v& t1) {
+    const u32x4_v xv = __builtin_bit_cast(u32x4_v, x), yv = __builtin_bit_cast(u32x4_v, y);
+    u32x4_v a0, a1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto r = __builtin_amdgcn_permlane16_swap(xv[i], yv[i], false, false);
+      a0[i] = r[0];
+      a1[i] = r[1];
+    }
+    t0 = __builtin_bit_cast(f16x8_v, a0);
+    t1 = __builtin_bit_cast(f16x8_v, a1);
   };
   // steps past the last one (the loop runs whole rings) get a zero scale
   auto deq = [&](const BReg<BITS>& b, int ks, int stg, f16x8_v* bq) {
@@ -336,12 +382,13 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
   // reads the fragments of ks + 1 and dequantizes its weights while its own
   // MFMAs run; the last sub-step does so for the first sub-step of the next
   // step (buffer nbuf, weights bn)
-  // Sub-step 1 also issues the activation loads of step dst into LDS
-  // buffer dbuf, sub-step 3 the weight and scale loads of step stg + kRing
-  // into b (its codes are last read by sub-step 2); the loads are spread
-  // between the MFMAs.  Sub-steps end with scheduling fences, so the order
-  // of the loads (activations, then weights and scales) is the same in
-  // every step.
+  // Sub-steps 0..2 also issue the activation loads of step dst into LDS
+  // buffer dbuf (piece i in sub-step i mod 3, so the four waves' 1 KB loads
+  // do not queue up at the CU's address unit at once), sub-step 3 the
+  // weight and scale loads of step stg + kRing into b (its codes are last
+  // read by sub-step 2); the loads are spread between the MFMAs.  Sub-steps
+  // end with scheduling fences, so the order of the loads (activations,
+  // then weights and scales) is the same in every step.
   auto step = [&](int buf, int nbuf, BReg<BITS>& b, const BReg<BITS>& bn, int stg, int dst,
                   int dbuf) {
     // prepacked: the scale word of step stg + kRing is read from LDS in
@@ -349,10 +396,21 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     // into b with its codes in sub-step 3, so the read has landed long
     // before the step's barrier waits for the LDS
     BReg<BITS> sn;
+    f16x8_v fh, bprev[2];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int cur = ks & 1, nxt = cur ^ 1;
       if (PP && ks == 0) load_s(stg + kRing, sn);
+      if (HT && cur == 0) {
+        fh = read_half(buf, ks);
+        bprev[0] = bq[cur][0];
+        bprev[1] = bq[cur][1];
+      }
+      f16x8_v th[2][2];
+      if (HT && cur == 1) {
+        swap16(bprev[0], bq[cur][0], th[0][0], th[0][1]);
+        swap16(bprev[1], bq[cur][1], th[1][0], th[1][1]);
+      }
       if (ks < 3) {
         read_frags(buf, ks + 1, fr[nxt]);
         deq(b, ks + 1, stg, bq[nxt]);
@@ -360,7 +418,7 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
         read_frags(nbuf, 0, fr[nxt]);
         deq(bn, 0, stg + 1, bq[nxt]);
       }
-      if (ks == 1) dma_a(dst, dbuf);
+      if (ks < 3) dma_a(dst, dbuf, ks);
       if (ks == 3) {
         if (PP) {
           load_c(stg + kRing, b);
@@ -374,16 +432,33 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
         acc[0][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[cur][mb], bq[cur][0], acc[0][mb], 0, 0, 0);
         acc[1][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[cur][mb], bq[cur][1], acc[1][mb], 0, 0, 0);
       }
+      if (HT && cur == 1) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            acch[p][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fh, th[p][q], acch[p][q], 0, 0, 0);
+      }
       // issue order: the LDS reads, then the MFMAs with the loads (one per
       // MFMA) and the dequantization between them
-      const int kLd = ks == 1 ? MBT : ks == 3 ? kBLoads : 0;
-      if (PP && ks == 0) __builtin_amdgcn_sched_group_barrier(0x100, MBT + 1, 0);
+      const int kLd = ks < 3 ? (MBA - ks + 2) / 3 : kBLoads;
+      const bool ds_s = PP && ks == 0, ds_h = HT && cur == 0;
+      if (ds_s && ds_h) __builtin_amdgcn_sched_group_barrier(0x100, MBT + 2, 0);
+      else if (ds_s || ds_h) __builtin_amdgcn_sched_group_barrier(0x100, MBT + 1, 0);
       else __builtin_amdgcn_sched_group_barrier(0x100, MBT, 0);
 #pragma unroll
       for (int i = 0; i < 2 * MBT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i < kLd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+      if (HT && cur == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (2 * MBT + i < kLd) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -398,7 +473,7 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
 #pragma unroll
   for (int j = 0; j < kAD; ++j) {
     __builtin_amdgcn_sched_barrier(0);
-    dma_a(j, j);
+    dma_a(j, j, -1);
   }
   vm_barrier<kWaitFirst>();
   if (PP) {
@@ -414,7 +489,7 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     const int db = buf + kAD >= kABufs ? buf + kAD - kABufs : buf + kAD; \
     step(buf, nb, BC, BN, base + J, base + J + kAD, db);      \
     if (J < 2 && base == 0)                                   \
-      vm_barrier<(kAD - 2) * MBT + kBLoads * (J + 1)>();      \
+      vm_barrier<(kAD - 2) * MBA + kBLoads * (J + 1)>();      \
     else                                                      \
       vm_barrier<kWaitSteady>();                              \
     buf = nb;                                                 \
@@ -454,11 +529,24 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
         const float hv = silu_mul_fast(acc[0][mb][j], acc[1][mb][j]);
         *reinterpret_cast<uint16_t*>(stg + m * kRowB + lc * 2) = (uint16_t)f32_to_bf16(hv);
       }
+    // half block: lane holds column 16 q + (lane & 15) of both parts, rows
+    // 32 MBT + 4 (lane >> 4) + j
+    if (HT) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = 32 * MBT + 4 * hg + j;
+          const float hv = silu_mul_fast(acch[0][q][j], acch[1][q][j]);
+          *reinterpret_cast<uint16_t*>(stg + m * kRowB + (16 * q + hc) * 2) =
+              (uint16_t)f32_to_bf16(hv);
+        }
+    }
     __syncthreads();   // lanes read what other lanes wrote
     const int q = lane & 3;
     const int u = ln_.wrow[0] - lc + 8 * q;   // first unit of the lane's 16 bytes
 #pragma unroll
-    for (int i = 0; i < (MBT * 32 + 15) / 16; ++i) {
+    for (int i = 0; i < (MBT * 32 + HT * 16 + 15) / 16; ++i) {
       const int m = 16 * i + (lane >> 2);
       const u32x4_v v = *reinterpret_cast<const u32x4_v*>(stg + m * kRowB + q * 16);
       if (m < nrows && ln_.wval[0]) {
@@ -481,11 +569,19 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
           const int m = 32 * mb + (j >> 2) * 8 + kh * 4 + (j & 3);
           *reinterpret_cast<float*>(stg + m * kRowB + lc * 4) = acc[p][mb][j];
         }
+      if (HT) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float*>(stg + (32 * MBT + 4 * hg + j) * kRowB + (16 * q + hc) * 4) =
+                acch[p][q][j];
+      }
       __syncthreads();   // lanes read what other lanes wrote
       const int q = lane & 7;
       const int col = ln_.wrow[p] - lc + 4 * q;
 #pragma unroll
-      for (int i = 0; i < (MBT * 32 + 7) / 8; ++i) {
+      for (int i = 0; i < (MBT * 32 + HT * 16 + 7) / 8; ++i) {
         const int m = 8 * i + (lane >> 3);
         const u32x4_v v = *reinterpret_cast<const u32x4_v*>(stg + m * kRowB + q * 16);
         if (m < nrows && ln_.wval[p])
@@ -574,12 +670,25 @@ __device__ __forceinline__ void tile(const ProjArgs& a, const Tile& t, u32x4_v* 
 
   for (int mc = t.r_begin; mc < t.r_end; mc += kRowsMax) {
     const int nrows = min(kRowsMax, t.r_end - mc);
-    const int mbt = (nrows + 31) >> 5;
-    if (mbt == 5) chunk<MODE, BITS, 5, PP>(a, t, L, As, tok, mc, nrows);
-    else if (mbt == 4) chunk<MODE, BITS, 4, PP>(a, t, L, As, tok, mc, nrows);
-    else if (mbt == 3) chunk<MODE, BITS, 3, PP>(a, t, L, As, tok, mc, nrows);
-    else if (mbt == 2) chunk<MODE, BITS, 2, PP>(a, t, L, As, tok, mc, nrows);
-    else chunk<MODE, BITS, 1, PP>(a, t, L, As, tok, mc, nrows);
+    // whole 32-row blocks, plus a 16-row half block when the last 1..16
+    // rows would otherwise fill a block of their own
+    const int full = nrows >> 5, rem = nrows & 31;
+    const bool half = full > 0 && rem > 0 && rem <= 16;
+    const int mbt = half ? full : (nrows + 31) >> 5;
+    if (mbt == 5) chunk<MODE, BITS, 5, 0, PP>(a, t, L, As, tok, mc, nrows);
+    else if (mbt == 4) {
+      if (half) chunk<MODE, BITS, 4, 1, PP>(a, t, L, As, tok, mc, nrows);
+      else chunk<MODE, BITS, 4, 0, PP>(a, t, L, As, tok, mc, nrows);
+    } else if (mbt == 3) {
+      if (half) chunk<MODE, BITS, 3, 1, PP>(a, t, L, As, tok, mc, nrows);
+      else chunk<MODE, BITS, 3, 0, PP>(a, t, L, As, tok, mc, nrows);
+    } else if (mbt == 2) {
+      if (half) chunk<MODE, BITS, 2, 1, PP>(a, t, L, As, tok, mc, nrows);
+      else chunk<MODE, BITS, 2, 0, PP>(a, t, L, As, tok, mc, nrows);
+    } else {
+      if (half) chunk<MODE, BITS, 1, 1, PP>(a, t, L, As, tok, mc, nrows);
+      else chunk<MODE, BITS, 1, 0, PP>(a, t, L, As, tok, mc, nrows);
+    }
   }
 }
 

@@ -732,6 +732,31 @@ def test_prepacked_bank_matches_canonical(name, tile_m):
     check_out(g1, g32, o["out"], f"prepacked {cfg.name}")
 
 
+@pytest.mark.parametrize("name,tile_m", [("mfma_mixed", 40), ("mfma_mixed", 80),
+                                         ("mfma_mixed", 112), ("mfma_mixed", 144),
+                                         ("mfma_g32_int2", 48)])
+def test_mfma_half_row_blocks(name, tile_m):
+    """Chunks of 32 m + 1 .. 32 m + 16 rows (m = 1 .. 4) run their last 16
+    rows as a half block on the 16x16x32 matrix instruction: tiles of 40,
+    48, 80, 112 and 144 rows (and the ragged last tile of each expert) put
+    half blocks after one to four whole blocks in both projections, on the
+    canonical and the prepacked bank; both meet the gate against the
+    oracle and agree bit for bit."""
+    cfg = MFMA[name]
+    dl = _dev(cfg)
+    g0, _ = run_layer_gpu(dl, "a16", tile_m, flags=2)
+    g32, _ = run_layer_gpu(dl, "a16", tile_m, flags=2, out_f32=True)
+    o = oracle.oracle_layer(_layer(cfg), tile_m=tile_m)
+    _check_integer_stages(g0, o, cfg)
+    ok, rl2, worst = h_gate(_valid_h(g0["h"], cfg), _valid_h(o["h"], cfg), "a16")
+    assert ok, ("h", rl2, worst)
+    check_out(g0, g32, o["out"], f"{cfg.name} tile_m={tile_m}")
+    dl.bank = dl.bank.prepack()
+    g1, _ = run_layer_gpu(dl, "a16", tile_m, flags=2)
+    assert g1["err"] == 0
+    assert np.array_equal(g1["h"], g0["h"]) and np.array_equal(g1["out"], g0["out"])
+
+
 def test_prepacked_prefill_layer_matches_canonical():
     """The prefill layer (4096 tokens, 192 int4 + 64 int2 experts) on a
     prepacked bank: h and out identical to the canonical bank's, which is
