@@ -57,6 +57,7 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_v;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_v;
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_v __attribute__((ext_vector_type(2)));
 
@@ -186,14 +187,17 @@ struct BReg {
 };
 
 // Wait until at most N vector-memory operations of this wave are in flight
-// and every LDS access has completed, then the workgroup barrier.  The
-// scheduling fences keep the compiler from moving any instruction across
-// it, so the count of loads issued after a given one is the program's.
-template <int N>
+// and every LDS access but the last LG has completed (LDS accesses complete
+// in order; an outstanding scalar load only makes the count stricter), then
+// the workgroup barrier.  The scheduling fences keep the compiler from
+// moving any instruction across it, so the count of loads issued after a
+// given one is the program's.
+template <int N, int LG = 0>
 __device__ __forceinline__ void vm_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  static_assert(LG >= 0 && LG < 16, "lgkmcnt range");
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (LG << 8));
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -489,9 +493,9 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     const int db = buf + kAD >= kABufs ? buf + kAD - kABufs : buf + kAD; \
     step(buf, nb, BC, BN, base + J, base + J + kAD, db);      \
     if (J < 2 && base == 0)                                   \
-      vm_barrier<(kAD - 2) * MBA + kBLoads * (J + 1)>();      \
+      vm_barrier<(kAD - 2) * MBA + kBLoads * (J + 1), MBT>(); \
     else                                                      \
-      vm_barrier<kWaitSteady>();                              \
+      vm_barrier<kWaitSteady, MBT>();                         \
     buf = nb;                                                 \
   }
   for (int base = 0; base < n_st; base += kRing) {
@@ -521,26 +525,29 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
     // on different banks)
     constexpr int kRowB = 80;
     unsigned char* stg = reinterpret_cast<unsigned char*>(As) + wave * (kRowsMax * kRowB);
+    // two rows of one column at a time: one packed round-to-nearest-even
+    // conversion, then the two halves
+    auto put2 = [&](int m, int c, float g0, float u0, float g1, float u1) {
+      const bf16x2_v v = {(__bf16)silu_mul_fast(g0, u0), (__bf16)silu_mul_fast(g1, u1)};
+      const uint32_t w = __builtin_bit_cast(uint32_t, v);
+      *reinterpret_cast<uint16_t*>(stg + m * kRowB + c * 2) = (uint16_t)w;
+      *reinterpret_cast<uint16_t*>(stg + (m + 1) * kRowB + c * 2) = (uint16_t)(w >> 16);
+    };
 #pragma unroll
     for (int mb = 0; mb < MBT; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = 32 * mb + (j >> 2) * 8 + kh * 4 + (j & 3);
-        const float hv = silu_mul_fast(acc[0][mb][j], acc[1][mb][j]);
-        *reinterpret_cast<uint16_t*>(stg + m * kRowB + lc * 2) = (uint16_t)f32_to_bf16(hv);
-      }
+      for (int j = 0; j < 16; j += 2)
+        put2(32 * mb + (j >> 2) * 8 + kh * 4 + (j & 3), lc, acc[0][mb][j], acc[1][mb][j],
+             acc[0][mb][j + 1], acc[1][mb][j + 1]);
     // half block: lane holds column 16 q + (lane & 15) of both parts, rows
     // 32 MBT + 4 (lane >> 4) + j
     if (HT) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = 32 * MBT + 4 * hg + j;
-          const float hv = silu_mul_fast(acch[0][q][j], acch[1][q][j]);
-          *reinterpret_cast<uint16_t*>(stg + m * kRowB + (16 * q + hc) * 2) =
-              (uint16_t)f32_to_bf16(hv);
-        }
+        for (int j = 0; j < 4; j += 2)
+          put2(32 * MBT + 4 * hg + j, 16 * q + hc, acch[0][q][j], acch[1][q][j],
+               acch[0][q][j + 1], acch[1][q][j + 1]);
     }
     __syncthreads();   // lanes read what other lanes wrote
     const int q = lane & 3;
