@@ -845,9 +845,13 @@ def test_prepacked_bank_needs_the_matrix_core_path():
 
 BIG_SORT = LayerConfig("mfma_big_sort", 214, T=1100, H=256, E=40, k=8, I=128, group=64,
                        n_int2=7, group_int2=32)
+# 33600 pairs: 17 chunks of 2048, the last one partial
+SORT_TWO_LAUNCH = LayerConfig("mfma_sort_two_launch", 216, T=4200, H=256, E=40, k=8, I=128,
+                              group=64, n_int2=7, group_int2=32)
 
 
-@pytest.mark.parametrize("name", ["mfma_mixed", "gated_mfma", "big_sort", "prefill"])
+@pytest.mark.parametrize("name", ["mfma_mixed", "gated_mfma", "big_sort", "sort_two_launch",
+                                  "prefill"])
 def test_layer_call_matches_separate_calls_on_matrix_cores(name):
     """moe_w4_layer on the matrix-core path (its routing launch makes the fp16
     copy of x, its gate/up epilogue writes the fp16 h rows the down
@@ -856,7 +860,8 @@ def test_layer_call_matches_separate_calls_on_matrix_cores(name):
     output bits as the separate calls (one-workgroup sort, fp16 x and h made
     by conversion passes)."""
     cfg = {"mfma_mixed": MFMA["mfma_mixed"], "gated_mfma": GATED["gated_mfma"],
-           "big_sort": BIG_SORT, "prefill": LAYERS["prefill_mixed_t4096"]}[name]
+           "big_sort": BIG_SORT, "sort_two_launch": SORT_TWO_LAUNCH,
+           "prefill": LAYERS["prefill_mixed_t4096"]}[name]
     dl = _dev(cfg)
     g1, _ = run_layer_gpu(dl, "a16", 160)
     g2, _ = run_layer_gpu(dl, "a16", 160, fused=False)
@@ -864,11 +869,11 @@ def test_layer_call_matches_separate_calls_on_matrix_cores(name):
                 "n_tiles", "out", "h"):
         assert np.array_equal(g1[key], g2[key]), key
     assert g1["err"] == 0
-    if name == "big_sort":
+    if name in ("big_sort", "sort_two_launch"):
         o = oracle.oracle_layer(_layer(cfg), tile_m=160)
         _check_integer_stages(g1, o, cfg)
         g32, _ = run_layer_gpu(dl, "a16", 160, out_f32=True)
-        check_out(g1, g32, o["out"], "big sort")
+        check_out(g1, g32, o["out"], name)
 
 
 def test_gateup_reads_fp16_copy_left_by_the_layer_call():
