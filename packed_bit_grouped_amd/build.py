@@ -1,7 +1,12 @@
 """Build libmoe_w4.so in place with hipcc for gfx950.
 
-Usage: python -m packed_bit_grouped_amd.build [-j N]
+Usage: python -m packed_bit_grouped_amd.build [-j N] [--host-check OUT.so]
 Every call recompiles every source (the build check wants a real compile).
+--host-check also builds a copy of the library whose host code at the C ABI
+(argument checks, workspace carving, launch set-up: api.cpp and the entry
+points of noalloc.hip and probe.hip) carries AddressSanitizer and
+UndefinedBehaviorSanitizer; device code is not instrumented.  It is for
+CPU-side checks only (load it with the ASan runtime preloaded).
 """
 from __future__ import annotations
 
@@ -45,6 +50,45 @@ def _compile(src: str, objdir: str) -> str:
     return obj
 
 
+# sources whose host code is instrumented in the host-check build
+HOST_CHECK_SOURCES = ["api.cpp", "noalloc.hip", "probe.hip"]
+# host-side sanitizers only: each flag goes to the host compilation
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_check(out: str, jobs: int = 0) -> str:
+    """The library with sanitized host code at the ABI (see the module
+    docstring); the kernel sources' objects come from the regular build
+    (built first if missing)."""
+    objdir = os.path.join(HERE, "_build")
+    plain = [s for s in SOURCES if s not in HOST_CHECK_SOURCES]
+    if not all(os.path.exists(os.path.join(objdir, s + ".o")) for s in plain):
+        build(jobs, verbose=False)
+    sandir = os.path.join(objdir, "host_check")
+    os.makedirs(sandir, exist_ok=True)
+
+    def comp(src):
+        obj = os.path.join(sandir, src + ".o")
+        flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", *SAN_FLAGS]
+        r = subprocess.run([hipcc(), "-x", "hip", *flags, "-c", os.path.join(CSRC, src), "-o",
+                            obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=jobs or len(HOST_CHECK_SOURCES)) as ex:
+        objs = list(ex.map(comp, HOST_CHECK_SOURCES))
+    objs += [os.path.join(objdir, s + ".o") for s in plain]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS[:4],
+           "-Xarch_host", "-shared-libsan", "-o", out, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr[-8000:]}")
+    return out
+
+
 def build(jobs: int = 0, verbose: bool = True) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -65,4 +109,8 @@ def build(jobs: int = 0, verbose: bool = True) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=0)
-    build(ap.parse_args().j)
+    ap.add_argument("--host-check", metavar="OUT", default=None)
+    a = ap.parse_args()
+    build(a.j)
+    if a.host_check:
+        print(f"built {build_host_check(a.host_check, a.j)}")
