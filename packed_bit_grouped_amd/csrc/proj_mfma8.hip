@@ -19,9 +19,14 @@
 //  * the K loop walks 64 K per step, four 16-K MFMA sub-steps; each
 //    sub-step reads the next sub-step's activation fragments and
 //    dequantizes its weights while its own MFMAs run;
+//  * a chunk whose last block would hold 1..16 rows runs those rows as a
+//    16-row half block on v_mfma_f32_16x16x32_f16 (two sub-steps at once,
+//    the weight fragments rearranged by permlane16 swaps), so padding
+//    stays under 16 rows per chunk;
 //  * activations (fp16, in the K order of the unpack) go from memory
 //    straight into a ring of six LDS buffers [row][8 x 16-byte chunks] with
-//    buffer loads that write LDS, five steps ahead; chunk c of row m sits in
+//    buffer loads that write LDS, five steps ahead, a step's loads spread
+//    over three sub-steps; chunk c of row m sits in
 //    slot c ^ ((m >> 1) & 7) (a 128-bit LDS access is served 16 lanes at a
 //    time, and 16 consecutive rows' chunk c then cover the 64 banks once);
 //    a load writes its 64 lanes' 16 bytes contiguously, so each lane loads
@@ -35,7 +40,8 @@
 //    are reordered (0, 2, 1, 3) first, so int2 codes unpack in the same K
 //    order as int4 and one fp16 copy of x serves both;
 //  * one barrier per step, with the wait for the activation loads counted
-//    by hand (every step issues the same loads in the same order);
+//    by hand (every step issues the same loads in the same order) and the
+//    LDS wait leaving the next step's first fragment reads in flight;
 //  * canonical layout: lane (row c, half h) of a 32-row block reads bytes
 //    [32 s + 16 h, +16) (int4; int2 [16 s + 8 h, +8)) of its row at step s;
 //    prepacked layout (moe_w4_prepack): those 16 (8) bytes of the 64 lanes
