@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOE_W4_ABI_VERSION 3
+#define MOE_W4_ABI_VERSION 4
 
 /* Version of the compiled library.  The Python binding refuses to load a
  * library whose version differs from the header it was written for. */
@@ -541,6 +541,24 @@ moe_status moe_dbg_w4a8_down_partials(
     const int32_t* pair_pos, const int32_t* tiles, const int32_t* n_tiles,
     int tile_m, void* out, void* workspace, size_t ws_bytes, int flags,
     int32_t* partials, int ng_ld, void* stream);
+
+/* ---------------------------------------------------------------------
+ * moe_dbg_dec_stamps -- measurement aid for the decode timeline (build log
+ * "Two 96 GB Ascend cards run Qwen3.8 Flash-Next", section "Remove sync
+ * and launch overhead from the token loop": where the time of a decode
+ * step goes).  In a library built with MOE_DEC_STAMPS
+ * (`python -m packed_bit_grouped_amd.build --stamps OUT.so`) it names the
+ * device buffer (unsigned 64-bit [grid][8], caller-owned, zeroed by the
+ * caller) into which the decode kernels' workgroups write the 100 MHz
+ * realtime counter at each phase end: dec_route_gateup_kernel slots 0
+ * entry, 1 routed, 2 sorted, 3 weights issued, 4 activations staged, 5
+ * products done; dec_down_combine_kernel 0 entry, 1 tables in, 2 weights
+ * issued, 3 h staged, 4 products done, 5 outputs stored.  Null stops the
+ * stamps.  It applies to launches that follow it on any stream.  Errors:
+ * MOE_E_UNSUPPORTED in the regular library (nothing is touched),
+ * MOE_E_DEVICE.
+ * ------------------------------------------------------------------- */
+moe_status moe_dbg_dec_stamps(unsigned long long* stamps);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,7 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_DEVICE, MOE_E_WORKSPACE = 0, -1, -2, -3, -4
 MOE_A16, MOE_A8 = 0, 1
@@ -100,6 +100,7 @@ _SIGS = {
                                            c_void_p, c_int, c_void_p,
                                            c_void_p, c_size_t, c_int, c_void_p,
                                            c_int, c_void_p]),
+    "moe_dbg_dec_stamps": (c_int, [c_void_p]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -333,3 +334,8 @@ def moe_dbg_w4a8_down_partials(h, T, H, I, E, k, w2, w2_shared, n_shared,
                  _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos), _ptr(tiles),
                  _ptr(n_tiles), tile_m, _ptr(out), _ptr(workspace), ws_bytes,
                  flags, _ptr(partials), ng_ld, _stream(stream), check=check)
+
+
+def moe_dbg_dec_stamps(stamps, check=True):
+    """The decode kernels' phase-stamp buffer (a MOE_DEC_STAMPS build only)."""
+    return _call("moe_dbg_dec_stamps", _ptr(stamps), check=check)

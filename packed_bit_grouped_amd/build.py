@@ -1,12 +1,16 @@
 """Build libmoe_w4.so in place with hipcc for gfx950.
 
 Usage: python -m packed_bit_grouped_amd.build [-j N] [--host-check OUT.so]
+                                               [--stamps OUT.so]
 Every call recompiles every source (the build check wants a real compile).
 --host-check also builds a copy of the library whose host code at the C ABI
 (argument checks, workspace carving, launch set-up: api.cpp and the entry
 points of noalloc.hip and probe.hip) carries AddressSanitizer and
 UndefinedBehaviorSanitizer; device code is not instrumented.  It is for
 CPU-side checks only (load it with the ASan runtime preloaded).
+--stamps also builds a copy whose decode kernels write phase clock stamps
+(MOE_DEC_STAMPS; moe_dbg_dec_stamps names the buffer), for the timeline
+measurement only.
 """
 from __future__ import annotations
 
@@ -89,6 +93,30 @@ def build_host_check(out: str, jobs: int = 0) -> str:
     return out
 
 
+def build_stamps(out: str, jobs: int = 0) -> str:
+    """The library with the decode kernels' phase stamps compiled in; the
+    other sources' objects come from the regular build (built first if
+    missing)."""
+    objdir = os.path.join(HERE, "_build")
+    plain = [s for s in SOURCES if s != "proj_decode.hip"]
+    if not all(os.path.exists(os.path.join(objdir, s + ".o")) for s in plain):
+        build(jobs, verbose=False)
+    sdir = os.path.join(objdir, "stamps")
+    os.makedirs(sdir, exist_ok=True)
+    obj = os.path.join(sdir, "proj_decode.hip.o")
+    r = subprocess.run([hipcc(), "-x", "hip", *FLAGS, "-DMOE_DEC_STAMPS", "-c",
+                        os.path.join(CSRC, "proj_decode.hip"), "-o", obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for proj_decode.hip:\n{r.stderr[-8000:]}")
+    objs = [obj] + [os.path.join(objdir, s + ".o") for s in plain]
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr[-8000:]}")
+    return out
+
+
 def build(jobs: int = 0, verbose: bool = True) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -110,7 +138,10 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=0)
     ap.add_argument("--host-check", metavar="OUT", default=None)
+    ap.add_argument("--stamps", metavar="OUT", default=None)
     a = ap.parse_args()
     build(a.j)
     if a.host_check:
         print(f"built {build_host_check(a.host_check, a.j)}")
+    if a.stamps:
+        print(f"built {build_stamps(a.stamps, a.j)}")

@@ -34,6 +34,23 @@
 
 namespace moe {
 
+// Phase clock stamps (a build with MOE_DEC_STAMPS only, for the timeline
+// measurement; compiled out otherwise): thread 0 of workgroup b writes the
+// 100 MHz realtime counter into slot i of stamps[b][8] at each phase end,
+// with an ordinary vector store.
+#ifdef MOE_DEC_STAMPS
+__constant__ unsigned long long* g_dec_stamps = nullptr;
+#define DEC_STAMP(i)                                                            \
+  do {                                                                          \
+    if (g_dec_stamps && threadIdx.x == 0)                                       \
+      g_dec_stamps[(size_t)blockIdx.x * 8 + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define DEC_STAMP(i) \
+  do {               \
+  } while (0)
+#endif
+
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecGuLanes = 32;   // lanes per weight row, gate/up
@@ -281,6 +298,7 @@ __device__ __forceinline__ void gateup_tile(const ProjArgs& a, bool is_sh, int e
   }
   GuRows<CPL> g;
   gu_issue<CPL>(g, a, is_sh, q, ub);
+  DEC_STAMP(3);   // weight loads issued
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int u = tid + i * kDecThreads;
@@ -290,7 +308,9 @@ __device__ __forceinline__ void gateup_tile(const ProjArgs& a, bool is_sh, int e
     }
   }
   lds_barrier();
+  DEC_STAMP(4);   // activations staged
   gu_compute<MAXT, CPL>(g, a, is_sh, e, r_begin, nt, xs, xsum);
+  DEC_STAMP(5);   // products and h stores done
 }
 
 // LDS carve-up shared by the gate/up kernels: activation planes, their
@@ -486,6 +506,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_route_gateup_kernel(ProjArgs 
   int* ntl = srt + kFusedMaxP;                                         // [1]
 
   // ---- round trip 1: descriptors and logits together; routing and sorting
+  DEC_STAMP(0);   // entry
   DescCopy<1> dc;
   dc.fetch(a);
   const bool writer = blockIdx.x == 0;
@@ -494,8 +515,10 @@ __global__ __launch_bounds__(kDecThreads) void dec_route_gateup_kernel(ProjArgs 
                       writer ? ro.ids : nullptr, writer ? ro.w : nullptr, rid, rw);
   dc.put(descs, a);
   lds_barrier();
+  DEC_STAMP(1);   // logits and descriptors in, top-k done
   block_permute<NV>(rid, P, E, tile_m, srt, til, ntl, nullptr, writer, ro);
   lds_barrier();
+  DEC_STAMP(2);   // sorted, tile list in LDS
 
   bool is_sh;
   int e, r_begin, r_end;
@@ -719,6 +742,7 @@ __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs 
   const int n = n0 + (threadIdx.x & 63) / kDecDnLanes;
 
   // ---- round trip 1, all independent: counts and every table
+  DEC_STAMP(0);   // entry
   const int n_tiles = min(ld_global(a.n_tiles), a.max_tiles);
   const int total_valid = ld_global(a.offsets + a.E);
   const u32x4_v* tsrc = reinterpret_cast<const u32x4_v*>(a.tiles);
@@ -735,13 +759,16 @@ __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs 
   pc.put(ppos, a.pair_pos, a.P);
   wc.put(reinterpret_cast<int*>(gw), wsrc, a.P);
   lds_barrier();
+  DEC_STAMP(1);   // tables in
   const int S = a.n_sh_slots + n_tiles;
 
   // ---- this wave's tiles, kDecDnRounds at a time: every weight load of
   // the batch (round trip 2, together with the h rows below)
   DnSlots<CPL> d;
   dn_issue<CPL>(d, a, 0, S, n_tiles, tls, descs, n);
+  DEC_STAMP(2);   // weight loads issued
   dn_stage(a, S, n_tiles, tls, descs, R_rows, total_valid, L);
+  DEC_STAMP(3);   // h rows staged
 
   static_assert(kDecDnRounds == 2, "one dn_run() per round below");
   const int n_batches = (S + kDecWaves * kDecDnRounds - 1) / (kDecWaves * kDecDnRounds);
@@ -751,7 +778,9 @@ __global__ __launch_bounds__(kDecThreads) void dec_down_combine_kernel(ProjArgs 
     dn_run<MAXT, CPL>(d, 1, a, L, n);
   }
   lds_barrier();
+  DEC_STAMP(4);   // products done
   dn_combine(a, ppos, gw, L.yb, out, n0);
+  DEC_STAMP(5);   // outputs stored
 }
 
 // ---------------------------------------------------------------------
@@ -1247,3 +1276,16 @@ hipError_t launch_dec_layer(const ProjArgs& ag_in, const ProjArgs& ad_in, const 
 }
 
 }  // namespace moe
+
+// The phase-stamp buffer of the decode kernels (the MOE_DEC_STAMPS build;
+// otherwise MOE_E_UNSUPPORTED and nothing is touched).
+extern "C" moe_status moe_dbg_dec_stamps(unsigned long long* stamps) {
+#ifdef MOE_DEC_STAMPS
+  return hipMemcpyToSymbol(HIP_SYMBOL(moe::g_dec_stamps), &stamps, sizeof(stamps)) == hipSuccess
+             ? MOE_OK
+             : MOE_E_DEVICE;
+#else
+  (void)stamps;
+  return MOE_E_UNSUPPORTED;
+#endif
+}

@@ -173,6 +173,13 @@ def test_down_validation():
     assert call() == L.MOE_E_DEVICE
 
 
+def test_stamps_hook_is_inert_in_the_regular_library():
+    """moe_dbg_dec_stamps only works in the MOE_DEC_STAMPS build; the
+    regular library reports it unsupported and touches nothing."""
+    assert L.moe_dbg_dec_stamps(FAKE, check=False) == L.MOE_E_UNSUPPORTED
+    assert L.moe_dbg_dec_stamps(None, check=False) == L.MOE_E_UNSUPPORTED
+
+
 def test_quant_validation():
     assert L.moe_quant_a8_rows(FAKE, 2, 4, 8, 8, FAKE, FAKE, stream=0, check=False) == L.MOE_E_INVAL
     assert L.moe_quant_a8_rows(FAKE, 0, 4, 8, 4, FAKE, FAKE, stream=0, check=False) == L.MOE_E_INVAL
