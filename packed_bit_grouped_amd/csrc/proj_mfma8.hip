@@ -234,17 +234,22 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
   const int lc = lane & 31, kh = lane >> 5;
   const int n_st = ln_.n_st;
 
+  // the weight stream is read once: non-temporal loads (cache policy nt),
+  // so it does not push the tile's activation rows out of L2
+  constexpr int kWeightCpol = 2;
   auto load_c = [&](int st, BReg<BITS>& b) {
     st = min(st, n_st - 1);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       if constexpr (BITS == 4) {
         const u32x4_v v =
-            __builtin_amdgcn_raw_buffer_load_b128(ln_.crs, ln_.coff[p], st * ln_.cstride, 0);
+            __builtin_amdgcn_raw_buffer_load_b128(ln_.crs, ln_.coff[p], st * ln_.cstride,
+                                                  kWeightCpol);
         b.c[p][0] = v.x; b.c[p][1] = v.y; b.c[p][2] = v.z; b.c[p][3] = v.w;
       } else {
         const u32x2_v v =
-            __builtin_amdgcn_raw_buffer_load_b64(ln_.crs, ln_.coff[p], st * ln_.cstride, 0);
+            __builtin_amdgcn_raw_buffer_load_b64(ln_.crs, ln_.coff[p], st * ln_.cstride,
+                                                 kWeightCpol);
         b.c[p][0] = PP ? v.x : int2_order(v.x);
         b.c[p][1] = PP ? v.y : int2_order(v.y);
       }
