@@ -602,9 +602,13 @@ __device__ __forceinline__ void chunk(const ProjArgs& a, const Tile& t, const La
       for (int i = 0; i < (MBT * 32 + HT * 16 + 7) / 8; ++i) {
         const int m = 8 * i + (lane >> 3);
         const u32x4_v v = *reinterpret_cast<const u32x4_v*>(stg + m * kRowB + q * 16);
+        // y is read once, by the combine after the whole launch: streamed
+        // out with non-temporal stores, which keep the caches for the
+        // tiles' h rows and weights
         if (m < nrows && ln_.wval[p])
-          *reinterpret_cast<u32x4_v*>(static_cast<float*>(a.out) +
-                                      (size_t)(orow0 + m) * a.ld_out + col) = v;
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<u32x4_v*>(static_cast<float*>(a.out) +
+                                            (size_t)(orow0 + m) * a.ld_out + col));
       }
     }
   }

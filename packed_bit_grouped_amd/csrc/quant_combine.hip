@@ -43,6 +43,8 @@ hipError_t launch_quant_a8(const void* src, int is_f32, int R, int C, int ld,
 // accumulated in fp32 in that fixed order (deterministic).  Four outputs
 // per thread with 16-byte loads; the y rows of eight pairs are loaded
 // before the first of their multiply-adds, so they are in flight together.
+// Every y value is read once: non-temporal loads.
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y, int ld_y, const float* __restrict__ topk_w,
     const int32_t* __restrict__ pair_pos, int T, int k, int H, int P,
@@ -63,8 +65,13 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = pp[u] >= 0 ? *reinterpret_cast<const float4*>(y + (size_t)pp[u] * ld_y + n)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (pp[u] >= 0) {
+        const f32x4_nt t = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_nt*>(y + (size_t)pp[u] * ld_y + n));
+        v[u] = make_float4(t.x, t.y, t.z, t.w);
+      } else {
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (pp[u] < 0) continue;
