@@ -67,10 +67,17 @@ __device__ void convert_x_rows(const XPrep& xp, int T, int b, int nb) {
   const uint4* src = reinterpret_cast<const uint4*>(xp.x);
   uint4* dst = reinterpret_cast<uint4*>(xp.x16);
   for (long long u0 = (long long)b * THREADS + threadIdx.x; u0 < units; u0 += 8 * S) {
+    // x is read once here (non-temporal loads); the fp16 copy, read by
+    // every gate/up workgroup of a tile, is stored normally
+    typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
     uint4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (u0 + i * S < units) v[i] = src[u0 + i * S];
+      if (u0 + i * S < units) {
+        const u32x4_nt t =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(src + u0 + i * S));
+        v[i] = make_uint4(t.x, t.y, t.z, t.w);
+      }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (u0 + i * S < units) dst[u0 + i * S] = convert8(v[i]);
